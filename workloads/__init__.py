@@ -1,0 +1,372 @@
+"""Seeded synthetic inputs for paged KV-cache decode attention.
+
+This module is shared by the CPU oracle's tests and by the GPU path's tests
+and benchmark.  It draws random numbers, rounds them to the storage type,
+assigns physical blocks and builds slot mappings.  It contains none of the
+attention arithmetic: no scores, no softmax, no gathers through the block
+table, no scatter of new tokens.
+
+The workload shapes follow the pages' description of a paged KV cache
+("LLM Inference Serving", systeminternals.dev: per layer K and V are each
+stored as [num_blocks, block_size, num_kv_heads, head_dim]; the block size is
+16 tokens) and of the block table ("LLM serving: KV cache, batching, paged
+attention and quantization", learn.mohebi.ai, section 3.5: logical block i
+holds tokens 16i..16i+15 and maps to any physical block).
+
+Every array is reproducible from (spec, seed) alone.  Large arrays are drawn in
+fixed-size chunks whose seeds derive from (seed, stream, chunk index), so the
+values do not depend on how many threads fill them.
+"""
+
+from __future__ import annotations
+
+import math
+import os
+from concurrent.futures import ThreadPoolExecutor
+from dataclasses import dataclass, field, replace
+from typing import Optional
+
+import numpy as np
+
+BLOCK_SIZE = 16
+BF16_QNAN_BITS = np.uint16(0x7FC0)
+F32_QNAN = np.float32("nan")
+
+# stream ids for the derived seeds of the large arrays
+_STREAM_Q, _STREAM_K, _STREAM_V, _STREAM_NEWK, _STREAM_NEWV = 1, 2, 3, 4, 5
+_CHUNK = 1 << 22  # values per independently seeded chunk
+
+
+# ----------------------------------------------------------------------------
+# storage-type helpers (input preparation, not part of the method)
+
+
+def round_to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """fp32 -> bf16 bit patterns by round-to-nearest-even (finite inputs)."""
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
+    return ((u + np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1))) >> np.uint32(16)).astype(np.uint16)
+
+
+def bf16_bits_to_f32(bits: np.ndarray) -> np.ndarray:
+    """bf16 bit patterns -> fp32 values (exact)."""
+    return (np.ascontiguousarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32)
+
+
+def _threads() -> int:
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
+def fill_normal(shape, dtype: str, seed: int, stream: int) -> np.ndarray:
+    """N(0,1) draws in fp32, stored as fp32 ("f32") or bf16 bits ("bf16")."""
+    n = int(np.prod(shape, dtype=np.int64))
+    out = np.empty(n, dtype=np.float32 if dtype == "f32" else np.uint16)
+    nchunks = max(1, (n + _CHUNK - 1) // _CHUNK)
+
+    def work(c):
+        lo = c * _CHUNK
+        hi = min(n, lo + _CHUNK)
+        if hi <= lo:
+            return
+        g = np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, stream, c])))
+        tmp = np.empty(hi - lo, dtype=np.float32)
+        g.standard_normal(out=tmp, dtype=np.float32)
+        if dtype == "f32":
+            out[lo:hi] = tmp
+        else:
+            out[lo:hi] = round_to_bf16_bits(tmp)
+
+    if nchunks == 1:
+        work(0)
+    else:
+        with ThreadPoolExecutor(max_workers=_threads()) as ex:
+            list(ex.map(work, range(nchunks)))
+    return out.reshape(shape)
+
+
+# ----------------------------------------------------------------------------
+# specs
+
+
+@dataclass(frozen=True)
+class Spec:
+    """Shape and distribution of one synthetic paged-decode workload.
+
+    lens: ("fixed", (l0, l1, ...)) | ("uniform", lo, hi) | ("lognormal", mu, sigma, lo, hi)
+    num_blocks: physical pool size; None -> shared + ceil(1.25 * sum of private blocks)
+    max_len: the largest context the block table must hold (sets max_blocks_per_seq)
+    """
+
+    name: str
+    dtype: str  # "f32" | "bf16"
+    num_seqs: int
+    num_q_heads: int
+    num_kv_heads: int
+    head_dim: int
+    lens: tuple
+    max_len: int
+    q_len: int = 1
+    num_blocks: Optional[int] = None
+    shared_prefix_blocks: int = 0
+    write_new_tokens: bool = False
+    partition_size: int = 0
+    seed: int = 0
+    scale: Optional[float] = None  # None -> fp32(1/sqrt(head_dim))
+    pad: str = "valid"  # block-table padding: "valid" random in-range ids | "garbage"
+    poison: bool = False  # NaN in cache rows never read (unused blocks, rows >= L)
+    description: str = ""
+
+    @property
+    def group(self) -> int:
+        return self.num_q_heads // self.num_kv_heads
+
+    @property
+    def max_blocks_per_seq(self) -> int:
+        return (self.max_len + BLOCK_SIZE - 1) // BLOCK_SIZE
+
+    def with_(self, **kw) -> "Spec":
+        return replace(self, **kw)
+
+
+CONFIGS = {
+    "tiny-f32": Spec(
+        name="tiny-f32", dtype="f32", num_seqs=2, num_q_heads=4, num_kv_heads=2, head_dim=64,
+        lens=("fixed", (17, 40)), max_len=48, num_blocks=16, seed=0,
+        description="2 sequences (17, 40 tokens), 4 q heads / 2 kv heads, d=64, fp32, 16-block pool",
+    ),
+    "llama3-8b-decode": Spec(
+        name="llama3-8b-decode", dtype="bf16", num_seqs=64, num_q_heads=32, num_kv_heads=8, head_dim=128,
+        lens=("uniform", 512, 4096), max_len=4096, num_blocks=20000, write_new_tokens=True, seed=1,
+        description="Llama-3-8B-shaped layer: 32/8 heads, d=128, bf16, batch 64, L~U[512,4096], 20k-block pool, 64 new tokens written",
+    ),
+    "llama3-70b-decode": Spec(
+        name="llama3-70b-decode", dtype="bf16", num_seqs=256, num_q_heads=64, num_kv_heads=8, head_dim=128,
+        lens=("lognormal", math.log(1024.0) - 0.5, 1.0, 16, 8192), max_len=8192, seed=2,
+        description="Llama-3-70B-shaped layer: 64/8 heads, d=128, bf16, batch 256, L lognormal mean 1024 clipped to [16,8192]",
+    ),
+    "long-split": Spec(
+        name="long-split", dtype="bf16", num_seqs=8, num_q_heads=32, num_kv_heads=8, head_dim=128,
+        lens=("uniform", 32768, 131072), max_len=131072, partition_size=512, seed=3,
+        description="long contexts: 32/8 heads, d=128, bf16, batch 8, L~U[32768,131072], 512-token partitions + reduce",
+    ),
+    "spec-verify": Spec(
+        name="spec-verify", dtype="bf16", num_seqs=128, num_q_heads=64, num_kv_heads=8, head_dim=128,
+        lens=("uniform", 1024, 4096), max_len=4096, q_len=5, shared_prefix_blocks=32, write_new_tokens=True, seed=4,
+        description="speculative verify: 4 drafts + 1 = 5 query tokens, causal among them, 64/8 heads, d=128, bf16, batch 128, L~U[1024,4096], 32 shared prefix blocks, 640 new tokens written",
+    ),
+}
+
+CONFIG_ORDER = ["tiny-f32", "llama3-8b-decode", "llama3-70b-decode", "long-split", "spec-verify"]
+
+
+# ----------------------------------------------------------------------------
+# problems
+
+
+@dataclass
+class Problem:
+    spec: Spec
+    context_lens: np.ndarray  # int32 [S]; counts the q_len newest tokens
+    block_tables: np.ndarray  # int32 [S, max_blocks_per_seq]
+    q: np.ndarray  # [S*q_len, n_h, d]  float32 or uint16 (bf16 bits)
+    k_cache: np.ndarray  # [NB, 16, n_kv, d]  (before new tokens are written)
+    v_cache: np.ndarray
+    scale: np.float32
+    new_k: Optional[np.ndarray] = None  # [T, n_kv, d]
+    new_v: Optional[np.ndarray] = None
+    slot_mapping: Optional[np.ndarray] = None  # int64 [T]
+    extra: dict = field(default_factory=dict)
+
+    # convenience views of the spec
+    @property
+    def dtype(self) -> str:
+        return self.spec.dtype
+
+    @property
+    def num_seqs(self) -> int:
+        return self.spec.num_seqs
+
+    @property
+    def q_len(self) -> int:
+        return self.spec.q_len
+
+    @property
+    def num_q_heads(self) -> int:
+        return self.spec.num_q_heads
+
+    @property
+    def num_kv_heads(self) -> int:
+        return self.spec.num_kv_heads
+
+    @property
+    def head_dim(self) -> int:
+        return self.spec.head_dim
+
+    @property
+    def num_blocks(self) -> int:
+        return int(self.k_cache.shape[0])
+
+    @property
+    def max_blocks_per_seq(self) -> int:
+        return int(self.block_tables.shape[1])
+
+    @property
+    def partition_size(self) -> int:
+        return self.spec.partition_size
+
+    def as_float32(self, a: np.ndarray) -> np.ndarray:
+        return a if self.dtype == "f32" else bf16_bits_to_f32(a)
+
+
+def draw_lens(spec: Spec, rng: np.random.Generator) -> np.ndarray:
+    kind = spec.lens[0]
+    S = spec.num_seqs
+    if kind == "fixed":
+        vals = np.asarray(spec.lens[1], dtype=np.int64)
+        assert vals.size == S, "fixed lens must list one length per sequence"
+        lens = vals
+    elif kind == "uniform":
+        lo, hi = spec.lens[1], spec.lens[2]
+        lens = rng.integers(lo, hi, size=S, endpoint=True)
+    elif kind == "lognormal":
+        mu, sigma, lo, hi = spec.lens[1:5]
+        lens = np.clip(np.rint(rng.lognormal(mu, sigma, size=S)), lo, hi).astype(np.int64)
+    else:
+        raise ValueError(f"unknown length distribution {kind!r}")
+    assert lens.min() >= 1 and lens.max() <= spec.max_len
+    return lens.astype(np.int32)
+
+
+def make_problem(spec: Spec) -> Problem:
+    """Draw every input of one workload from spec.seed."""
+    if isinstance(spec, str):
+        spec = CONFIGS[spec]
+    rng = np.random.default_rng(spec.seed)
+    S, bs = spec.num_seqs, BLOCK_SIZE
+    lens = draw_lens(spec, rng)
+    assert lens.min() >= spec.q_len, "every context must hold its q_len newest tokens"
+    nblk = (lens.astype(np.int64) + bs - 1) // bs
+    shared = spec.shared_prefix_blocks
+    if shared:
+        assert (lens.astype(np.int64) - spec.q_len).min() >= shared * bs, "new tokens must land past the shared prefix"
+    private = nblk - shared
+    if spec.num_blocks is None:
+        NB = shared + int(math.ceil(1.25 * float(private.sum())))
+    else:
+        NB = spec.num_blocks
+    assert NB >= shared + int(private.sum()), "pool too small for the assigned blocks"
+
+    # block assignment: a seeded permutation of the pool, handed out in sequence order
+    perm = rng.permutation(NB).astype(np.int32)
+    MB = spec.max_blocks_per_seq
+    tables = np.empty((S, MB), dtype=np.int32)
+    if spec.pad == "valid":
+        tables[:] = rng.integers(0, NB, size=(S, MB), dtype=np.int32)
+    elif spec.pad == "garbage":
+        tables[:] = np.int32(0x7FFFFFF0)
+    else:
+        raise ValueError(spec.pad)
+    cursor = shared
+    for b in range(S):
+        tables[b, :shared] = perm[:shared]
+        n = int(private[b])
+        tables[b, shared:shared + n] = perm[cursor:cursor + n]
+        cursor += n
+
+    n_kv, d = spec.num_kv_heads, spec.head_dim
+    q = fill_normal((S * spec.q_len, spec.num_q_heads, d), spec.dtype, spec.seed, _STREAM_Q)
+    k_cache = fill_normal((NB, bs, n_kv, d), spec.dtype, spec.seed, _STREAM_K)
+    v_cache = fill_normal((NB, bs, n_kv, d), spec.dtype, spec.seed, _STREAM_V)
+
+    new_k = new_v = slots = None
+    if spec.write_new_tokens:
+        T = S * spec.q_len
+        new_k = fill_normal((T, n_kv, d), spec.dtype, spec.seed, _STREAM_NEWK)
+        new_v = fill_normal((T, n_kv, d), spec.dtype, spec.seed, _STREAM_NEWV)
+        slots = np.empty(T, dtype=np.int64)
+        for b in range(S):
+            for j in range(spec.q_len):
+                pos = int(lens[b]) - spec.q_len + j
+                slots[b * spec.q_len + j] = int(tables[b, pos // bs]) * bs + pos % bs
+
+    if spec.poison:
+        poison_unread(spec, lens, tables, k_cache, v_cache)
+
+    scale = np.float32(1.0 / math.sqrt(d)) if spec.scale is None else np.float32(spec.scale)
+    return Problem(spec=spec, context_lens=lens, block_tables=tables, q=q, k_cache=k_cache, v_cache=v_cache,
+                   scale=scale, new_k=new_k, new_v=new_v, slot_mapping=slots)
+
+
+def poison_unread(spec: Spec, lens, tables, k_cache, v_cache) -> None:
+    """Write NaN into every cache row that a correct kernel never reads."""
+    bs = BLOCK_SIZE
+    nan = BF16_QNAN_BITS if spec.dtype == "bf16" else F32_QNAN
+    used = np.zeros(k_cache.shape[0], dtype=bool)
+    for b in range(len(lens)):
+        nb = (int(lens[b]) + bs - 1) // bs
+        used[tables[b, :nb]] = True
+    k_cache[~used] = nan
+    v_cache[~used] = nan
+    for b in range(len(lens)):
+        L = int(lens[b])
+        nb = (L + bs - 1) // bs
+        tail = L - (nb - 1) * bs
+        if tail < bs:
+            last = tables[b, nb - 1]
+            k_cache[last, tail:] = nan
+            v_cache[last, tail:] = nan
+
+
+def permute_physical(problem: Problem, seed: int) -> Problem:
+    """The same logical problem with every physical block moved to a new id.
+
+    Pool contents move with their ids, and block tables and slots are rewritten,
+    so every sequence still sees the same tokens in the same logical order.
+    """
+    NB = problem.num_blocks
+    rng = np.random.default_rng(seed)
+    new_id = rng.permutation(NB).astype(np.int64)  # old id -> new id
+    k = np.empty_like(problem.k_cache)
+    v = np.empty_like(problem.v_cache)
+    k[new_id] = problem.k_cache
+    v[new_id] = problem.v_cache
+    tables = problem.block_tables.astype(np.int64)
+    in_range = (tables >= 0) & (tables < NB)
+    tables = np.where(in_range, new_id[np.clip(tables, 0, NB - 1)], tables).astype(np.int32)
+    slots = None
+    if problem.slot_mapping is not None:
+        s = problem.slot_mapping
+        slots = new_id[s // BLOCK_SIZE] * BLOCK_SIZE + s % BLOCK_SIZE
+    return replace(problem, k_cache=k, v_cache=v, block_tables=tables, slot_mapping=slots)
+
+
+def algorithmic_bytes(problem: Problem) -> dict:
+    """KV and Q bytes one decode call must read: each KV row once per (sequence, kv head).
+
+    'unique' counts physical rows once when sequences share prefix blocks.
+    """
+    esz = 4 if problem.dtype == "f32" else 2
+    row = problem.num_kv_heads * problem.head_dim * esz  # one token's K (or V) over all kv heads
+    logical_tokens = int(problem.context_lens.astype(np.int64).sum())
+    shared_tokens = problem.spec.shared_prefix_blocks * BLOCK_SIZE
+    unique_tokens = logical_tokens - max(0, problem.num_seqs - 1) * shared_tokens if shared_tokens else logical_tokens
+    q_bytes = problem.num_seqs * problem.q_len * problem.num_q_heads * problem.head_dim * esz
+    return {
+        "kv_logical": 2 * logical_tokens * row,
+        "kv_unique": 2 * unique_tokens * row,
+        "q": q_bytes,
+        "out": q_bytes,
+        "tokens": problem.num_seqs * problem.q_len,
+    }
+
+
+def kv_bytes_per_token(layers: int, kv_heads: int, head_dim: int, bytes_per_value: int) -> int:
+    """K and V bytes per token: 2 * layers * kv_heads * head_dim * bytes (the pages' KV sizing)."""
+    return 2 * layers * kv_heads * head_dim * bytes_per_value
+
+
+def kv_bytes_per_block(block_tokens: int, layers: int, kv_heads: int, head_dim: int, bytes_per_value: int) -> int:
+    return block_tokens * kv_bytes_per_token(layers, kv_heads, head_dim, bytes_per_value)
