@@ -1,0 +1,298 @@
+#!/usr/bin/env python3
+"""Benchmark of the paged decode-attention path on one MI355X.
+
+One step = the whole path over one batch: pa_cache_write of the batch's new
+tokens, pa_decode, and pa_reduce when the context is split.  The inputs are
+the seeded synthetic Llama-3-8B-shaped decode layer (64 sequences, 32 query
+heads / 8 KV heads, head_dim 128, bf16, contexts uniform in [512, 4096], a
+20,000-block pool), resident in HBM before timing starts.
+
+Prints one JSON line:
+  value          tokens/s of whole steps (num_seqs * q_len tokens per step)
+  roofline       the decode kernel: algorithmic KV + Q bytes per launch over its
+                 average launch time (HIP events on the launch stream) against
+                 the 8 TB/s HBM peak; traffic from the committed counter summary
+  cpu_baseline   the fp64 oracle on a bounded sample of the same workload
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config NAME] [--partition P]
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import workloads as wl  # noqa: E402
+
+HBM_PEAK_GBPS = 8000.0
+DEFAULT_CONFIG = "llama3-8b-decode"
+METRIC = "decode tokens/s and achieved KV HBM GB/s (% of MI355X peak) per pa_decode call"
+KERNEL_SOURCES = ("decode_valu.hip", "pa_device.h")
+
+
+def partition_for(p: wl.Problem) -> int:
+    """Launch configuration: the context split used for each workload.
+
+    Split into 512-token partitions (32 blocks, one workgroup each) whenever a
+    context is longer than one partition, so that the grid has thousands of
+    workgroups and ragged lengths balance; short-context batches run in one pass.
+    """
+    if p.partition_size:
+        return p.partition_size
+    return 512 if int(p.context_lens.max()) > 512 else 0
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "paged_kv_attention_decode_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def to_dev(a, torch):
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint16:
+        return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
+    return torch.from_numpy(a).cuda()
+
+
+class Resident:
+    """The workload in HBM and the three calls of one step."""
+
+    def __init__(self, p: wl.Problem, partition: int, torch):
+        import paged_kv_attention_decode_amd as pa
+
+        self.pa, self.p, self.partition, self.torch = pa, p, partition, torch
+        self.q = to_dev(p.q, torch)
+        self.k_cache = to_dev(p.k_cache, torch)
+        self.v_cache = to_dev(p.v_cache, torch)
+        self.tables = torch.from_numpy(p.block_tables).cuda()
+        self.lens = torch.from_numpy(p.context_lens).cuda()
+        self.new_k = to_dev(p.new_k, torch) if p.new_k is not None else None
+        self.new_v = to_dev(p.new_v, torch) if p.new_v is not None else None
+        self.slots = torch.from_numpy(p.slot_mapping).cuda() if p.slot_mapping is not None else None
+        self.out = torch.empty_like(self.q)
+        self.ws = None
+        if partition:
+            n = pa.decode_workspace_size(p.num_seqs, p.q_len, p.num_q_heads, p.head_dim, p.max_blocks_per_seq,
+                                         partition)
+            self.ws = torch.empty(n, dtype=torch.uint8, device="cuda")
+
+    def write(self):
+        if self.new_k is not None:
+            self.pa.cache_write(self.new_k, self.new_v, self.k_cache, self.v_cache, self.slots)
+
+    def decode(self):
+        p = self.p
+        if self.partition:
+            self.pa.decode(self.q, self.k_cache, self.v_cache, self.tables, self.lens, float(p.scale), p.q_len,
+                           self.partition, workspace=self.ws)
+        else:
+            self.pa.decode(self.q, self.k_cache, self.v_cache, self.tables, self.lens, float(p.scale), p.q_len, 0,
+                           out=self.out)
+
+    def reduce(self):
+        if self.partition:
+            p = self.p
+            self.pa.reduce(self.out, self.ws, self.lens, p.q_len, p.max_blocks_per_seq, self.partition)
+
+    def step(self):
+        self.write()
+        self.decode()
+        self.reduce()
+
+
+def load_traffic(workload: str, decode_s: float):
+    """HBM traffic of the decode kernel from the committed counter summary, if it
+    was taken on the current kernel sources."""
+    path = os.path.join(ROOT, "profiles", f"decode_traffic_{workload}.json")
+    if not os.path.exists(path):
+        return None, None
+    with open(path) as f:
+        t = json.load(f)
+    if t.get("kernel_source_sha") != kernel_source_hash():
+        return None, "kernel changed since the counters were taken"
+    per_launch = float(t["fetch_bytes_per_launch"]) + float(t["write_bytes_per_launch"])
+    return per_launch / decode_s / 1e9, per_launch
+
+
+def cpu_baseline(p: wl.Problem, gpu_out, budget_s: float = 12.0):
+    """The oracle, untuned, on the first sequences of the same workload until the
+    time budget is spent; scaled to tokens/s of the whole batch."""
+    import oracle
+    from threadpoolctl import threadpool_info
+
+    t0 = time.perf_counter()
+    kc, vc = (oracle.cache_write(p.k_cache, p.v_cache, p.new_k, p.new_v, p.slot_mapping)
+              if p.new_k is not None else (p.k_cache, p.v_cache))
+    t_write = time.perf_counter() - t0
+    n = 0
+    worst = 0.0
+    t0 = time.perf_counter()
+    while n < p.num_seqs and time.perf_counter() - t0 < budget_s:
+        rows = [(n, j, h) for j in range(p.q_len) for h in range(p.num_q_heads)]
+        ref = oracle.paged_decode_rows(p.q, kc, vc, p.block_tables, p.context_lens, p.scale, p.q_len, p.dtype, rows)
+        if gpu_out is not None:
+            got = np.stack([gpu_out[n * p.q_len + j, h] for (_, j, h) in rows])
+            worst = max(worst, float(np.max(np.abs(got - ref))))
+        n += 1
+    t_attn = time.perf_counter() - t0
+    est = t_write + t_attn * p.num_seqs / n
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    return {
+        "value": p.num_seqs * p.q_len / est,
+        "unit": "tokens/s",
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": (f"fp64 NumPy oracle: cache write of all {len(p.slot_mapping) if p.slot_mapping is not None else 0} "
+                   f"new tokens ({t_write:.2f} s) plus attention of the first {n} of {p.num_seqs} sequences "
+                   f"x {p.num_q_heads} heads ({t_attn:.2f} s), scaled to the whole batch"),
+        "max_abs_vs_gpu": worst,
+    }
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--config", default=DEFAULT_CONFIG, choices=list(wl.CONFIGS))
+    ap.add_argument("--partition", type=int, default=None, help="override the context split (0 = one pass)")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the cpu_baseline leg")
+    ap.add_argument("--cold", type=int, default=20, help="launches timed one by one after a 1 GiB cache flush")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="also run a 1 GiB device copy (for scaling memory counters)")
+    args = ap.parse_args(argv)
+
+    if args.gpus != 1:
+        print(json.dumps({"error": "this benchmark runs on one GPU only; every figure is for one MI355X",
+                          "n_gpus_requested": args.gpus}))
+        return 2
+
+    import torch
+
+    if not torch.cuda.is_available():
+        print(json.dumps({"error": "no GPU visible"}))
+        return 1
+    torch.cuda.set_device(0)
+
+    spec = wl.CONFIGS[args.config]
+    p = wl.make_problem(spec)
+    partition = partition_for(p) if args.partition is None else args.partition
+    r = Resident(p, partition, torch)
+
+    for _ in range(max(0, args.warmup)):
+        r.step()
+    torch.cuda.synchronize()
+
+    K = args.steps
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(K)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(K):
+        e = ev[k]
+        e[0].record()
+        r.write()
+        e[1].record()
+        r.decode()
+        e[2].record()
+        r.reduce()
+        e[3].record()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1e3 / K
+    write_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
+    decode_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in ev]))
+    reduce_ms = float(np.mean([e[2].elapsed_time(e[3]) for e in ev]))
+    gpu_ms = float(np.mean([e[0].elapsed_time(e[3]) for e in ev]))
+
+    # cold-cache decode launches: a 1 GiB write between launches evicts L2 and MALL
+    cold_ms = None
+    if args.cold > 0:
+        scratch = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
+        times = []
+        for _ in range(args.cold):
+            scratch.fill_(1.0)
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            r.decode()
+            b.record()
+            r.reduce()
+            torch.cuda.synchronize()
+            times.append(a.elapsed_time(b))
+        cold_ms = float(np.median(times))
+        del scratch
+
+    if args.calibrate_copy:
+        src = torch.empty(1 << 28, dtype=torch.float32, device="cuda").fill_(2.0)
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    out = r.out.float().cpu().numpy().astype(np.float64)
+    finite = bool(np.isfinite(out).all())
+
+    ab = wl.algorithmic_bytes(p)
+    kv_bytes = ab["kv_unique"] + ab["q"]
+    tokens = ab["tokens"]
+    decode_s = decode_ms / 1e3
+    achieved = kv_bytes / decode_s / 1e9
+    traffic, traffic_bytes = load_traffic(args.config, decode_s)
+    roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBPS, 4),
+            "traffic": round(traffic, 1) if isinstance(traffic, float) else None,
+            "kernel": "decode_valu_kernel<bf16,128,4>" if p.dtype == "bf16" else "decode_valu_kernel",
+            "algorithmic_bytes_per_launch": kv_bytes,
+            "avg_launch_us": round(decode_ms * 1e3, 2)}
+    if isinstance(traffic_bytes, str):
+        roof["traffic_note"] = traffic_bytes
+    elif traffic_bytes is not None:
+        roof["traffic_bytes_per_launch"] = traffic_bytes
+
+    res = {
+        "metric": METRIC,
+        "value": round(tokens / (ms_per_step / 1e3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": p.dtype,
+        "data": "synthetic",
+        "config": {
+            "workload": args.config, "num_seqs": p.num_seqs, "num_q_heads": p.num_q_heads,
+            "num_kv_heads": p.num_kv_heads, "head_dim": p.head_dim, "block_size": 16, "q_len": p.q_len,
+            "context_tokens": int(p.context_lens.sum()), "num_blocks": p.num_blocks,
+            "new_tokens_written": 0 if p.slot_mapping is None else int(len(p.slot_mapping)),
+            "partition_size": partition, "seed": spec.seed,
+        },
+        "kv_hbm_gbps_step": round(kv_bytes / (ms_per_step / 1e3) / 1e9, 1),
+        "breakdown_us": {"cache_write": round(write_ms * 1e3, 2), "decode": round(decode_ms * 1e3, 2),
+                         "reduce": round(reduce_ms * 1e3, 2), "gpu_step": round(gpu_ms * 1e3, 2),
+                         "decode_plus_reduce_cold": None if cold_ms is None else round(cold_ms * 1e3, 2)},
+        "roofline": roof,
+        "outputs_finite": finite,
+    }
+    if not args.no_cpu:
+        res["cpu_baseline"] = cpu_baseline(p, out)
+    print(json.dumps(res), flush=True)
+    return 0 if finite else 1
+
+
+if __name__ == "__main__":
+    sys.exit(main())

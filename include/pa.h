@@ -1,0 +1,167 @@
+/*
+ * pa.h - paged KV-cache decode attention for AMD Instinct MI355X (gfx950).
+ *
+ * A C ABI over hand-written HIP kernels.  Three operations:
+ *
+ *   pa_cache_write  store the K/V rows of new tokens into their cache slots;
+ *   pa_decode       attention of the newest q_len tokens of every sequence over
+ *                   its paged KV cache, either in one pass or as per-partition
+ *                   partials (split context);
+ *   pa_reduce       merge the partials of a split pa_decode into the output.
+ *
+ * Sources of the definitions (the web pages this library implements):
+ *   - per layer, K and V are each stored as [num_blocks, block_size,
+ *     num_kv_heads, head_dim] ("LLM Inference Serving", systeminternals.dev,
+ *     the passage on the per-layer cache shape);
+ *   - a sequence's block table maps logical block i (tokens 16i .. 16i+15) to
+ *     a physical block id; the kernel follows the table and reads keys and
+ *     values one block at a time ("LLM serving: KV cache, batching, paged
+ *     attention and quantization", learn.mohebi.ai, section 3.5);
+ *   - a generated token is appended in place in the last block while it has
+ *     room (systeminternals.dev, the Sequence / block_table sketch);
+ *   - decode attention: q^T K, softmax, weighted sum of V per query head;
+ *     n_h / n_kv query heads share one KV head (learn.mohebi.ai, section 3.3
+ *     and the notation of section 3);
+ *   - speculative verify scores all K+1 positions in one pass under a causal
+ *     mask ("07 - Inference", lourdhu02.github.io, section 3);
+ *   - split context: chunks produce partials (m, l, acc) that a second small
+ *     kernel merges with the online-softmax rescaling rule (lourdhu02.github.io,
+ *     section 5.3 "Decode attention and FlashDecoding").
+ *
+ * Conventions shared by every entry point:
+ *   - Every data pointer is a DEVICE pointer owned by the caller.  The library
+ *     never allocates, frees or synchronizes; it enqueues kernels on `stream`
+ *     (a hipStream_t; NULL means the default stream) and returns.
+ *   - Tensors are dense, row-major, and 16-byte aligned.
+ *   - dtype selects the element type of q, out, k, v and the caches:
+ *     PA_F32 (IEEE binary32) or PA_BF16 (bfloat16).  Arithmetic is fp32.
+ *   - block_size must be 16; head_dim must be 64 or 128.
+ *   - Arguments are validated on the host before anything is launched; an
+ *     invalid argument returns an error status and launches nothing.
+ *   - Values that live in device memory (context lengths, block ids, slots)
+ *     cannot be checked on the host without a synchronization.  The kernels
+ *     never access memory out of bounds because of them: a slot outside the
+ *     pool is skipped, a block id outside [0, num_blocks) contributes no
+ *     tokens, a context length is clamped to max_blocks_per_seq * block_size.
+ *     Such values are still caller errors and give unspecified results.
+ *   - Stateless and re-entrant; no global state.
+ */
+#ifndef PA_H
+#define PA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  PA_OK = 0,
+  PA_ERR_NULL = 1,        /* a required pointer is NULL */
+  PA_ERR_SHAPE = 2,       /* sizes inconsistent or out of range */
+  PA_ERR_UNSUPPORTED = 3, /* valid but not implemented (head_dim, block_size, rows per KV head, dtype) */
+  PA_ERR_WORKSPACE = 4,   /* workspace missing or smaller than pa_decode_workspace_size() */
+  PA_ERR_HIP = 5          /* the HIP runtime reported an error at launch */
+} pa_status;
+
+typedef enum { PA_F32 = 0, PA_BF16 = 1 } pa_dtype;
+
+/*
+ * pa_cache_write - write the K and V rows of new tokens into the paged caches.
+ *
+ *   k, v          [num_tokens, num_kv_heads, head_dim]  new keys / values
+ *   k_cache,      [num_blocks, block_size, num_kv_heads, head_dim]
+ *   v_cache
+ *   slot_mapping  int64 [num_tokens]: slot = physical_block * block_size + row.
+ *                 A negative slot skips the token; a slot >= num_blocks *
+ *                 block_size is skipped as well (caller error).  Two tokens with
+ *                 the same slot is a caller error (which one lands is unspecified).
+ *
+ * The rows are copied as raw bits (bit-exact, NaN payloads included); nothing
+ * else in the caches changes.  num_tokens == 0 is valid and launches nothing.
+ */
+pa_status pa_cache_write(const void* k, const void* v, void* k_cache, void* v_cache,
+                         const int64_t* slot_mapping, int32_t num_tokens, int32_t num_blocks,
+                         int32_t block_size, int32_t num_kv_heads, int32_t head_dim, pa_dtype dtype,
+                         void* stream);
+
+/*
+ * pa_decode - paged attention of the q_len newest tokens of each sequence.
+ *
+ *   out           [num_seqs * q_len, num_q_heads, head_dim], dtype.  Written when
+ *                 partition_size == 0; untouched otherwise (may be NULL then).
+ *   q             [num_seqs * q_len, num_q_heads, head_dim], dtype.  Row
+ *                 b * q_len + j is query token j of sequence b.
+ *   k_cache,      [num_blocks, block_size, num_kv_heads, head_dim], dtype
+ *   v_cache
+ *   block_tables  int32 [num_seqs, max_blocks_per_seq]; entry i of row b is the
+ *                 physical block holding tokens i*block_size .. +block_size-1 of
+ *                 sequence b.  Entries at or past ceil(L_b / block_size) are never read.
+ *   context_lens  int32 [num_seqs]; L_b counts the q_len new tokens, which must
+ *                 already be in the cache.  Query token j sits at position
+ *                 L_b - q_len + j and attends to positions 0 .. L_b - q_len + j
+ *                 (causal among the new tokens; all L_b positions when q_len == 1).
+ *                 A query row with no visible position gets zeros.
+ *   scale         softmax scale applied to q.k (typically 1/sqrt(head_dim)).
+ *   q_len         1 .. 8 new tokens per sequence.
+ *   num_q_heads   a multiple of num_kv_heads; query head h reads KV head
+ *                 h / (num_q_heads / num_kv_heads).  Rows per KV head
+ *                 (num_q_heads / num_kv_heads) * q_len must be <= 8 for PA_F32 and
+ *                 <= 64 for PA_BF16.
+ *   partition_size 0: one pass, writes out.  Otherwise a positive multiple of
+ *                 block_size: the context is split into partitions
+ *                 [p*partition_size, (p+1)*partition_size), and for every query row
+ *                 the partition's partial result is written to the workspace;
+ *                 pa_reduce then produces out.
+ *   workspace     device buffer of at least pa_decode_workspace_size(...) bytes
+ *                 (only used, and only required, when partition_size > 0).  Its
+ *                 contents are private to pa_decode / pa_reduce.
+ *
+ * Results depend only on the logical contents (bitwise deterministic from run
+ * to run, independent of the physical block ids and of the other sequences).
+ */
+pa_status pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache,
+                    const int32_t* block_tables, const int32_t* context_lens, float scale, int32_t q_len,
+                    int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                    int32_t num_blocks, int32_t block_size, int32_t max_blocks_per_seq,
+                    int32_t partition_size, void* workspace, size_t workspace_bytes, pa_dtype dtype,
+                    void* stream);
+
+/*
+ * pa_decode_workspace_size - bytes of workspace a split pa_decode needs.
+ *
+ * With P = ceil(max_blocks_per_seq * block_size / partition_size) partitions
+ * and R = num_seqs * q_len * num_q_heads query rows the workspace holds fp32
+ * max_logits[R][P], exp_sums[R][P] and partial outputs [R][P][head_dim], each
+ * region 256-byte aligned.  Returns 0 when partition_size <= 0 or the sizes are
+ * invalid.
+ */
+size_t pa_decode_workspace_size(int32_t num_seqs, int32_t q_len, int32_t num_q_heads, int32_t head_dim,
+                                int32_t max_blocks_per_seq, int32_t block_size, int32_t partition_size);
+
+/*
+ * pa_reduce - merge the per-partition partials of a split pa_decode into out.
+ *
+ * The arguments must repeat those of the pa_decode call that filled the
+ * workspace (same shapes, partition_size, context_lens), on the same stream or
+ * after it.  For each query row: M = max over partitions of m_p,
+ * w_p = l_p * 2^(m_p - M), out = sum_p w_p * o_p / sum_p w_p, over the
+ * partitions that hold at least one position the row may see.
+ */
+pa_status pa_reduce(void* out, const void* workspace, size_t workspace_bytes, const int32_t* context_lens,
+                    int32_t num_seqs, int32_t q_len, int32_t num_q_heads, int32_t head_dim,
+                    int32_t max_blocks_per_seq, int32_t block_size, int32_t partition_size, pa_dtype dtype,
+                    void* stream);
+
+/* A static, human-readable description of a status code. */
+const char* pa_status_string(pa_status status);
+
+/* Library version as major * 10000 + minor * 100 + patch. */
+int32_t pa_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PA_H */

@@ -1,0 +1,223 @@
+"""Paged KV-cache decode attention for AMD Instinct MI355X (gfx950).
+
+A thin ctypes binding of libpa.so, the C ABI declared in include/pa.h.  Every
+function here only checks and marshals arguments (device pointers, sizes,
+torch's current HIP stream) and calls the library; all arithmetic runs in the
+HIP kernels.  There is no fallback: if libpa.so is missing or a tensor is not
+on the GPU, the call raises.
+
+    cache_write(k, v, k_cache, v_cache, slot_mapping)
+    decode(q, k_cache, v_cache, block_tables, context_lens, scale, q_len, ...)
+    reduce(out, workspace, context_lens, ...)
+    decode_workspace_size(...)
+    paged_attention(...)   # decode, plus reduce when the context is split
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+__all__ = [
+    "PA_F32", "PA_BF16", "PagedAttentionError", "library_path", "load_library", "status_string", "version",
+    "cache_write", "decode", "reduce", "decode_workspace_size", "paged_attention", "SYMBOLS",
+]
+
+PA_F32, PA_BF16 = 0, 1
+BLOCK_SIZE = 16
+SYMBOLS = ("pa_cache_write", "pa_decode", "pa_decode_workspace_size", "pa_reduce", "pa_status_string", "pa_version")
+_STATUS = {0: "PA_OK", 1: "PA_ERR_NULL", 2: "PA_ERR_SHAPE", 3: "PA_ERR_UNSUPPORTED", 4: "PA_ERR_WORKSPACE",
+           5: "PA_ERR_HIP"}
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_lib = None
+
+
+class PagedAttentionError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {status_string(status)}")
+
+
+def library_path() -> str:
+    return os.environ.get("PA_LIBRARY", os.path.join(_HERE, "libpa.so"))
+
+
+def load_library():
+    """Load libpa.so once; raise if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    path = library_path()
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with `python -m paged_kv_attention_decode_amd.build`")
+    lib = ctypes.CDLL(path)
+    i32, i64, f32, sz, vp = ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t, ctypes.c_void_p
+    lib.pa_cache_write.restype = ctypes.c_int
+    lib.pa_cache_write.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, ctypes.c_int, vp]
+    lib.pa_decode.restype = ctypes.c_int
+    lib.pa_decode.argtypes = [vp, vp, vp, vp, vp, vp, f32, i32, i32, i32, i32, i32, i32, i32, i32, i32, vp, sz,
+                              ctypes.c_int, vp]
+    lib.pa_decode_workspace_size.restype = sz
+    lib.pa_decode_workspace_size.argtypes = [i32] * 7
+    lib.pa_reduce.restype = ctypes.c_int
+    lib.pa_reduce.argtypes = [vp, vp, sz, vp, i32, i32, i32, i32, i32, i32, i32, ctypes.c_int, vp]
+    lib.pa_status_string.restype = ctypes.c_char_p
+    lib.pa_status_string.argtypes = [ctypes.c_int]
+    lib.pa_version.restype = i32
+    lib.pa_version.argtypes = []
+    del i64
+    _lib = lib
+    return lib
+
+
+def status_string(status: int) -> str:
+    return load_library().pa_status_string(status).decode()
+
+
+def version() -> int:
+    return int(load_library().pa_version())
+
+
+# ---------------------------------------------------------------------------
+# marshalling helpers
+
+
+def _torch():
+    import torch
+
+    return torch
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.float32:
+        return PA_F32
+    if t.dtype == torch.bfloat16:
+        return PA_BF16
+    raise TypeError(f"unsupported dtype {t.dtype}; expected float32 or bfloat16")
+
+
+def _dev(t, name, dtype=None, ndim=None):
+    torch = _torch()
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be on the GPU (got {t.device})")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dimensions, got shape {tuple(t.shape)}")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream=None) -> ctypes.c_void_p:
+    torch = _torch()
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _check(status: int, where: str):
+    if status != 0:
+        raise PagedAttentionError(status, where)
+
+
+# ---------------------------------------------------------------------------
+# the entry points
+
+
+def cache_write(k, v, k_cache, v_cache, slot_mapping, stream=None) -> None:
+    """pa_cache_write: store token t's K/V rows at flat slot slot_mapping[t] (negative = skip)."""
+    torch = _torch()
+    pk = _dev(k, "k", ndim=3)
+    pv = _dev(v, "v", k.dtype, 3)
+    pkc = _dev(k_cache, "k_cache", k.dtype, 4)
+    pvc = _dev(v_cache, "v_cache", k.dtype, 4)
+    ps = _dev(slot_mapping, "slot_mapping", torch.int64, 1)
+    T, n_kv, d = k.shape
+    if v.shape != k.shape or k_cache.shape != v_cache.shape or tuple(k_cache.shape[2:]) != (n_kv, d):
+        raise ValueError("k/v must be [T, n_kv, d] and the caches [num_blocks, block_size, n_kv, d]")
+    if slot_mapping.shape[0] != T:
+        raise ValueError("slot_mapping must hold one slot per token")
+    st = load_library().pa_cache_write(pk, pv, pkc, pvc, ps, T, k_cache.shape[0], k_cache.shape[1], n_kv, d,
+                                       _dtype_code(k), _stream(stream))
+    _check(st, "pa_cache_write")
+
+
+def decode_workspace_size(num_seqs, q_len, num_q_heads, head_dim, max_blocks_per_seq, partition_size,
+                          block_size=BLOCK_SIZE) -> int:
+    return int(load_library().pa_decode_workspace_size(num_seqs, q_len, num_q_heads, head_dim, max_blocks_per_seq,
+                                                       block_size, partition_size))
+
+
+def _decode_shapes(q, k_cache, block_tables, context_lens, q_len):
+    torch = _torch()
+    if q.dim() != 3 or k_cache.dim() != 4:
+        raise ValueError("q must be [S*q_len, n_h, d] and the caches [num_blocks, block_size, n_kv, d]")
+    S = block_tables.shape[0]
+    if q.shape[0] != S * q_len:
+        raise ValueError(f"q holds {q.shape[0]} rows; expected num_seqs * q_len = {S * q_len}")
+    if context_lens.shape != (S,) or context_lens.dtype != torch.int32 or block_tables.dtype != torch.int32:
+        raise ValueError("block_tables must be int32 [S, max_blocks] and context_lens int32 [S]")
+    return S
+
+
+def decode(q, k_cache, v_cache, block_tables, context_lens, scale: float, q_len: int = 1, partition_size: int = 0,
+           out=None, workspace=None, stream=None):
+    """pa_decode.  partition_size == 0: returns out.  Otherwise fills the workspace
+    with per-partition partials (allocated here if not given) and returns it."""
+    torch = _torch()
+    S = _decode_shapes(q, k_cache, block_tables, context_lens, q_len)
+    n_h, d = q.shape[1], q.shape[2]
+    NB, bs, n_kv = k_cache.shape[0], k_cache.shape[1], k_cache.shape[2]
+    MB = block_tables.shape[1]
+    args_common = (_dev(q, "q", ndim=3), _dev(k_cache, "k_cache", q.dtype, 4), _dev(v_cache, "v_cache", q.dtype, 4),
+                   _dev(block_tables, "block_tables", torch.int32, 2), _dev(context_lens, "context_lens", torch.int32, 1))
+    if v_cache.shape != k_cache.shape:
+        raise ValueError("k_cache and v_cache must have the same shape")
+    if partition_size == 0:
+        if out is None:
+            out = torch.empty_like(q)
+        pout = _dev(out, "out", q.dtype, 3)
+        if out.shape != q.shape:
+            raise ValueError("out must have q's shape")
+        st = load_library().pa_decode(pout, *args_common, float(scale), q_len, S, n_h, n_kv, d, NB, bs, MB, 0,
+                                      None, 0, _dtype_code(q), _stream(stream))
+        _check(st, "pa_decode")
+        return out
+    need = decode_workspace_size(S, q_len, n_h, d, MB, partition_size, bs)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    pws = _dev(workspace, "workspace", torch.uint8, 1)
+    st = load_library().pa_decode(None, *args_common, float(scale), q_len, S, n_h, n_kv, d, NB, bs, MB,
+                                  partition_size, pws, workspace.numel(), _dtype_code(q), _stream(stream))
+    _check(st, "pa_decode")
+    return workspace
+
+
+def reduce(out, workspace, context_lens, q_len: int, max_blocks_per_seq: int, partition_size: int, stream=None):
+    """pa_reduce: merge the partials of a split decode into out [S*q_len, n_h, d]."""
+    torch = _torch()
+    S = context_lens.shape[0]
+    n_h, d = out.shape[1], out.shape[2]
+    st = load_library().pa_reduce(_dev(out, "out", ndim=3), _dev(workspace, "workspace", torch.uint8, 1),
+                                  workspace.numel(), _dev(context_lens, "context_lens", torch.int32, 1), S, q_len,
+                                  n_h, d, max_blocks_per_seq, BLOCK_SIZE, partition_size, _dtype_code(out),
+                                  _stream(stream))
+    _check(st, "pa_reduce")
+    return out
+
+
+def paged_attention(q, k_cache, v_cache, block_tables, context_lens, scale: float, q_len: int = 1,
+                    partition_size: int = 0, out=None, workspace=None, stream=None):
+    """The whole attention step: pa_decode, followed by pa_reduce when partition_size > 0."""
+    torch = _torch()
+    if partition_size == 0:
+        return decode(q, k_cache, v_cache, block_tables, context_lens, scale, q_len, 0, out, None, stream)
+    ws = decode(q, k_cache, v_cache, block_tables, context_lens, scale, q_len, partition_size, None, workspace, stream)
+    if out is None:
+        out = torch.empty_like(q)
+    return reduce(out, ws, context_lens, q_len, block_tables.shape[1], partition_size, stream)

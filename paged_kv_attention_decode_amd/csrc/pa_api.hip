@@ -1,0 +1,188 @@
+// C ABI of the paged-attention library: argument validation, kernel choice,
+// launch.  Declarations and contracts are in include/pa.h.
+#include "pa.h"
+
+#include <hip/hip_runtime.h>
+
+#include "pa_kernels.h"
+
+namespace {
+
+constexpr int kBlock = 16;
+constexpr size_t kAlign = 256;
+constexpr int kMaxRowsF32 = 8;
+constexpr int kMaxRowsBF16 = 8;  // raised to 64 once the matrix-core kernel is in
+constexpr int kMaxRowsValu = 8;  // beyond this the matrix-core kernel takes bf16 inputs
+
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+struct WsLayout {
+  size_t m_off, l_off, o_off, total;
+  int parts;
+};
+
+bool workspace_layout(int32_t S, int32_t q_len, int32_t n_h, int32_t D, int32_t MB, int32_t bs, int32_t ps,
+                      WsLayout* w) {
+  if (S < 0 || q_len <= 0 || n_h <= 0 || D <= 0 || MB <= 0 || bs <= 0 || ps <= 0 || ps % bs != 0) return false;
+  const size_t ctx = (size_t)MB * bs;
+  const size_t parts = (ctx + ps - 1) / ps;
+  if (parts > 0x7fffffff) return false;
+  const size_t rows = (size_t)S * q_len * n_h;
+  const size_t stats = align_up(rows * parts * sizeof(float));
+  w->parts = (int)parts;
+  w->m_off = 0;
+  w->l_off = stats;
+  w->o_off = 2 * stats;
+  w->total = 2 * stats + align_up(rows * parts * (size_t)D * sizeof(float));
+  return true;
+}
+
+pa_status from_hip(hipError_t e) { return e == hipSuccess ? PA_OK : PA_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+const char* pa_status_string(pa_status s) {
+  switch (s) {
+    case PA_OK: return "PA_OK: success";
+    case PA_ERR_NULL: return "PA_ERR_NULL: a required pointer is NULL";
+    case PA_ERR_SHAPE: return "PA_ERR_SHAPE: sizes inconsistent, out of range, or a pointer not 16-byte aligned";
+    case PA_ERR_UNSUPPORTED:
+      return "PA_ERR_UNSUPPORTED: head_dim must be 64 or 128, block_size 16, rows per KV head <= 8 (fp32) or "
+             "<= 64 (bf16), dtype PA_F32 or PA_BF16";
+    case PA_ERR_WORKSPACE: return "PA_ERR_WORKSPACE: workspace missing or smaller than pa_decode_workspace_size()";
+    case PA_ERR_HIP: return "PA_ERR_HIP: the HIP runtime reported an error at launch";
+  }
+  return "unknown pa_status";
+}
+
+int32_t pa_version(void) { return 10000; }
+
+pa_status pa_cache_write(const void* k, const void* v, void* k_cache, void* v_cache, const int64_t* slot_mapping,
+                         int32_t num_tokens, int32_t num_blocks, int32_t block_size, int32_t num_kv_heads,
+                         int32_t head_dim, pa_dtype dtype, void* stream) {
+  if (num_tokens < 0 || num_blocks <= 0 || num_kv_heads <= 0) return PA_ERR_SHAPE;
+  if (dtype != PA_F32 && dtype != PA_BF16) return PA_ERR_UNSUPPORTED;
+  if (block_size != kBlock || (head_dim != 64 && head_dim != 128)) return PA_ERR_UNSUPPORTED;
+  if (num_tokens == 0) return PA_OK;
+  if (!k || !v || !k_cache || !v_cache || !slot_mapping) return PA_ERR_NULL;
+  if (!aligned16(k) || !aligned16(v) || !aligned16(k_cache) || !aligned16(v_cache)) return PA_ERR_SHAPE;
+  const size_t esz = dtype == PA_F32 ? 4 : 2;
+  const size_t row_bytes = (size_t)num_kv_heads * head_dim * esz;
+  if (row_bytes / 16 > 0x7fffffff || 2 * (row_bytes / 16) * (size_t)num_tokens / 256 > 0x7fffffff)
+    return PA_ERR_SHAPE;
+  pa::CacheWriteParams p;
+  p.k = k;
+  p.v = v;
+  p.k_cache = k_cache;
+  p.v_cache = v_cache;
+  p.slots = slot_mapping;
+  p.num_tokens = num_tokens;
+  p.num_blocks = num_blocks;
+  p.row_chunks = (int)(row_bytes / 16);
+  return from_hip(pa::launch_cache_write(p, static_cast<hipStream_t>(stream)));
+}
+
+size_t pa_decode_workspace_size(int32_t num_seqs, int32_t q_len, int32_t num_q_heads, int32_t head_dim,
+                                int32_t max_blocks_per_seq, int32_t block_size, int32_t partition_size) {
+  WsLayout w;
+  if (!workspace_layout(num_seqs, q_len, num_q_heads, head_dim, max_blocks_per_seq, block_size, partition_size, &w))
+    return 0;
+  return w.total;
+}
+
+pa_status pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache,
+                    const int32_t* block_tables, const int32_t* context_lens, float scale, int32_t q_len,
+                    int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                    int32_t num_blocks, int32_t block_size, int32_t max_blocks_per_seq, int32_t partition_size,
+                    void* workspace, size_t workspace_bytes, pa_dtype dtype, void* stream) {
+  if (dtype != PA_F32 && dtype != PA_BF16) return PA_ERR_UNSUPPORTED;
+  if (block_size != kBlock || (head_dim != 64 && head_dim != 128)) return PA_ERR_UNSUPPORTED;
+  if (num_seqs < 0 || q_len < 1 || q_len > 8 || num_q_heads <= 0 || num_kv_heads <= 0 ||
+      num_q_heads % num_kv_heads != 0 || num_blocks <= 0 || max_blocks_per_seq <= 0 || partition_size < 0 ||
+      partition_size % kBlock != 0)
+    return PA_ERR_SHAPE;
+  if (num_seqs > 65535 || num_kv_heads > 65535) return PA_ERR_UNSUPPORTED;
+  const int group = num_q_heads / num_kv_heads;
+  const int rows = group * q_len;
+  if (rows > (dtype == PA_F32 ? kMaxRowsF32 : kMaxRowsBF16)) return PA_ERR_UNSUPPORTED;
+  if (num_seqs == 0) return PA_OK;
+  const bool split = partition_size > 0;
+  if (!q || !k_cache || !v_cache || !block_tables || !context_lens || (!split && !out)) return PA_ERR_NULL;
+  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || (out && !aligned16(out))) return PA_ERR_SHAPE;
+
+  pa::DecodeParams p = {};
+  p.out = out;
+  p.q = q;
+  p.k_cache = k_cache;
+  p.v_cache = v_cache;
+  p.tables = block_tables;
+  p.lens = context_lens;
+  p.scale_log2 = (float)((double)scale * 1.4426950408889634);
+  p.q_len = q_len;
+  p.group = group;
+  p.n_h = num_q_heads;
+  p.n_kv = num_kv_heads;
+  p.num_blocks = num_blocks;
+  p.max_blocks = max_blocks_per_seq;
+  p.num_seqs = num_seqs;
+  p.part_blocks = 0;
+  p.num_parts = 1;
+  if (split) {
+    WsLayout w;
+    if (!workspace_layout(num_seqs, q_len, num_q_heads, head_dim, max_blocks_per_seq, block_size, partition_size,
+                          &w))
+      return PA_ERR_SHAPE;
+    if (!workspace) return PA_ERR_WORKSPACE;
+    if (workspace_bytes < w.total || !aligned16(workspace)) return PA_ERR_WORKSPACE;
+    char* base = static_cast<char*>(workspace);
+    p.ws_m = reinterpret_cast<float*>(base + w.m_off);
+    p.ws_l = reinterpret_cast<float*>(base + w.l_off);
+    p.ws_o = reinterpret_cast<float*>(base + w.o_off);
+    p.part_blocks = partition_size / kBlock;
+    p.num_parts = w.parts;
+  }
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  static_assert(kMaxRowsBF16 <= kMaxRowsValu, "rows beyond the VALU kernel need the matrix-core kernel");
+  return from_hip(pa::launch_decode_valu(p, dtype == PA_F32 ? pa::kF32 : pa::kBF16, head_dim, rows, s));
+}
+
+pa_status pa_reduce(void* out, const void* workspace, size_t workspace_bytes, const int32_t* context_lens,
+                    int32_t num_seqs, int32_t q_len, int32_t num_q_heads, int32_t head_dim,
+                    int32_t max_blocks_per_seq, int32_t block_size, int32_t partition_size, pa_dtype dtype,
+                    void* stream) {
+  if (dtype != PA_F32 && dtype != PA_BF16) return PA_ERR_UNSUPPORTED;
+  if (block_size != kBlock || (head_dim != 64 && head_dim != 128)) return PA_ERR_UNSUPPORTED;
+  if (num_seqs < 0 || q_len < 1 || q_len > 8 || num_q_heads <= 0 || max_blocks_per_seq <= 0 ||
+      partition_size <= 0 || partition_size % kBlock != 0)
+    return PA_ERR_SHAPE;
+  if (num_seqs == 0) return PA_OK;
+  if (!out || !context_lens) return PA_ERR_NULL;
+  if (!aligned16(out)) return PA_ERR_SHAPE;
+  WsLayout w;
+  if (!workspace_layout(num_seqs, q_len, num_q_heads, head_dim, max_blocks_per_seq, block_size, partition_size, &w))
+    return PA_ERR_SHAPE;
+  if (!workspace) return PA_ERR_WORKSPACE;
+  if (workspace_bytes < w.total || !aligned16(workspace)) return PA_ERR_WORKSPACE;
+  if ((size_t)num_seqs * q_len * num_q_heads > 0x7fffffff) return PA_ERR_SHAPE;
+  const char* base = static_cast<const char*>(workspace);
+  pa::ReduceParams p;
+  p.out = out;
+  p.ws_m = reinterpret_cast<const float*>(base + w.m_off);
+  p.ws_l = reinterpret_cast<const float*>(base + w.l_off);
+  p.ws_o = reinterpret_cast<const float*>(base + w.o_off);
+  p.lens = context_lens;
+  p.q_len = q_len;
+  p.n_h = num_q_heads;
+  p.max_blocks = max_blocks_per_seq;
+  p.part_blocks = partition_size / kBlock;
+  p.num_parts = w.parts;
+  p.num_seqs = num_seqs;
+  return from_hip(pa::launch_reduce(p, dtype == PA_F32 ? pa::kF32 : pa::kBF16, head_dim,
+                                    static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

@@ -1,0 +1,53 @@
+// Internal launch interface between the C ABI (pa_api.hip) and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace pa {
+
+enum ElemType { kF32 = 0, kBF16 = 1 };
+
+struct DecodeParams {
+  void* out;             // [S*q_len, n_h, D] (single pass only)
+  const void* q;         // [S*q_len, n_h, D]
+  const void* k_cache;   // [NB, 16, n_kv, D]
+  const void* v_cache;
+  const int32_t* tables; // [S, MB]
+  const int32_t* lens;   // [S]
+  float* ws_m;           // [S*q_len*n_h, P]  (split only)
+  float* ws_l;           // [S*q_len*n_h, P]
+  float* ws_o;           // [S*q_len*n_h, P, D]
+  float scale_log2;      // softmax scale * log2(e)
+  int q_len, group, n_h, n_kv, num_blocks, max_blocks;
+  int part_blocks;       // blocks per partition (split), 0 = whole context
+  int num_parts;         // partition stride of the workspace (split), else 1
+  int num_seqs;
+};
+
+struct ReduceParams {
+  void* out;
+  const float* ws_m;
+  const float* ws_l;
+  const float* ws_o;
+  const int32_t* lens;
+  int q_len, n_h, max_blocks, part_blocks, num_parts, num_seqs;
+};
+
+struct CacheWriteParams {
+  const void* k;
+  const void* v;
+  void* k_cache;
+  void* v_cache;
+  const int64_t* slots;
+  int num_tokens, num_blocks, row_chunks;  // row_chunks = 16-byte chunks per token row (n_kv * D * esize / 16)
+};
+
+// rows_per_kv = group * q_len (already validated)
+hipError_t launch_decode_valu(const DecodeParams& p, ElemType t, int head_dim, int rows_per_kv, hipStream_t s);
+hipError_t launch_decode_mfma(const DecodeParams& p, int head_dim, int rows_per_kv, hipStream_t s);
+hipError_t launch_reduce(const ReduceParams& p, ElemType t, int head_dim, hipStream_t s);
+hipError_t launch_cache_write(const CacheWriteParams& p, hipStream_t s);
+
+}  // namespace pa

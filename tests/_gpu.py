@@ -1,0 +1,122 @@
+"""Helpers shared by the GPU tests and bench.py: move a workload to the GPU,
+run the library's path on it, bring results back, and the parity gates."""
+
+from __future__ import annotations
+
+import numpy as np
+
+import workloads as wl
+
+# parity gates: the stated tolerances plus a relative-L2 gate on the whole output
+TOL = {
+    "f32": dict(atol=2e-3, rtol=0.0, rel_l2=1e-5),
+    "bf16": dict(atol=2e-2, rtol=1e-2, rel_l2=5e-3),
+}
+
+
+def parity(got: np.ndarray, ref: np.ndarray, dtype: str, atol=None, rtol=None, rel_l2=None) -> dict:
+    t = dict(TOL[dtype])
+    if atol is not None:
+        t["atol"] = atol
+    if rtol is not None:
+        t["rtol"] = rtol
+    if rel_l2 is not None:
+        t["rel_l2"] = rel_l2
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    err = np.abs(got - ref)
+    bound = t["atol"] + t["rtol"] * np.abs(ref)
+    finite = bool(np.isfinite(got).all())
+    excess = float(np.max(err - bound)) if err.size else 0.0
+    denom = float(np.linalg.norm(ref))
+    rl2 = float(np.linalg.norm(got - ref) / denom) if denom > 0 else float(np.linalg.norm(got))
+    ok = finite and excess <= 0.0 and rl2 <= t["rel_l2"]
+    return dict(ok=ok, finite=finite, max_abs=float(err.max()) if err.size else 0.0, excess=excess, rel_l2=rl2,
+                tol=t)
+
+
+def to_dev(a: np.ndarray, dtype: str, device="cuda"):
+    import torch
+
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint16:
+        return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(device)
+    return torch.from_numpy(a).to(device)
+
+
+def to_host(t) -> np.ndarray:
+    import torch
+
+    t = t.detach().cpu().contiguous()
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).numpy().view(np.uint16)
+    return t.numpy()
+
+
+def widen(a: np.ndarray, dtype: str) -> np.ndarray:
+    return (wl.bf16_bits_to_f32(a) if dtype == "bf16" else np.asarray(a, np.float32)).astype(np.float64)
+
+
+class DeviceProblem:
+    """A workload resident in HBM, ready for the path."""
+
+    def __init__(self, p: wl.Problem, device="cuda"):
+        import torch
+
+        self.p = p
+        dt = p.dtype
+        self.q = to_dev(p.q, dt, device)
+        self.k_cache = to_dev(p.k_cache, dt, device)
+        self.v_cache = to_dev(p.v_cache, dt, device)
+        self.block_tables = torch.from_numpy(p.block_tables).to(device)
+        self.context_lens = torch.from_numpy(p.context_lens).to(device)
+        self.new_k = self.new_v = self.slots = None
+        if p.new_k is not None:
+            self.new_k = to_dev(p.new_k, dt, device)
+            self.new_v = to_dev(p.new_v, dt, device)
+            self.slots = torch.from_numpy(p.slot_mapping).to(device)
+        self.out = torch.empty_like(self.q)
+        self.workspace = None
+
+    def step(self, partition_size: int, write: bool = True):
+        """One pass of the path: cache write of the new tokens, decode, reduce."""
+        import paged_kv_attention_decode_amd as pa
+
+        p = self.p
+        if write and self.new_k is not None:
+            pa.cache_write(self.new_k, self.new_v, self.k_cache, self.v_cache, self.slots)
+        if partition_size == 0:
+            pa.decode(self.q, self.k_cache, self.v_cache, self.block_tables, self.context_lens, float(p.scale),
+                      p.q_len, 0, out=self.out)
+        else:
+            self.workspace = pa.decode(self.q, self.k_cache, self.v_cache, self.block_tables, self.context_lens,
+                                       float(p.scale), p.q_len, partition_size, workspace=self.workspace)
+            pa.reduce(self.out, self.workspace, self.context_lens, p.q_len, p.max_blocks_per_seq, partition_size)
+        return self.out
+
+
+def host_caches_after_write(p: wl.Problem):
+    """The caches as the oracle sees them after the new tokens are stored."""
+    import oracle
+
+    if p.new_k is None:
+        return p.k_cache, p.v_cache
+    return oracle.cache_write(p.k_cache, p.v_cache, p.new_k, p.new_v, p.slot_mapping)
+
+
+def sample_rows(p: wl.Problem, n: int, seed: int = 0):
+    """(b, j, h) rows to check one by one: the shortest and the longest sequence,
+    then random ones; sorted by sequence so the oracle gathers each once."""
+    rng = np.random.default_rng(seed)
+    lens = p.context_lens
+    bs = {int(np.argmin(lens)), int(np.argmax(lens))}
+    while len(bs) < min(p.num_seqs, max(2, n // 4)):
+        bs.add(int(rng.integers(0, p.num_seqs)))
+    rows = set()
+    for b in sorted(bs):
+        rows.add((b, p.q_len - 1, 0))
+        rows.add((b, 0, p.num_q_heads - 1))
+    while len(rows) < n:
+        b = sorted(bs)[int(rng.integers(0, len(bs)))]
+        rows.add((b, int(rng.integers(0, p.q_len)), int(rng.integers(0, p.num_q_heads))))
+    return sorted(rows)

@@ -1,0 +1,114 @@
+"""The C ABI on the host (no GPU): the library loads, exports every function
+include/pa.h declares, and rejects invalid arguments before launching anything."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import paged_kv_attention_decode_amd as pa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_functions():
+    text = open(os.path.join(ROOT, "include", "pa.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(pa_[a-z_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return pa.load_library()
+
+
+def test_header_declares_the_binding_symbols():
+    assert declared_functions() == sorted(pa.SYMBOLS)
+
+
+def test_every_declared_symbol_is_exported(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+        assert ctypes.cast(getattr(lib, name), ctypes.c_void_p).value
+
+
+def test_status_strings(lib):
+    for code, name in pa._STATUS.items():
+        assert pa.status_string(code).startswith(name)
+    assert "unknown" in pa.status_string(99)
+    assert pa.version() == 10000
+
+
+def test_workspace_size_layout(lib):
+    # fp32 max_logits and exp_sums [rows][P], partial outputs [rows][P][d], each region 256-byte aligned
+    S, q_len, n_h, d, MB, ps = 8, 1, 32, 128, 8192, 512
+    P = -(-MB * 16 // ps)
+    rows = S * q_len * n_h
+    stats = -(-rows * P * 4 // 256) * 256
+    assert pa.decode_workspace_size(S, q_len, n_h, d, MB, ps) == 2 * stats + -(-rows * P * d * 4 // 256) * 256
+    assert pa.decode_workspace_size(3, 5, 7, 64, 3, 48) == 2 * 512 + -(-105 * 1 * 64 * 4 // 256) * 256
+    assert pa.decode_workspace_size(S, q_len, n_h, d, MB, 0) == 0
+    assert pa.decode_workspace_size(S, q_len, n_h, d, MB, 24) == 0  # not a multiple of the block size
+
+
+FAKE = ctypes.c_void_p(0x10000)  # aligned, never dereferenced: every call below fails validation first
+
+
+def _decode(lib, **kw):
+    a = dict(out=FAKE, q=FAKE, kc=FAKE, vc=FAKE, bt=FAKE, cl=FAKE, scale=0.1, q_len=1, S=2, n_h=4, n_kv=2, d=64,
+             NB=16, bs=16, MB=3, ps=0, ws=None, wsb=0, dt=pa.PA_F32, stream=None)
+    a.update(kw)
+    return lib.pa_decode(a["out"], a["q"], a["kc"], a["vc"], a["bt"], a["cl"], a["scale"], a["q_len"], a["S"],
+                         a["n_h"], a["n_kv"], a["d"], a["NB"], a["bs"], a["MB"], a["ps"], a["ws"], a["wsb"], a["dt"],
+                         a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), 1),
+    (dict(out=None), 1),
+    (dict(bt=None), 1),
+    (dict(n_h=5), 2),
+    (dict(q_len=0), 2),
+    (dict(q_len=9), 2),
+    (dict(ps=24), 2),
+    (dict(d=96), 3),
+    (dict(bs=32), 3),
+    (dict(dt=7), 3),
+    (dict(n_h=18, n_kv=2), 3),          # 9 rows per KV head in fp32
+    (dict(ps=512, ws=None), 4),
+    (dict(ps=512, ws=FAKE, wsb=16), 4),
+    (dict(q=ctypes.c_void_p(0x10008)), 2),  # not 16-byte aligned
+])
+def test_decode_rejects_invalid_arguments(lib, kw, status):
+    assert _decode(lib, **kw) == status
+
+
+def test_zero_sequences_is_a_no_op(lib):
+    assert _decode(lib, S=0, q=None, out=None) == 0
+
+
+def test_cache_write_rejects_invalid_arguments(lib):
+    f = lib.pa_cache_write
+    assert f(FAKE, FAKE, FAKE, FAKE, None, 4, 16, 16, 2, 64, pa.PA_BF16, None) == 1
+    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, 4, 16, 8, 2, 64, pa.PA_BF16, None) == 3
+    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, 4, 16, 16, 2, 80, pa.PA_BF16, None) == 3
+    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, -1, 16, 16, 2, 64, pa.PA_BF16, None) == 2
+    assert f(None, None, None, None, None, 0, 16, 16, 2, 64, pa.PA_BF16, None) == 0  # nothing to write
+
+
+def test_reduce_rejects_invalid_arguments(lib):
+    f = lib.pa_reduce
+    assert f(FAKE, FAKE, 1 << 30, FAKE, 2, 1, 4, 64, 3, 16, 0, pa.PA_F32, None) == 2     # partition_size 0
+    assert f(FAKE, None, 0, FAKE, 2, 1, 4, 64, 3, 16, 32, pa.PA_F32, None) == 4
+    assert f(FAKE, FAKE, 8, FAKE, 2, 1, 4, 64, 3, 16, 32, pa.PA_F32, None) == 4
+    assert f(None, FAKE, 1 << 30, FAKE, 2, 1, 4, 64, 3, 16, 32, pa.PA_F32, None) == 1
+
+
+def test_binding_refuses_host_tensors():
+    import torch
+
+    q = torch.zeros(2, 4, 64)
+    with pytest.raises(ValueError, match="GPU"):
+        pa.decode(q, torch.zeros(16, 16, 2, 64), torch.zeros(16, 16, 2, 64), torch.zeros(2, 3, dtype=torch.int32),
+                  torch.ones(2, dtype=torch.int32), 0.125)

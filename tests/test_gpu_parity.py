@@ -1,0 +1,277 @@
+"""Parity of the HIP path with the fp64 oracle, through the C ABI, on the GPU.
+
+Gates (elementwise, on every compared output):
+  fp32: |gpu - ref| <= 2e-3, and ||gpu - ref|| / ||ref|| <= 1e-5
+  bf16: |gpu - ref| <= 2e-2 + 1e-2 |ref|, and ||gpu - ref|| / ||ref|| <= 5e-3
+cache writes: bit-exact.  Invariants that must hold bit for bit: physical block
+permutation, batch composition, run-to-run repetition, unread rows poisoned
+with NaN, future tokens of a verify row.
+"""
+
+import os
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+import workloads as wl
+from _gpu import DeviceProblem, host_caches_after_write, parity, sample_rows, to_dev, to_host, widen
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def need_gpu():
+    if not torch.cuda.is_available():
+        pytest.fail("GPU tests need a GPU (run the CPU suite with -m 'not gpu')")
+    import paged_kv_attention_decode_amd as pa
+
+    pa.load_library()
+
+
+def say(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def run(p: wl.Problem, partition_size: int, write: bool = True):
+    d = DeviceProblem(p)
+    out = d.step(partition_size, write)
+    torch.cuda.synchronize()
+    return d, widen(to_host(out), p.dtype)
+
+
+def full_reference(p: wl.Problem):
+    kc, vc = host_caches_after_write(p)
+    return oracle.paged_decode(p.q, kc, vc, p.block_tables, p.context_lens, p.scale, p.q_len, p.dtype)
+
+
+def assert_parity(got, ref, dtype, what, **kw):
+    r = parity(got, ref, dtype, **kw)
+    assert r["ok"], f"{what}: {r}"
+    return r
+
+
+# ---------------------------------------------------------------------------
+# pa_cache_write: bit-exact
+
+
+@pytest.mark.parametrize("dtype,n_kv,d", [("bf16", 8, 128), ("f32", 2, 64), ("bf16", 1, 64), ("f32", 3, 128)])
+def test_cache_write_bit_exact(dtype, n_kv, d):
+    rng = np.random.default_rng(hash((dtype, n_kv, d)) % 2**32)
+    NB, T = 37, 29
+    bits = np.uint16 if dtype == "bf16" else np.uint32
+    kc = rng.integers(0, np.iinfo(bits).max, size=(NB, 16, n_kv, d), dtype=bits, endpoint=True)
+    vc = rng.integers(0, np.iinfo(bits).max, size=(NB, 16, n_kv, d), dtype=bits, endpoint=True)
+    k = rng.integers(0, np.iinfo(bits).max, size=(T, n_kv, d), dtype=bits, endpoint=True)
+    v = rng.integers(0, np.iinfo(bits).max, size=(T, n_kv, d), dtype=bits, endpoint=True)
+    slots = rng.choice(NB * 16, size=T, replace=False).astype(np.int64)
+    slots[3] = -1
+    slots[7] = -5
+    slots[11] = NB * 16 + 3  # outside the pool: skipped
+    view = (lambda a: a) if dtype == "bf16" else (lambda a: a.view(np.float32))
+    say(f"cache_write {dtype} n_kv={n_kv} d={d} T={T}")
+    dk, dv = to_dev(view(k), dtype), to_dev(view(v), dtype)
+    dkc, dvc = to_dev(view(kc), dtype), to_dev(view(vc), dtype)
+    import paged_kv_attention_decode_amd as pa
+
+    pa.cache_write(dk, dv, dkc, dvc, torch.from_numpy(slots).cuda())
+    torch.cuda.synchronize()
+    keep = (slots >= 0) & (slots < NB * 16)
+    ek, ev = oracle.cache_write(kc, vc, k[keep], v[keep], slots[keep])
+    gk = to_host(dkc).view(bits)
+    gv = to_host(dvc).view(bits)
+    assert np.array_equal(gk, ek) and np.array_equal(gv, ev)
+
+
+# ---------------------------------------------------------------------------
+# small problems, full output
+
+
+def test_tiny_f32_config():
+    p = wl.make_problem("tiny-f32")
+    say("tiny-f32")
+    _, got = run(p, 0)
+    assert_parity(got, full_reference(p), "f32", "tiny-f32")
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("q_len,n_h,n_kv", [(1, 8, 2), (5, 2, 2), (2, 8, 2)])
+def test_length_sweep_f32(d, q_len, n_h, n_kv):
+    """Every context length 1..48 crossed with block boundaries, fp32 inputs, 1e-5."""
+    lens = tuple(range(max(1, q_len), 49))
+    spec = wl.Spec(name="sweep", dtype="f32", num_seqs=len(lens), num_q_heads=n_h, num_kv_heads=n_kv, head_dim=d,
+                   lens=("fixed", lens), max_len=64, q_len=q_len, seed=d + q_len)
+    p = wl.make_problem(spec)
+    for ps in (0, 16, 32):
+        say(f"sweep f32 d={d} q_len={q_len} heads={n_h}/{n_kv} partition={ps}")
+        _, got = run(p, ps)
+        assert_parity(got, full_reference(p), "f32", f"sweep ps={ps}", atol=1e-5)
+
+
+SMALL_BF16 = [
+    dict(G=1, d=128, q_len=1), dict(G=2, d=128, q_len=1), dict(G=4, d=128, q_len=1), dict(G=8, d=128, q_len=1),
+    dict(G=4, d=64, q_len=1), dict(G=8, d=64, q_len=1), dict(G=4, d=128, q_len=2), dict(G=1, d=128, q_len=5),
+    dict(G=3, d=128, q_len=1),
+]
+
+
+@pytest.mark.parametrize("case", SMALL_BF16, ids=lambda c: f"G{c['G']}-d{c['d']}-q{c['q_len']}")
+def test_small_bf16(case):
+    G, d, q_len = case["G"], case["d"], case["q_len"]
+    spec = wl.Spec(name="small", dtype="bf16", num_seqs=7, num_q_heads=2 * G, num_kv_heads=2, head_dim=d,
+                   lens=("uniform", max(1, q_len), 700), max_len=720, q_len=q_len, write_new_tokens=True,
+                   seed=17 + G + d + q_len)
+    p = wl.make_problem(spec)
+    ref = full_reference(p)
+    for ps in (0, 16, 48, 512):
+        say(f"small bf16 G={G} d={d} q_len={q_len} partition={ps} lens={p.context_lens.tolist()}")
+        _, got = run(p, ps)
+        assert_parity(got, ref, "bf16", f"partition {ps}")
+
+
+def test_many_sequences_single_block():
+    spec = wl.Spec(name="short", dtype="bf16", num_seqs=300, num_q_heads=32, num_kv_heads=8, head_dim=128,
+                   lens=("uniform", 1, 16), max_len=16, seed=5)
+    p = wl.make_problem(spec)
+    say("300 sequences of 1..16 tokens")
+    _, got = run(p, 0)
+    assert_parity(got, full_reference(p), "bf16", "short")
+
+
+# ---------------------------------------------------------------------------
+# invariants, bit for bit
+
+INV_SPEC = wl.Spec(name="inv", dtype="bf16", num_seqs=6, num_q_heads=16, num_kv_heads=4, head_dim=128,
+                   lens=("uniform", 2, 900), max_len=960, q_len=2, seed=23)
+
+
+@pytest.mark.parametrize("ps", [0, 64])
+def test_physical_permutation_is_bitwise_invariant(ps):
+    p = wl.make_problem(INV_SPEC)
+    say(f"permutation ps={ps}")
+    _, a = run(p, ps)
+    _, b = run(wl.permute_physical(p, 99), ps)
+    assert np.array_equal(a, b)
+
+
+@pytest.mark.parametrize("ps", [0, 64])
+def test_repeatable_and_batch_independent(ps):
+    p = wl.make_problem(INV_SPEC)
+    say(f"repeat / batch ps={ps}")
+    d = DeviceProblem(p)
+    o1 = to_host(d.step(ps).clone())
+    o2 = to_host(d.step(ps).clone())
+    assert np.array_equal(o1, o2)
+    # sequence 3 alone
+    b = 3
+    one = wl.Problem(spec=p.spec.with_(num_seqs=1), context_lens=p.context_lens[b:b + 1].copy(),
+                     block_tables=p.block_tables[b:b + 1].copy(), q=p.q[b * 2:(b + 1) * 2].copy(),
+                     k_cache=p.k_cache, v_cache=p.v_cache, scale=p.scale)
+    _, alone = run(one, ps)
+    assert np.array_equal(widen(o1[b * 2:(b + 1) * 2], "bf16"), alone)
+
+
+def test_unread_rows_poisoned_and_garbage_padding():
+    clean = wl.make_problem(INV_SPEC)
+    dirty = wl.make_problem(INV_SPEC.with_(poison=True, pad="garbage"))
+    for ps in (0, 64):
+        say(f"poison ps={ps}")
+        _, a = run(clean, ps)
+        _, b = run(dirty, ps)
+        assert np.isfinite(b).all()
+        assert np.array_equal(a, b)
+
+
+def test_future_tokens_do_not_change_earlier_verify_rows():
+    spec = INV_SPEC.with_(q_len=2, num_q_heads=8, num_kv_heads=4)
+    p = wl.make_problem(spec)
+    _, base = run(p, 0)
+    q = wl.make_problem(spec)
+    for b in range(q.num_seqs):
+        t = int(q.context_lens[b]) - 1  # visible to query token 1 only
+        q.k_cache[q.block_tables[b, t // 16], t % 16] = np.uint16(0x4100)
+        q.v_cache[q.block_tables[b, t // 16], t % 16] = np.uint16(0xC100)
+    _, pert = run(q, 0)
+    rows0 = [b * 2 for b in range(p.num_seqs)]
+    rows1 = [b * 2 + 1 for b in range(p.num_seqs)]
+    assert np.array_equal(base[rows0], pert[rows0])
+    assert not np.array_equal(base[rows1], pert[rows1])
+
+
+def test_values_all_one_give_exactly_one():
+    p = wl.make_problem(INV_SPEC)
+    p.v_cache[:] = np.uint16(0x3F80)
+    for ps in (0, 64):
+        _, got = run(p, ps)
+        assert np.all(got == 1.0), ps
+
+
+def test_one_token_context_returns_v_exactly():
+    spec = wl.Spec(name="one", dtype="bf16", num_seqs=5, num_q_heads=8, num_kv_heads=2, head_dim=128,
+                   lens=("fixed", (1, 1, 1, 1, 1)), max_len=16, seed=3)
+    p = wl.make_problem(spec)
+    _, got = run(p, 0)
+    for b in range(5):
+        for h in range(8):
+            expect = widen(p.v_cache[p.block_tables[b, 0], 0, h // 4], "bf16")
+            assert np.array_equal(got[b, h], expect)
+
+
+@pytest.mark.parametrize("q_len,L", [(1, 300), (5, 77), (1, 20000)])
+def test_identical_keys_count_probe_fp32(q_len, L):
+    """All keys equal, V[t, c] = 1 where c == t mod d: each output is an exact count / (p + 1)."""
+    d = 128
+    lens = (L, L - 1, max(q_len, L // 3))
+    spec = wl.Spec(name="count", dtype="f32", num_seqs=3, num_q_heads=1, num_kv_heads=1, head_dim=d,
+                   lens=("fixed", lens), max_len=L + 16, q_len=q_len, seed=8)
+    p = wl.make_problem(spec)
+    p.k_cache[:] = np.float32(0.25)
+    p.v_cache[:] = 0
+    for b, Lb in enumerate(lens):
+        for t in range(Lb):
+            p.v_cache[p.block_tables[b, t // 16], t % 16, 0, t % d] = 1.0
+    for ps in (0, 512):
+        say(f"count probe q_len={q_len} L={L} ps={ps}")
+        _, got = run(p, ps)
+        for b, Lb in enumerate(lens):
+            for j in range(q_len):
+                pos = Lb - q_len + j
+                expect = np.array([len(range(c, pos + 1, d)) for c in range(d)]) / (pos + 1)
+                np.testing.assert_allclose(got[b * q_len + j, 0], expect, rtol=2e-6, atol=0)
+
+
+# ---------------------------------------------------------------------------
+# the full-size workloads, in the launch configuration bench.py times
+
+FULL = ["llama3-8b-decode", "llama3-70b-decode", "long-split", "spec-verify"]
+
+
+@pytest.mark.parametrize("name", FULL)
+def test_full_size_sampled_rows(name):
+    import bench
+
+    spec = wl.CONFIGS[name]
+    if spec.group * spec.q_len > 8:
+        pytest.skip("more than 8 query rows per KV head needs the matrix-core kernel, not built yet")
+    say(f"{name}: generating")
+    p = wl.make_problem(spec)
+    ps = bench.partition_for(p)
+    say(f"{name}: GPU path, partition {ps}")
+    d = DeviceProblem(p)
+    out = widen(to_host(d.step(ps)), p.dtype)
+    assert np.isfinite(out).all()
+    # the cache write, checked on the rows it touched
+    if p.new_k is not None:
+        kc = to_host(d.k_cache)
+        flat = kc.reshape(-1, p.num_kv_heads, p.head_dim)
+        assert np.array_equal(flat[p.slot_mapping], p.new_k)
+    rows = sample_rows(p, 48)
+    say(f"{name}: oracle on {len(rows)} rows")
+    kc, vc = host_caches_after_write(p)
+    ref = oracle.paged_decode_rows(p.q, kc, vc, p.block_tables, p.context_lens, p.scale, p.q_len, p.dtype, rows)
+    got = np.stack([out[b * p.q_len + j, h] for (b, j, h) in rows])
+    r = assert_parity(got, ref, p.dtype, name)
+    say(f"{name}: {r}")
