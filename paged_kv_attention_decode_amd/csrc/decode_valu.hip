@@ -1,38 +1,51 @@
 // Paged decode attention on the vector ALUs, for up to 8 query rows per KV head.
 //
-// What is computed (see include/pa.h): for every sequence b, KV head g and
-// query row r = j * group + hh (query token j, head h = g * group + hh),
-//   out = sum_t softmax_t(scale * q . k_t) v_t   over visible positions t,
+// What is computed (contract in include/pa.h): for every sequence b, KV head g
+// and query row r = j * group + hh (query token j, head h = g * group + hh),
+//   out = sum_t softmax_t(scale * q . k_t) v_t   over the positions t row r sees,
 // reading K and V through the block table one 16-token block at a time
 // ("LLM serving: KV cache, batching, paged attention and quantization",
 // section 3.5), with one load of each K/V row serving every query row of the
-// GQA group (section 3.3, intensity n_h / n_kv).
+// GQA group (section 3.3: the intensity of decode attention is n_h / n_kv).
 //
-// Work decomposition: one workgroup of 4 waves per (partition, KV head,
-// sequence).  The partition's blocks are dealt to the waves round-robin.
+// Work decomposition: one workgroup of NW waves per (partition, KV head,
+// sequence); a partition's blocks are dealt to the waves round-robin.
 //
 // Lane layouts inside a wave (bf16, head_dim 128; other shapes scale alike):
-//   scores  4 lanes per token, 16 tokens = one block per pass; each lane owns
+//   scores  4 lanes per token, 16 tokens = one block per load; each lane owns
 //           4 of the 16 sixteen-byte chunks of the token's row and dots them
-//           with the same chunks of every query row (v_dot2_f32_bf16), then a
-//           quad DPP reduction leaves the full score in all 4 lanes.
-//   values  16 lanes per token, 4 tokens per pass, 4 passes per block; each
-//           lane owns one chunk (8 columns) and accumulates p * v for every
-//           query row.  The weights p move from the score layout to the value
-//           layout through a 16 x rows LDS tile.
-// Both loads are 16 bytes per lane; the four lanes (scores) or sixteen lanes
-// (values) of a token read contiguous bytes of its row.
+//           with the same chunks of every query row (v_dot2_f32_bf16); a quad
+//           DPP sum leaves the full score in all 4 lanes.
+//   values  16 lanes per token, 4 tokens per load, 4 loads per block; each lane
+//           owns one chunk (8 columns) and accumulates p * v for every query
+//           row.  Load i of lane row q (lanes 16q .. 16q+15) takes token
+//           4q + i, whose weights the score layout holds in lanes 16q + 4i ..
+//           16q + 4i + 3 of the same row, so one DPP row_newbcast per row and
+//           load moves them (other head shapes use a cross-lane permute).
 //
-// Online softmax (lourdhu02.github.io "07 - Inference", section 5.1: running
-// max m, running sum l, rescaled accumulator; normalized once at the end,
-// section 5.2).  Scores are kept in log2 units (scale * log2 e folded in) so
-// the exponential is v_exp_f32.  The running max is only raised when a score
-// exceeds it by more than kRescaleSlack, a wave-uniform test (ballot); below
-// that the weights stay <= 2^kRescaleSlack and no rescale is needed.  The
-// result is the same softmax: numerator and denominator carry the same factor.
+// Memory-level parallelism: K/V are read with buffer loads whose descriptor
+// (wave-uniform) points at one physical block, so the per-lane offsets never
+// change, and NBUF blocks are in flight per wave.  A descriptor's record count
+// ends at the last context token, so rows past it (never written, possibly
+// NaN) and invalid or past-the-end blocks load as zeros without touching
+// memory; the next loads are therefore issued unconditionally, which keeps
+// the compiler's wait counts exact.
 //
-// The partition's partial (m, l, acc) per wave is merged across the 4 waves in
-// LDS; a split call stores the normalized partial and (m, l) for pa_reduce
+// Softmax.  The pages' online softmax keeps a running max m, a running sum l
+// and a rescaled accumulator, normalized once at the end ("07 - Inference",
+// lourdhu02.github.io, sections 5.1 and 5.2).  Any reference value gives the
+// same result as long as the weights stay in range, because numerator and
+// denominator carry the same factor.  Each wave takes the exact maximum of its
+// first block (log2 units, scale * log2 e folded in, v_exp_f32) as the
+// reference and never moves it in the hot loop: later weights may grow up to
+// 2^kOverflowSlack, which fp32 holds with full relative precision.  A score
+// beyond that sets a wave-uniform flag, and after the loop the wave redoes its
+// share exactly in two passes (maximum first, then the weighted sums).  The
+// hot loop therefore has no rescale branch and the accumulators are only ever
+// touched by FMAs.
+//
+// The waves' partials (m, l, acc) are merged in LDS with the rescaling rule;
+// a split call stores the normalized partial and (m, l) for pa_reduce
 // (section 5.3 "Decode attention and FlashDecoding"), a single pass writes
 // the output.
 #include "pa_device.h"
@@ -42,7 +55,7 @@ namespace pa {
 namespace {
 
 constexpr int kWaves = 4;
-constexpr float kRescaleSlack = 8.0f;
+constexpr float kOverflowSlack = 64.0f;  // log2 units
 // buffer descriptor word 3 for the gfx9 family (raw 32-bit access, no swizzle)
 constexpr int kBufferWord3 = 0x00020000;
 
@@ -64,20 +77,39 @@ __device__ __forceinline__ void store_out<float>(float* dst, float x) { *dst = x
 template <>
 __device__ __forceinline__ void store_out<uint16_t>(uint16_t* dst, float x) { *dst = (uint16_t)f32_to_bf16_bits(x); }
 
-template <typename T, int D, int R>
-__global__ __launch_bounds__(kWaves * 64) void decode_valu_kernel(DecodeParams a) {
+// pr[r] = p[r] of lane 4 * I of this lane's DPP row (row_newbcast); I is the
+// value-layout load index, a compile-time constant after unrolling
+template <int R>
+__device__ __forceinline__ void bcast_in_row(float (&pr)[R], const float (&p)[R], int i) {
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    switch (i) {
+      case 0: pr[r] = dpp_mov<0x150>(p[r]); break;
+      case 1: pr[r] = dpp_mov<0x154>(p[r]); break;
+      case 2: pr[r] = dpp_mov<0x158>(p[r]); break;
+      default: pr[r] = dpp_mov<0x15C>(p[r]); break;
+    }
+  }
+}
+
+// x as held by lane src (any lane of the wave)
+__device__ __forceinline__ float lane_from(float x, int src) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(src << 2, __builtin_bit_cast(int, x)));
+}
+
+template <typename T, int D, int R, int NW, int NBUF>
+__global__ __launch_bounds__(NW * 64) void decode_valu_kernel(DecodeParams a) {
   constexpr bool kBF16 = sizeof(T) == 2;
   constexpr int EPC = Elem<T>::kPer16B;  // elements per 16-byte chunk
   constexpr int NC = D / EPC;            // chunks per head row
   constexpr int NCK = NC / 4;            // score layout: chunks per lane
-  constexpr int TPV = 64 / NC;           // value layout: tokens per pass
-  constexpr int NV = kBlockTokens / TPV; // value layout: passes per block
+  constexpr int TPV = 64 / NC;           // value layout: tokens per load
+  constexpr int NV = kBlockTokens / TPV; // value layout: loads per block
   static_assert(NC % 4 == 0 && 64 % NC == 0 && kBlockTokens % TPV == 0, "unsupported head layout");
 
-  __shared__ float s_p[kWaves][kBlockTokens][R];
-  __shared__ float s_m[kWaves][R];
-  __shared__ float s_l[kWaves][R];
-  __shared__ float s_acc[kWaves][R][D];
+  __shared__ float s_m[NW][R];
+  __shared__ float s_l[NW][R];
+  __shared__ float s_acc[NW][R][D];
 
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave index, uniform
@@ -85,45 +117,21 @@ __global__ __launch_bounds__(kWaves * 64) void decode_valu_kernel(DecodeParams a
   const int g = blockIdx.y;
   const int b = blockIdx.z;
   const bool split = a.part_blocks > 0;
-
-  int L = a.lens[b];
-  const int Lmax = a.max_blocks * kBlockTokens;
-  L = L < 0 ? 0 : (L > Lmax ? Lmax : L);
-  const int nblk = (L + kBlockTokens - 1) / kBlockTokens;
-  const int pb = split ? a.part_blocks : nblk;
-  const int blk_begin = part * pb;
-  const int blk_end = min(blk_begin + pb, nblk);
   const int rows = a.group * a.q_len;
 
+  const int tk = lane >> 2;   // score layout: token of this lane
+  const int kq = lane & 3;    // score layout: chunk phase of this lane
+  const int vch = lane % NC;  // value layout: chunk of this lane
+  const int tv = lane / NC;   // value layout: token group of this lane
+  // value layout, load i: token kRowTokens ? TPV * tv + i : tv + TPV * i
+  constexpr bool kRowTokens = NC == 16;
+
+  // query rows in registers (score layout), issued before anything waits
   const T* __restrict__ qp = static_cast<const T*>(a.q);
-  T* __restrict__ op = static_cast<T*>(a.out);
-
-  if (blk_begin >= nblk) {
-    // split: the partition holds no token and pa_reduce never reads it.
-    // single pass with an empty context: every row is zero.
-    if (!split) {
-      for (int idx = threadIdx.x; idx < rows * D; idx += kWaves * 64) {
-        const int r = idx / D, c = idx % D;
-        const int j = r / a.group, hh = r % a.group;
-        const size_t orow = ((size_t)b * a.q_len + j) * a.n_h + (size_t)g * a.group + hh;
-        store_out<T>(op + orow * D + c, 0.0f);
-      }
-    }
-    return;
-  }
-
-  // ---- per-row constants and the query rows in registers (score layout) ----
-  const int tk = lane >> 2;  // token of this lane in the score layout
-  const int kq = lane & 3;   // chunk phase of this lane in the score layout
-  const int vch = lane % NC; // chunk of this lane in the value layout
-  const int tv = lane / NC;  // token phase of this lane in the value layout
-
-  int vis[R];
   uint4 qv[R][NCK];
 #pragma unroll
   for (int r = 0; r < R; ++r) {
     const int j = r / a.group, hh = r % a.group;
-    vis[r] = r < rows ? L - a.q_len + j + 1 : 0;
 #pragma unroll
     for (int c = 0; c < NCK; ++c) qv[r][c] = make_uint4(0, 0, 0, 0);
     if (r < rows) {
@@ -133,144 +141,219 @@ __global__ __launch_bounds__(kWaves * 64) void decode_valu_kernel(DecodeParams a
     }
   }
 
-  float mref[R], lsum[R], acc[R][EPC];
+  int L = a.lens[b];
+  const int Lmax = a.max_blocks * kBlockTokens;
+  L = L < 0 ? 0 : (L > Lmax ? Lmax : L);
+  const int nblk = (L + kBlockTokens - 1) / kBlockTokens;
+  const int pb = split ? a.part_blocks : nblk;
+  const int blk_begin = part * pb;
+  const int blk_end = min(blk_begin + pb, nblk);
+  T* __restrict__ op = static_cast<T*>(a.out);
+
+  if (blk_begin >= nblk) {
+    // split: the partition holds no token and pa_reduce never reads it.
+    // single pass with an empty context: every row is zero.
+    if (!split) {
+      for (int idx = threadIdx.x; idx < rows * D; idx += NW * 64) {
+        const int r = idx / D, c = idx % D;
+        const int j = r / a.group, hh = r % a.group;
+        const size_t orow = ((size_t)b * a.q_len + j) * a.n_h + (size_t)g * a.group + hh;
+        store_out<T>(op + orow * D + c, 0.0f);
+      }
+    }
+    return;
+  }
+
+  int vis[R];  // positions row r may see
+#pragma unroll
+  for (int r = 0; r < R; ++r) vis[r] = r < rows ? L - a.q_len + r / a.group + 1 : 0;
+
+  float m_ref[R], m_use[R], lsum[R], acc[R][EPC];
 #pragma unroll
   for (int r = 0; r < R; ++r) {
-    mref[r] = kNegInf;
+    m_ref[r] = kNegInf;
+    m_use[r] = 0.0f;
     lsum[r] = 0.0f;
 #pragma unroll
     for (int e = 0; e < EPC; ++e) acc[r][e] = 0.0f;
   }
 
-  // K/V rows are read with buffer loads: the descriptor (wave-uniform) points at
-  // one physical block, the per-lane byte offsets never change.  A descriptor
-  // with no records makes every load of an invalid or past-the-end block
-  // return zeros without touching memory, so the next block's loads can be
-  // issued unconditionally and the wait counts stay exact.
   const uint32_t tok_bytes = (uint32_t)a.n_kv * D * sizeof(T);
   const uint32_t blk_bytes = tok_bytes * kBlockTokens;
   const uint32_t head_off = (uint32_t)g * D * sizeof(T);
   const uint32_t k_off = (uint32_t)tk * tok_bytes + head_off + (uint32_t)kq * 16;
-  const uint32_t v_off = (uint32_t)tv * tok_bytes + head_off + (uint32_t)vch * 16;
+  const uint32_t v_off = (uint32_t)(kRowTokens ? TPV * tv : tv) * tok_bytes + head_off + (uint32_t)vch * 16;
+  const uint32_t v_step = (kRowTokens ? 1u : (uint32_t)TPV) * tok_bytes;  // bytes between loads i and i + 1
   const char* kbase = static_cast<const char*>(a.k_cache);
   const char* vbase = static_cast<const char*>(a.v_cache);
   const int32_t* __restrict__ table = a.tables + (size_t)b * a.max_blocks;
   const float scale_log2 = a.scale_log2;
 
-  // this wave's blocks: blk_begin + w + kWaves * k
-  const int n_mine = (blk_end - blk_begin - w + kWaves - 1) / kWaves;
+  // this wave's blocks: blk_begin + w + NW * k
+  const int n_mine = (blk_end - blk_begin - w + NW - 1) / NW;
 
+  // ids of this wave's blocks k0 .. k0 + 63, one per lane
+  auto block_ids = [&](int k0, int cnt) { return lane < cnt ? table[blk_begin + w + NW * (k0 + lane)] : 0; };
+
+  auto issue = [&](int ids, int cnt, int k0, int kk, uint4(&kb)[NCK], uint4(&vb)[NV], int& lblk, bool& ok) {
+    const int phys = __builtin_amdgcn_readlane(ids, kk < cnt ? kk : 0);
+    ok = kk < cnt && (unsigned)phys < (unsigned)a.num_blocks;
+    lblk = blk_begin + w + NW * (k0 + kk);
+    const int valid = min(kBlockTokens, L - lblk * kBlockTokens);
+    const size_t boff = ok ? (size_t)phys * blk_bytes : 0;
+    const uint32_t nrec = ok ? (uint32_t)valid * tok_bytes : 0u;
+    const __amdgpu_buffer_rsrc_t kr =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(kbase + boff), (short)0, (int)nrec, kBufferWord3);
+    const __amdgpu_buffer_rsrc_t vr =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(vbase + boff), (short)0, (int)nrec, kBufferWord3);
+#pragma unroll
+    for (int c = 0; c < NCK; ++c)
+      kb[c] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(kr, k_off + 64 * c, 0, 0));
+#pragma unroll
+    for (int i = 0; i < NV; ++i)
+      vb[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(vr, v_off, i * v_step, 0));
+  };
+
+  // scores of this lane's token for every row, log2 units, -inf where masked
+  auto scores = [&](const uint4(&kb)[NCK], int lblk, bool ok, float(&s)[R]) {
+    const int pos = lblk * kBlockTokens + tk;
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      float x = 0.0f;
+#pragma unroll
+      for (int c = 0; c < NCK; ++c) {
+        if constexpr (kBF16) {
+          x = dot2_bf16(qv[r][c].x, kb[c].x, x);
+          x = dot2_bf16(qv[r][c].y, kb[c].y, x);
+          x = dot2_bf16(qv[r][c].z, kb[c].z, x);
+          x = dot2_bf16(qv[r][c].w, kb[c].w, x);
+        } else {
+          x = fmaf(__builtin_bit_cast(float, qv[r][c].x), __builtin_bit_cast(float, kb[c].x), x);
+          x = fmaf(__builtin_bit_cast(float, qv[r][c].y), __builtin_bit_cast(float, kb[c].y), x);
+          x = fmaf(__builtin_bit_cast(float, qv[r][c].z), __builtin_bit_cast(float, kb[c].z), x);
+          x = fmaf(__builtin_bit_cast(float, qv[r][c].w), __builtin_bit_cast(float, kb[c].w), x);
+        }
+      }
+      const float sr = quad_sum(x) * scale_log2;  // every lane, so the DPP sources are live
+      s[r] = (ok && pos < vis[r]) ? sr : kNegInf;
+    }
+  };
+
+  // weights against the wave's reference, l, and P * V
+  auto accumulate = [&](const float(&s)[R], const uint4(&vb)[NV]) {
+    float p[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      p[r] = fast_exp2(s[r] - m_use[r]);
+      lsum[r] += p[r];
+    }
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      // weights of the token this lane's value load i holds
+      float pr[R];
+      if constexpr (kRowTokens) {
+        bcast_in_row<R>(pr, p, i);
+      } else {
+        const int src = 4 * (tv + TPV * i);
+#pragma unroll
+        for (int r = 0; r < R; ++r) pr[r] = lane_from(p[r], src);
+      }
+      float vf[EPC];
+      if constexpr (kBF16) {
+        vf[0] = bf16_lo(vb[i].x); vf[1] = bf16_hi(vb[i].x);
+        vf[2] = bf16_lo(vb[i].y); vf[3] = bf16_hi(vb[i].y);
+        vf[4] = bf16_lo(vb[i].z); vf[5] = bf16_hi(vb[i].z);
+        vf[6] = bf16_lo(vb[i].w); vf[7] = bf16_hi(vb[i].w);
+      } else {
+        vf[0] = __builtin_bit_cast(float, vb[i].x); vf[1] = __builtin_bit_cast(float, vb[i].y);
+        vf[2] = __builtin_bit_cast(float, vb[i].z); vf[3] = __builtin_bit_cast(float, vb[i].w);
+      }
+#pragma unroll
+      for (int r = 0; r < R; ++r)
+#pragma unroll
+        for (int e = 0; e < EPC; ++e) acc[r][e] = fmaf(pr[r], vf[e], acc[r][e]);
+    }
+  };
+
+  auto set_reference = [&](const float(&mx)[R]) {
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      m_ref[r] = wave_max(mx[r]);
+      m_use[r] = m_ref[r] == kNegInf ? 0.0f : m_ref[r];
+    }
+  };
+
+  bool overflow = false;  // wave-uniform
   for (int k0 = 0; k0 < n_mine; k0 += 64) {
     const int cnt = min(64, n_mine - k0);
-    const int ids = lane < cnt ? table[blk_begin + w + kWaves * (k0 + lane)] : 0;
+    const int ids = block_ids(k0, cnt);
 
-    auto issue = [&](int kk, uint4(&kb)[NCK], uint4(&vb)[NV], int& lblk, bool& ok) {
-      const int phys = __builtin_amdgcn_readlane(ids, kk < cnt ? kk : 0);
-      ok = kk < cnt && (unsigned)phys < (unsigned)a.num_blocks;
-      lblk = blk_begin + w + kWaves * (k0 + kk);
-      const size_t boff = ok ? (size_t)phys * blk_bytes : 0;
-      const uint32_t nrec = ok ? blk_bytes : 0u;
-      const __amdgpu_buffer_rsrc_t kr =
-          __builtin_amdgcn_make_buffer_rsrc((void*)(kbase + boff), (short)0, (int)nrec, kBufferWord3);
-      const __amdgpu_buffer_rsrc_t vr =
-          __builtin_amdgcn_make_buffer_rsrc((void*)(vbase + boff), (short)0, (int)nrec, kBufferWord3);
+    // NBUF register sets in flight: block kk + u computes while the next NBUF - 1 load
+    uint4 kb[NBUF][NCK], vb[NBUF][NV];
+    int lb[NBUF];
+    bool okb[NBUF];
 #pragma unroll
-      for (int c = 0; c < NCK; ++c)
-        kb[c] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(kr, k_off + 64 * c, 0, 0));
+    for (int u = 0; u < NBUF; ++u) issue(ids, cnt, k0, u, kb[u], vb[u], lb[u], okb[u]);
+    if (k0 == 0) {
+      float s0[R];
+      scores(kb[0], lb[0], okb[0], s0);
+      set_reference(s0);
+    }
+    for (int kk = 0; kk < cnt; kk += NBUF) {
 #pragma unroll
-      for (int i = 0; i < NV; ++i)
-        vb[i] = __builtin_bit_cast(uint4,
-                                   __builtin_amdgcn_raw_buffer_load_b128(vr, v_off, i * TPV * tok_bytes, 0));
-    };
+      for (int u = 0; u < NBUF; ++u) {
+        if (kk + u < cnt) {
+          float s[R];
+          scores(kb[u], lb[u], okb[u], s);
+          bool big = false;
+#pragma unroll
+          for (int r = 0; r < R; ++r) big |= s[r] > m_ref[r] + kOverflowSlack;
+          overflow |= __builtin_amdgcn_ballot_w64(big) != 0;
+          accumulate(s, vb[u]);
+        }
+        issue(ids, cnt, k0, kk + u + NBUF, kb[u], vb[u], lb[u], okb[u]);
+      }
+    }
+  }
 
-    auto compute = [&](const uint4(&kb)[NCK], const uint4(&vb)[NV], int lblk, bool ok) {
-      // scores of this lane's token for every row, log2 units
-      float s[R];
+  if (overflow) {
+    // some weight would have left the safe range: redo this wave's share
+    // exactly, the maximum first and then the weighted sums
+    float mx[R];
 #pragma unroll
-      for (int r = 0; r < R; ++r) {
-        float x = 0.0f;
+    for (int r = 0; r < R; ++r) {
+      mx[r] = kNegInf;
+      lsum[r] = 0.0f;
 #pragma unroll
-        for (int c = 0; c < NCK; ++c) {
-          if constexpr (kBF16) {
-            x = dot2_bf16(qv[r][c].x, kb[c].x, x);
-            x = dot2_bf16(qv[r][c].y, kb[c].y, x);
-            x = dot2_bf16(qv[r][c].z, kb[c].z, x);
-            x = dot2_bf16(qv[r][c].w, kb[c].w, x);
-          } else {
-            x = fmaf(__builtin_bit_cast(float, qv[r][c].x), __builtin_bit_cast(float, kb[c].x), x);
-            x = fmaf(__builtin_bit_cast(float, qv[r][c].y), __builtin_bit_cast(float, kb[c].y), x);
-            x = fmaf(__builtin_bit_cast(float, qv[r][c].z), __builtin_bit_cast(float, kb[c].z), x);
-            x = fmaf(__builtin_bit_cast(float, qv[r][c].w), __builtin_bit_cast(float, kb[c].w), x);
-          }
-        }
-        s[r] = quad_sum(x) * scale_log2;
+      for (int e = 0; e < EPC; ++e) acc[r][e] = 0.0f;
+    }
+    for (int k0 = 0; k0 < n_mine; k0 += 64) {
+      const int cnt = min(64, n_mine - k0);
+      const int ids = block_ids(k0, cnt);
+      for (int kk = 0; kk < cnt; ++kk) {
+        uint4 kb1[NCK], vb1[NV];
+        int lb1;
+        bool ok1;
+        issue(ids, cnt, k0, kk, kb1, vb1, lb1, ok1);
+        float s[R];
+        scores(kb1, lb1, ok1, s);
+#pragma unroll
+        for (int r = 0; r < R; ++r) mx[r] = fmaxf(mx[r], s[r]);
       }
-      const int pos = lblk * kBlockTokens + tk;
-      bool raise = false;
-#pragma unroll
-      for (int r = 0; r < R; ++r) {
-        s[r] = (ok && pos < vis[r]) ? s[r] : kNegInf;
-        raise |= s[r] > mref[r] + kRescaleSlack;
+    }
+    set_reference(mx);
+    for (int k0 = 0; k0 < n_mine; k0 += 64) {
+      const int cnt = min(64, n_mine - k0);
+      const int ids = block_ids(k0, cnt);
+      for (int kk = 0; kk < cnt; ++kk) {
+        uint4 kb1[NCK], vb1[NV];
+        int lb1;
+        bool ok1;
+        issue(ids, cnt, k0, kk, kb1, vb1, lb1, ok1);
+        float s[R];
+        scores(kb1, lb1, ok1, s);
+        accumulate(s, vb1);
       }
-      if (__builtin_amdgcn_ballot_w64(raise)) {
-#pragma unroll
-        for (int r = 0; r < R; ++r) {
-          const float mnew = fmaxf(mref[r], wave_max(s[r]));
-          if (mnew > mref[r]) {
-            const float alpha = fast_exp2(mref[r] - mnew);
-            lsum[r] *= alpha;
-#pragma unroll
-            for (int e = 0; e < EPC; ++e) acc[r][e] *= alpha;
-            mref[r] = mnew;
-          }
-        }
-      }
-      float p[R];
-#pragma unroll
-      for (int r = 0; r < R; ++r) {
-        p[r] = fast_exp2(s[r] - (mref[r] == kNegInf ? 0.0f : mref[r]));
-        lsum[r] += p[r];
-      }
-      if (kq == 0) {
-#pragma unroll
-        for (int r = 0; r < R; ++r) s_p[w][tk][r] = p[r];
-      }
-      wave_lds_sync();
-#pragma unroll
-      for (int i = 0; i < NV; ++i) {
-        const int tok = tv + TPV * i;
-        float pr[R];
-#pragma unroll
-        for (int r = 0; r < R; ++r) pr[r] = s_p[w][tok][r];
-        float vf[EPC];
-        if constexpr (kBF16) {
-          vf[0] = bf16_lo(vb[i].x); vf[1] = bf16_hi(vb[i].x);
-          vf[2] = bf16_lo(vb[i].y); vf[3] = bf16_hi(vb[i].y);
-          vf[4] = bf16_lo(vb[i].z); vf[5] = bf16_hi(vb[i].z);
-          vf[6] = bf16_lo(vb[i].w); vf[7] = bf16_hi(vb[i].w);
-        } else {
-          vf[0] = __builtin_bit_cast(float, vb[i].x); vf[1] = __builtin_bit_cast(float, vb[i].y);
-          vf[2] = __builtin_bit_cast(float, vb[i].z); vf[3] = __builtin_bit_cast(float, vb[i].w);
-        }
-#pragma unroll
-        for (int r = 0; r < R; ++r)
-#pragma unroll
-          for (int e = 0; e < EPC; ++e) acc[r][e] = fmaf(pr[r], vf[e], acc[r][e]);
-      }
-      wave_lds_sync();
-    };
-
-    // two register sets in flight: block kk computes while kk + 1 loads
-    uint4 kA[NCK], vA[NV], kB[NCK], vB[NV];
-    int lA = 0, lB = 0;
-    bool okA = false, okB = false;
-    issue(0, kA, vA, lA, okA);
-    issue(1, kB, vB, lB, okB);
-    for (int kk = 0; kk < cnt; kk += 2) {
-      compute(kA, vA, lA, okA);
-      issue(kk + 2, kA, vA, lA, okA);
-      if (kk + 1 < cnt) compute(kB, vB, lB, okB);
-      issue(kk + 3, kB, vB, lB, okB);
     }
   }
 
@@ -286,7 +369,7 @@ __global__ __launch_bounds__(kWaves * 64) void decode_valu_kernel(DecodeParams a
       acc[r][e] = x;
     }
     if (lane == 0) {
-      s_m[w][r] = mref[r];
+      s_m[w][r] = m_ref[r];
       s_l[w][r] = lw;
     }
     if (lane < NC) {
@@ -296,16 +379,16 @@ __global__ __launch_bounds__(kWaves * 64) void decode_valu_kernel(DecodeParams a
   }
   __syncthreads();
 
-  // ---- merge the 4 waves, then normalize (single pass) or store the partial (split)
-  for (int idx = threadIdx.x; idx < rows * D; idx += kWaves * 64) {
+  // ---- merge the waves, then normalize (single pass) or store the partial (split)
+  for (int idx = threadIdx.x; idx < rows * D; idx += NW * 64) {
     const int r = idx / D, c = idx % D;
     float M = s_m[0][r];
 #pragma unroll
-    for (int u = 1; u < kWaves; ++u) M = fmaxf(M, s_m[u][r]);
+    for (int u = 1; u < NW; ++u) M = fmaxf(M, s_m[u][r]);
     float o = 0.0f, l = 0.0f;
     if (M != kNegInf) {
 #pragma unroll
-      for (int u = 0; u < kWaves; ++u) {
+      for (int u = 0; u < NW; ++u) {
         const float f = fast_exp2(s_m[u][r] - M);
         l += f * s_l[u][r];
         o += f * s_acc[u][r][c];
@@ -327,10 +410,23 @@ __global__ __launch_bounds__(kWaves * 64) void decode_valu_kernel(DecodeParams a
   }
 }
 
+// Blocks in flight per wave: as many as fit next to the query chunks and the
+// accumulators in about 200 VGPRs (two waves per SIMD), at least 2.
+template <typename T, int D, int R>
+constexpr int blocks_in_flight() {
+  constexpr int chunks = D * (int)sizeof(T) / 16;     // 16-byte chunks per head row
+  constexpr int per_block = 4 * (chunks / 4 + kBlockTokens / (64 / chunks));  // VGPRs of one block (K + V)
+  constexpr int qregs = 4 * R * (chunks / 4);
+  constexpr int budget = 200 - qregs - R * (16 / (int)sizeof(T));  // minus the accumulators
+  constexpr int n = budget / per_block;
+  return n < 2 ? 2 : (n > 4 ? 4 : n);
+}
+
 template <typename T, int D, int R>
 hipError_t launch_one(const DecodeParams& p, hipStream_t s) {
   dim3 grid(p.part_blocks > 0 ? p.num_parts : 1, p.n_kv, p.num_seqs);
-  hipLaunchKernelGGL((decode_valu_kernel<T, D, R>), grid, dim3(kWaves * 64), 0, s, p);
+  hipLaunchKernelGGL((decode_valu_kernel<T, D, R, kWaves, blocks_in_flight<T, D, R>()>), grid, dim3(kWaves * 64), 0,
+                     s, p);
   return hipGetLastError();
 }
 

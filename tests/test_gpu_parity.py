@@ -243,6 +243,31 @@ def test_identical_keys_count_probe_fp32(q_len, L):
                 np.testing.assert_allclose(got[b * q_len + j, 0], expect, rtol=2e-6, atol=0)
 
 
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("q_len", [1, 2])
+def test_scores_rising_far_past_the_first_block(dtype, q_len):
+    """Scores grow by ~0.1 per position, so weights relative to a wave's first
+    block exceed 2^64 and the kernel must take its exact two-pass path."""
+    d = 64
+    spec = wl.Spec(name="ramp", dtype=dtype, num_seqs=3, num_q_heads=2, num_kv_heads=1, head_dim=d,
+                   lens=("fixed", (1000, 700, 40)), max_len=1024, q_len=q_len, seed=31)
+    p = wl.make_problem(spec)
+    p.q[:] = 0
+    p.k_cache[:] = 0
+    one = np.float32(4.0)
+    p.q[:, :, 0] = wl.round_to_bf16_bits(np.array([one]))[0] if dtype == "bf16" else one
+    for b, L in enumerate(p.context_lens):
+        for t in range(int(L)):
+            val = np.float32(0.2 * t)
+            p.k_cache[p.block_tables[b, t // 16], t % 16, 0, 0] = (
+                wl.round_to_bf16_bits(np.array([val]))[0] if dtype == "bf16" else val)
+    ref = full_reference(p)
+    for ps in (0, 512):
+        say(f"ramp {dtype} q_len={q_len} ps={ps}")
+        _, got = run(p, ps)
+        assert_parity(got, ref, dtype, f"ramp ps={ps}")
+
+
 # ---------------------------------------------------------------------------
 # the full-size workloads, in the launch configuration bench.py times
 
