@@ -84,9 +84,7 @@ class Resident:
         self.out = torch.empty_like(self.q)
         self.ws = None
         if partition:
-            n = pa.decode_workspace_size(p.num_seqs, p.q_len, p.num_q_heads, p.head_dim, p.max_blocks_per_seq,
-                                         partition)
-            self.ws = torch.empty(n, dtype=torch.uint8, device="cuda")
+            self.ws = pa.new_workspace(self.q, self.k_cache, self.tables, p.q_len, partition)
 
     def write(self):
         if self.new_k is not None:
@@ -94,15 +92,11 @@ class Resident:
 
     def decode(self):
         p = self.p
-        if self.partition:
-            self.pa.decode(self.q, self.k_cache, self.v_cache, self.tables, self.lens, float(p.scale), p.q_len,
-                           self.partition, workspace=self.ws)
-        else:
-            self.pa.decode(self.q, self.k_cache, self.v_cache, self.tables, self.lens, float(p.scale), p.q_len, 0,
-                           out=self.out)
+        self.pa.decode(self.q, self.k_cache, self.v_cache, self.tables, self.lens, float(p.scale), p.q_len,
+                       self.partition, out=self.out, workspace=self.ws)
 
     def reduce(self):
-        if self.partition:
+        if self.partition > 0:
             p = self.p
             self.pa.reduce(self.out, self.ws, self.lens, p.q_len, p.max_blocks_per_seq, self.partition)
 

@@ -5,8 +5,8 @@
  *
  *   pa_cache_write  store the K/V rows of new tokens into their cache slots;
  *   pa_decode       attention of the newest q_len tokens of every sequence over
- *                   its paged KV cache, either in one pass or as per-partition
- *                   partials (split context);
+ *                   its paged KV cache: in one pass, work-balanced across the
+ *                   GPU, or as per-partition partials (split context);
  *   pa_reduce       merge the partials of a split pa_decode into the output.
  *
  * Sources of the definitions (the web pages this library implements):
@@ -67,6 +67,9 @@ typedef enum {
 
 typedef enum { PA_F32 = 0, PA_BF16 = 1 } pa_dtype;
 
+/* partition_size value selecting the work-balanced mode of pa_decode */
+#define PA_BALANCED (-1)
+
 /*
  * pa_cache_write - write the K and V rows of new tokens into the paged caches.
  *
@@ -90,7 +93,8 @@ pa_status pa_cache_write(const void* k, const void* v, void* k_cache, void* v_ca
  * pa_decode - paged attention of the q_len newest tokens of each sequence.
  *
  *   out           [num_seqs * q_len, num_q_heads, head_dim], dtype.  Written when
- *                 partition_size == 0; untouched otherwise (may be NULL then).
+ *                 partition_size is 0 or PA_BALANCED; untouched by a split call
+ *                 (may be NULL then).
  *   q             [num_seqs * q_len, num_q_heads, head_dim], dtype.  Row
  *                 b * q_len + j is query token j of sequence b.
  *   k_cache,      [num_blocks, block_size, num_kv_heads, head_dim], dtype
@@ -109,14 +113,27 @@ pa_status pa_cache_write(const void* k, const void* v, void* k_cache, void* v_ca
  *                 h / (num_q_heads / num_kv_heads).  Rows per KV head
  *                 (num_q_heads / num_kv_heads) * q_len must be <= 8 for PA_F32 and
  *                 <= 64 for PA_BF16.
- *   partition_size 0: one pass, writes out.  Otherwise a positive multiple of
- *                 block_size: the context is split into partitions
- *                 [p*partition_size, (p+1)*partition_size), and for every query row
- *                 the partition's partial result is written to the workspace;
- *                 pa_reduce then produces out.
+ *   partition_size
+ *                 0: one pass, one workgroup per (KV head, sequence); writes out.
+ *                 PA_BALANCED (-1): writes out; the (sequence, KV head, block)
+ *                 work is cut into equal ranges, one per workgroup, so ragged
+ *                 context lengths keep every compute unit equally busy; a
+ *                 (sequence, head) cut between ranges is merged inside the call
+ *                 with the rescaling rule, in a fixed order.  Needs a workspace
+ *                 whose first 4 * num_seqs * num_kv_heads bytes are zero before
+ *                 the first such call; every balanced call leaves them zero, so
+ *                 one workspace serves any number of calls.  Batches of more than
+ *                 4096 sequences fall back to the one-pass mode.
+ *                 Otherwise a positive multiple of block_size: the context is
+ *                 split into partitions [p*partition_size, (p+1)*partition_size),
+ *                 and for every query row the partition's partial result is
+ *                 written to the workspace; pa_reduce then produces out.
  *   workspace     device buffer of at least pa_decode_workspace_size(...) bytes
- *                 (only used, and only required, when partition_size > 0).  Its
- *                 contents are private to pa_decode / pa_reduce.
+ *                 for the same partition_size (only used, and only required,
+ *                 when partition_size != 0).  Its contents are private to the
+ *                 library; a workspace used by a split call must be zeroed again
+ *                 before it serves a balanced call.  Calls sharing one workspace
+ *                 must not overlap in time.
  *
  * Results depend only on the logical contents (bitwise deterministic from run
  * to run, independent of the physical block ids and of the other sequences).
@@ -129,16 +146,19 @@ pa_status pa_decode(void* out, const void* q, const void* k_cache, const void* v
                     void* stream);
 
 /*
- * pa_decode_workspace_size - bytes of workspace a split pa_decode needs.
+ * pa_decode_workspace_size - bytes of workspace pa_decode needs for partition_size.
  *
- * With P = ceil(max_blocks_per_seq * block_size / partition_size) partitions
- * and R = num_seqs * q_len * num_q_heads query rows the workspace holds fp32
- * max_logits[R][P], exp_sums[R][P] and partial outputs [R][P][head_dim], each
- * region 256-byte aligned.  Returns 0 when partition_size <= 0 or the sizes are
- * invalid.
+ * Split (partition_size > 0): with P = ceil(max_blocks_per_seq * block_size /
+ * partition_size) partitions and R = num_seqs * q_len * num_q_heads query rows,
+ * fp32 max_logits[R][P], exp_sums[R][P] and partial outputs [R][P][head_dim].
+ * Balanced (PA_BALANCED): int32 arrival counters [num_seqs * num_kv_heads], then
+ * fp32 partials for 2 * 1024 pieces of (num_q_heads / num_kv_heads) * q_len rows
+ * of head_dim + 2 values.  Each region is 256-byte aligned.  Returns 0 for
+ * partition_size 0, invalid sizes, or a partition_size that is neither.
  */
-size_t pa_decode_workspace_size(int32_t num_seqs, int32_t q_len, int32_t num_q_heads, int32_t head_dim,
-                                int32_t max_blocks_per_seq, int32_t block_size, int32_t partition_size);
+size_t pa_decode_workspace_size(int32_t num_seqs, int32_t q_len, int32_t num_q_heads, int32_t num_kv_heads,
+                                int32_t head_dim, int32_t max_blocks_per_seq, int32_t block_size,
+                                int32_t partition_size);
 
 /*
  * pa_reduce - merge the per-partition partials of a split pa_decode into out.

@@ -9,7 +9,7 @@ on the GPU, the call raises.
     cache_write(k, v, k_cache, v_cache, slot_mapping)
     decode(q, k_cache, v_cache, block_tables, context_lens, scale, q_len, ...)
     reduce(out, workspace, context_lens, ...)
-    decode_workspace_size(...)
+    decode_workspace_size(...), new_workspace(...)
     paged_attention(...)   # decode, plus reduce when the context is split
 """
 
@@ -20,11 +20,12 @@ import os
 from typing import Optional
 
 __all__ = [
-    "PA_F32", "PA_BF16", "PagedAttentionError", "library_path", "load_library", "status_string", "version",
+    "PA_F32", "PA_BF16", "PA_BALANCED", "PagedAttentionError", "library_path", "load_library", "status_string", "version",
     "cache_write", "decode", "reduce", "decode_workspace_size", "paged_attention", "SYMBOLS",
 ]
 
 PA_F32, PA_BF16 = 0, 1
+PA_BALANCED = -1  # partition_size selecting the work-balanced decode
 BLOCK_SIZE = 16
 SYMBOLS = ("pa_cache_write", "pa_decode", "pa_decode_workspace_size", "pa_reduce", "pa_status_string", "pa_version")
 _STATUS = {0: "PA_OK", 1: "PA_ERR_NULL", 2: "PA_ERR_SHAPE", 3: "PA_ERR_UNSUPPORTED", 4: "PA_ERR_WORKSPACE",
@@ -60,7 +61,7 @@ def load_library():
     lib.pa_decode.argtypes = [vp, vp, vp, vp, vp, vp, f32, i32, i32, i32, i32, i32, i32, i32, i32, i32, vp, sz,
                               ctypes.c_int, vp]
     lib.pa_decode_workspace_size.restype = sz
-    lib.pa_decode_workspace_size.argtypes = [i32] * 7
+    lib.pa_decode_workspace_size.argtypes = [i32] * 8
     lib.pa_reduce.restype = ctypes.c_int
     lib.pa_reduce.argtypes = [vp, vp, sz, vp, i32, i32, i32, i32, i32, i32, i32, ctypes.c_int, vp]
     lib.pa_status_string.restype = ctypes.c_char_p
@@ -147,10 +148,19 @@ def cache_write(k, v, k_cache, v_cache, slot_mapping, stream=None) -> None:
     _check(st, "pa_cache_write")
 
 
-def decode_workspace_size(num_seqs, q_len, num_q_heads, head_dim, max_blocks_per_seq, partition_size,
+def decode_workspace_size(num_seqs, q_len, num_q_heads, num_kv_heads, head_dim, max_blocks_per_seq, partition_size,
                           block_size=BLOCK_SIZE) -> int:
-    return int(load_library().pa_decode_workspace_size(num_seqs, q_len, num_q_heads, head_dim, max_blocks_per_seq,
-                                                       block_size, partition_size))
+    return int(load_library().pa_decode_workspace_size(num_seqs, q_len, num_q_heads, num_kv_heads, head_dim,
+                                                       max_blocks_per_seq, block_size, partition_size))
+
+
+def new_workspace(q, k_cache, block_tables, q_len: int, partition_size: int):
+    """A workspace for decode(..., partition_size): zero-filled, which a balanced
+    call needs before its first use (every balanced call leaves it so)."""
+    torch = _torch()
+    need = decode_workspace_size(block_tables.shape[0], q_len, q.shape[1], k_cache.shape[2], q.shape[2],
+                                 block_tables.shape[1], partition_size, k_cache.shape[1])
+    return torch.zeros(max(need, 1), dtype=torch.uint8, device=q.device)
 
 
 def _decode_shapes(q, k_cache, block_tables, context_lens, q_len):
@@ -167,8 +177,13 @@ def _decode_shapes(q, k_cache, block_tables, context_lens, q_len):
 
 def decode(q, k_cache, v_cache, block_tables, context_lens, scale: float, q_len: int = 1, partition_size: int = 0,
            out=None, workspace=None, stream=None):
-    """pa_decode.  partition_size == 0: returns out.  Otherwise fills the workspace
-    with per-partition partials (allocated here if not given) and returns it."""
+    """pa_decode.
+
+    partition_size 0 (one pass) or PA_BALANCED: writes and returns out.
+    partition_size > 0: fills the workspace with per-partition partials for
+    reduce() and returns the workspace.  A workspace is allocated (zero-filled)
+    when none is given; pass the same one again to avoid the allocation.
+    """
     torch = _torch()
     S = _decode_shapes(q, k_cache, block_tables, context_lens, q_len)
     n_h, d = q.shape[1], q.shape[2]
@@ -178,24 +193,22 @@ def decode(q, k_cache, v_cache, block_tables, context_lens, scale: float, q_len:
                    _dev(block_tables, "block_tables", torch.int32, 2), _dev(context_lens, "context_lens", torch.int32, 1))
     if v_cache.shape != k_cache.shape:
         raise ValueError("k_cache and v_cache must have the same shape")
-    if partition_size == 0:
+    pws, nws = None, 0
+    if partition_size != 0:
+        if workspace is None:
+            workspace = new_workspace(q, k_cache, block_tables, q_len, partition_size)
+        pws, nws = _dev(workspace, "workspace", torch.uint8, 1), workspace.numel()
+    pout = None
+    if partition_size <= 0:
         if out is None:
             out = torch.empty_like(q)
-        pout = _dev(out, "out", q.dtype, 3)
         if out.shape != q.shape:
             raise ValueError("out must have q's shape")
-        st = load_library().pa_decode(pout, *args_common, float(scale), q_len, S, n_h, n_kv, d, NB, bs, MB, 0,
-                                      None, 0, _dtype_code(q), _stream(stream))
-        _check(st, "pa_decode")
-        return out
-    need = decode_workspace_size(S, q_len, n_h, d, MB, partition_size, bs)
-    if workspace is None:
-        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
-    pws = _dev(workspace, "workspace", torch.uint8, 1)
-    st = load_library().pa_decode(None, *args_common, float(scale), q_len, S, n_h, n_kv, d, NB, bs, MB,
-                                  partition_size, pws, workspace.numel(), _dtype_code(q), _stream(stream))
+        pout = _dev(out, "out", q.dtype, 3)
+    st = load_library().pa_decode(pout, *args_common, float(scale), q_len, S, n_h, n_kv, d, NB, bs, MB,
+                                  partition_size, pws, nws, _dtype_code(q), _stream(stream))
     _check(st, "pa_decode")
-    return workspace
+    return out if partition_size <= 0 else workspace
 
 
 def reduce(out, workspace, context_lens, q_len: int, max_blocks_per_seq: int, partition_size: int, stream=None):
@@ -215,8 +228,9 @@ def paged_attention(q, k_cache, v_cache, block_tables, context_lens, scale: floa
                     partition_size: int = 0, out=None, workspace=None, stream=None):
     """The whole attention step: pa_decode, followed by pa_reduce when partition_size > 0."""
     torch = _torch()
-    if partition_size == 0:
-        return decode(q, k_cache, v_cache, block_tables, context_lens, scale, q_len, 0, out, None, stream)
+    if partition_size <= 0:
+        return decode(q, k_cache, v_cache, block_tables, context_lens, scale, q_len, partition_size, out, workspace,
+                      stream)
     ws = decode(q, k_cache, v_cache, block_tables, context_lens, scale, q_len, partition_size, None, workspace, stream)
     if out is None:
         out = torch.empty_like(q)

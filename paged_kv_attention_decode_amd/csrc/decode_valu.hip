@@ -8,8 +8,9 @@
 // section 3.5), with one load of each K/V row serving every query row of the
 // GQA group (section 3.3: the intensity of decode attention is n_h / n_kv).
 //
-// Work decomposition: one workgroup of NW waves per (partition, KV head,
-// sequence); a partition's blocks are dealt to the waves round-robin.
+// A workgroup of NW waves attends a range of blocks of one (sequence, KV
+// head); the ranges come from pa_schedule.h (single pass, partitions, or the
+// balanced split).  The range's blocks are dealt to the waves round-robin.
 //
 // Lane layouts inside a wave (bf16, head_dim 128; other shapes scale alike):
 //   scores  4 lanes per token, 16 tokens = one block per load; each lane owns
@@ -42,14 +43,10 @@
 // beyond that sets a wave-uniform flag, and after the loop the wave redoes its
 // share exactly in two passes (maximum first, then the weighted sums).  The
 // hot loop therefore has no rescale branch and the accumulators are only ever
-// touched by FMAs.
-//
-// The waves' partials (m, l, acc) are merged in LDS with the rescaling rule;
-// a split call stores the normalized partial and (m, l) for pa_reduce
-// (section 5.3 "Decode attention and FlashDecoding"), a single pass writes
-// the output.
+// touched by FMAs.  The waves' (m, l, acc) are merged with the rescaling rule.
 #include "pa_device.h"
 #include "pa_kernels.h"
+#include "pa_schedule.h"
 
 namespace pa {
 namespace {
@@ -71,13 +68,13 @@ struct Elem<uint16_t> {
 };
 
 template <typename T>
-__device__ __forceinline__ void store_out(T* dst, float x);
+__device__ __forceinline__ void store_elem(T* dst, float x);
 template <>
-__device__ __forceinline__ void store_out<float>(float* dst, float x) { *dst = x; }
+__device__ __forceinline__ void store_elem<float>(float* dst, float x) { *dst = x; }
 template <>
-__device__ __forceinline__ void store_out<uint16_t>(uint16_t* dst, float x) { *dst = (uint16_t)f32_to_bf16_bits(x); }
+__device__ __forceinline__ void store_elem<uint16_t>(uint16_t* dst, float x) { *dst = (uint16_t)f32_to_bf16_bits(x); }
 
-// pr[r] = p[r] of lane 4 * I of this lane's DPP row (row_newbcast); I is the
+// pr[r] = p[r] of lane 4 * i of this lane's DPP row (row_newbcast); i is the
 // value-layout load index, a compile-time constant after unrolling
 template <int R>
 __device__ __forceinline__ void bcast_in_row(float (&pr)[R], const float (&p)[R], int i) {
@@ -97,317 +94,302 @@ __device__ __forceinline__ float lane_from(float x, int src) {
   return __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(src << 2, __builtin_bit_cast(int, x)));
 }
 
+template <typename T, int D, int R, int NW>
+struct WaveTotals {
+  float m[NW][R];
+  float l[NW][R];
+  float acc[NW][R][D];
+};
+
 template <typename T, int D, int R, int NW, int NBUF>
-__global__ __launch_bounds__(NW * 64) void decode_valu_kernel(DecodeParams a) {
-  constexpr bool kBF16 = sizeof(T) == 2;
-  constexpr int EPC = Elem<T>::kPer16B;  // elements per 16-byte chunk
-  constexpr int NC = D / EPC;            // chunks per head row
-  constexpr int NCK = NC / 4;            // score layout: chunks per lane
-  constexpr int TPV = 64 / NC;           // value layout: tokens per load
-  constexpr int NV = kBlockTokens / TPV; // value layout: loads per block
+struct ValuAttender {
+  static constexpr int kThreads = NW * 64;
+  static constexpr int kD = D;
+  static constexpr bool kBF16 = sizeof(T) == 2;
+  static constexpr int EPC = Elem<T>::kPer16B;     // elements per 16-byte chunk
+  static constexpr int NC = D / EPC;               // chunks per head row
+  static constexpr int NCK = NC / 4;               // score layout: chunks per lane
+  static constexpr int TPV = 64 / NC;              // value layout: tokens per load
+  static constexpr int NV = kBlockTokens / TPV;    // value layout: loads per block
+  static constexpr bool kRowTokens = NC == 16;     // value load i of lane row q holds token 4q + i
   static_assert(NC % 4 == 0 && 64 % NC == 0 && kBlockTokens % TPV == 0, "unsupported head layout");
 
-  __shared__ float s_m[NW][R];
-  __shared__ float s_l[NW][R];
-  __shared__ float s_acc[NW][R][D];
+  const DecodeParams& a;
+  WaveTotals<T, D, R, NW>& sm;
+  const int lane, w, tk, kq, vch, tv;
 
-  const int lane = threadIdx.x & 63;
-  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave index, uniform
-  const int part = blockIdx.x;
-  const int g = blockIdx.y;
-  const int b = blockIdx.z;
-  const bool split = a.part_blocks > 0;
-  const int rows = a.group * a.q_len;
+  __device__ ValuAttender(const DecodeParams& a_, WaveTotals<T, D, R, NW>& sm_)
+      : a(a_),
+        sm(sm_),
+        lane(threadIdx.x & 63),
+        w(__builtin_amdgcn_readfirstlane(threadIdx.x >> 6)),  // wave index, uniform
+        tk((threadIdx.x & 63) >> 2),
+        kq(threadIdx.x & 3),
+        vch((threadIdx.x & 63) % NC),
+        tv((threadIdx.x & 63) / NC) {}
 
-  const int tk = lane >> 2;   // score layout: token of this lane
-  const int kq = lane & 3;    // score layout: chunk phase of this lane
-  const int vch = lane % NC;  // value layout: chunk of this lane
-  const int tv = lane / NC;   // value layout: token group of this lane
-  // value layout, load i: token kRowTokens ? TPV * tv + i : tv + TPV * i
-  constexpr bool kRowTokens = NC == 16;
+  __device__ void store(size_t idx, float x) { store_elem<T>(static_cast<T*>(a.out) + idx, x); }
 
-  // query rows in registers (score layout), issued before anything waits
-  const T* __restrict__ qp = static_cast<const T*>(a.q);
-  uint4 qv[R][NCK];
+  // merged output of row r, column c over the waves
+  __device__ float result(int r, int c, float& M, float& l) const {
+    M = sm.m[0][r];
 #pragma unroll
-  for (int r = 0; r < R; ++r) {
-    const int j = r / a.group, hh = r % a.group;
+    for (int u = 1; u < NW; ++u) M = fmaxf(M, sm.m[u][r]);
+    float o = 0.0f;
+    l = 0.0f;
+    if (M != kNegInf) {
 #pragma unroll
-    for (int c = 0; c < NCK; ++c) qv[r][c] = make_uint4(0, 0, 0, 0);
-    if (r < rows) {
-      const T* qrow = qp + (((size_t)b * a.q_len + j) * a.n_h + (size_t)g * a.group + hh) * D;
-#pragma unroll
-      for (int c = 0; c < NCK; ++c) qv[r][c] = *reinterpret_cast<const uint4*>(qrow + (kq + 4 * c) * EPC);
+      for (int u = 0; u < NW; ++u) {
+        const float f = fast_exp2(sm.m[u][r] - M);
+        l += f * sm.l[u][r];
+        o += f * sm.acc[u][r][c];
+      }
     }
+    return l > 0.0f ? o / l : 0.0f;
   }
 
-  int L = a.lens[b];
-  const int Lmax = a.max_blocks * kBlockTokens;
-  L = L < 0 ? 0 : (L > Lmax ? Lmax : L);
-  const int nblk = (L + kBlockTokens - 1) / kBlockTokens;
-  const int pb = split ? a.part_blocks : nblk;
-  const int blk_begin = part * pb;
-  const int blk_end = min(blk_begin + pb, nblk);
-  T* __restrict__ op = static_cast<T*>(a.out);
+  __device__ void run(int b, int g, int L, int lo, int hi) {
+    const int rows = a.group * a.q_len;
 
-  if (blk_begin >= nblk) {
-    // split: the partition holds no token and pa_reduce never reads it.
-    // single pass with an empty context: every row is zero.
-    if (!split) {
-      for (int idx = threadIdx.x; idx < rows * D; idx += NW * 64) {
-        const int r = idx / D, c = idx % D;
-        const int j = r / a.group, hh = r % a.group;
-        const size_t orow = ((size_t)b * a.q_len + j) * a.n_h + (size_t)g * a.group + hh;
-        store_out<T>(op + orow * D + c, 0.0f);
-      }
-    }
-    return;
-  }
-
-  int vis[R];  // positions row r may see
-#pragma unroll
-  for (int r = 0; r < R; ++r) vis[r] = r < rows ? L - a.q_len + r / a.group + 1 : 0;
-
-  float m_ref[R], m_use[R], lsum[R], acc[R][EPC];
-#pragma unroll
-  for (int r = 0; r < R; ++r) {
-    m_ref[r] = kNegInf;
-    m_use[r] = 0.0f;
-    lsum[r] = 0.0f;
-#pragma unroll
-    for (int e = 0; e < EPC; ++e) acc[r][e] = 0.0f;
-  }
-
-  const uint32_t tok_bytes = (uint32_t)a.n_kv * D * sizeof(T);
-  const uint32_t blk_bytes = tok_bytes * kBlockTokens;
-  const uint32_t head_off = (uint32_t)g * D * sizeof(T);
-  const uint32_t k_off = (uint32_t)tk * tok_bytes + head_off + (uint32_t)kq * 16;
-  const uint32_t v_off = (uint32_t)(kRowTokens ? TPV * tv : tv) * tok_bytes + head_off + (uint32_t)vch * 16;
-  const uint32_t v_step = (kRowTokens ? 1u : (uint32_t)TPV) * tok_bytes;  // bytes between loads i and i + 1
-  const char* kbase = static_cast<const char*>(a.k_cache);
-  const char* vbase = static_cast<const char*>(a.v_cache);
-  const int32_t* __restrict__ table = a.tables + (size_t)b * a.max_blocks;
-  const float scale_log2 = a.scale_log2;
-
-  // this wave's blocks: blk_begin + w + NW * k
-  const int n_mine = (blk_end - blk_begin - w + NW - 1) / NW;
-
-  // ids of this wave's blocks k0 .. k0 + 63, one per lane
-  auto block_ids = [&](int k0, int cnt) { return lane < cnt ? table[blk_begin + w + NW * (k0 + lane)] : 0; };
-
-  auto issue = [&](int ids, int cnt, int k0, int kk, uint4(&kb)[NCK], uint4(&vb)[NV], int& lblk, bool& ok) {
-    const int phys = __builtin_amdgcn_readlane(ids, kk < cnt ? kk : 0);
-    ok = kk < cnt && (unsigned)phys < (unsigned)a.num_blocks;
-    lblk = blk_begin + w + NW * (k0 + kk);
-    const int valid = min(kBlockTokens, L - lblk * kBlockTokens);
-    const size_t boff = ok ? (size_t)phys * blk_bytes : 0;
-    const uint32_t nrec = ok ? (uint32_t)valid * tok_bytes : 0u;
-    const __amdgpu_buffer_rsrc_t kr =
-        __builtin_amdgcn_make_buffer_rsrc((void*)(kbase + boff), (short)0, (int)nrec, kBufferWord3);
-    const __amdgpu_buffer_rsrc_t vr =
-        __builtin_amdgcn_make_buffer_rsrc((void*)(vbase + boff), (short)0, (int)nrec, kBufferWord3);
-#pragma unroll
-    for (int c = 0; c < NCK; ++c)
-      kb[c] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(kr, k_off + 64 * c, 0, 0));
-#pragma unroll
-    for (int i = 0; i < NV; ++i)
-      vb[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(vr, v_off, i * v_step, 0));
-  };
-
-  // scores of this lane's token for every row, log2 units, -inf where masked
-  auto scores = [&](const uint4(&kb)[NCK], int lblk, bool ok, float(&s)[R]) {
-    const int pos = lblk * kBlockTokens + tk;
+    // query rows in registers (score layout)
+    const T* __restrict__ qp = static_cast<const T*>(a.q);
+    uint4 qv[R][NCK];
 #pragma unroll
     for (int r = 0; r < R; ++r) {
-      float x = 0.0f;
+      const int j = r / a.group, hh = r % a.group;
 #pragma unroll
-      for (int c = 0; c < NCK; ++c) {
-        if constexpr (kBF16) {
-          x = dot2_bf16(qv[r][c].x, kb[c].x, x);
-          x = dot2_bf16(qv[r][c].y, kb[c].y, x);
-          x = dot2_bf16(qv[r][c].z, kb[c].z, x);
-          x = dot2_bf16(qv[r][c].w, kb[c].w, x);
-        } else {
-          x = fmaf(__builtin_bit_cast(float, qv[r][c].x), __builtin_bit_cast(float, kb[c].x), x);
-          x = fmaf(__builtin_bit_cast(float, qv[r][c].y), __builtin_bit_cast(float, kb[c].y), x);
-          x = fmaf(__builtin_bit_cast(float, qv[r][c].z), __builtin_bit_cast(float, kb[c].z), x);
-          x = fmaf(__builtin_bit_cast(float, qv[r][c].w), __builtin_bit_cast(float, kb[c].w), x);
-        }
+      for (int c = 0; c < NCK; ++c) qv[r][c] = make_uint4(0, 0, 0, 0);
+      if (r < rows) {
+        const T* qrow = qp + (((size_t)b * a.q_len + j) * a.n_h + (size_t)g * a.group + hh) * D;
+#pragma unroll
+        for (int c = 0; c < NCK; ++c) qv[r][c] = *reinterpret_cast<const uint4*>(qrow + (kq + 4 * c) * EPC);
       }
-      const float sr = quad_sum(x) * scale_log2;  // every lane, so the DPP sources are live
-      s[r] = (ok && pos < vis[r]) ? sr : kNegInf;
     }
-  };
 
-  // weights against the wave's reference, l, and P * V
-  auto accumulate = [&](const float(&s)[R], const uint4(&vb)[NV]) {
-    float p[R];
+    int vis[R];  // positions row r may see
+#pragma unroll
+    for (int r = 0; r < R; ++r) vis[r] = r < rows ? L - a.q_len + r / a.group + 1 : 0;
+
+    float m_ref[R], m_use[R], lsum[R], acc[R][EPC];
 #pragma unroll
     for (int r = 0; r < R; ++r) {
-      p[r] = fast_exp2(s[r] - m_use[r]);
-      lsum[r] += p[r];
-    }
-#pragma unroll
-    for (int i = 0; i < NV; ++i) {
-      // weights of the token this lane's value load i holds
-      float pr[R];
-      if constexpr (kRowTokens) {
-        bcast_in_row<R>(pr, p, i);
-      } else {
-        const int src = 4 * (tv + TPV * i);
-#pragma unroll
-        for (int r = 0; r < R; ++r) pr[r] = lane_from(p[r], src);
-      }
-      float vf[EPC];
-      if constexpr (kBF16) {
-        vf[0] = bf16_lo(vb[i].x); vf[1] = bf16_hi(vb[i].x);
-        vf[2] = bf16_lo(vb[i].y); vf[3] = bf16_hi(vb[i].y);
-        vf[4] = bf16_lo(vb[i].z); vf[5] = bf16_hi(vb[i].z);
-        vf[6] = bf16_lo(vb[i].w); vf[7] = bf16_hi(vb[i].w);
-      } else {
-        vf[0] = __builtin_bit_cast(float, vb[i].x); vf[1] = __builtin_bit_cast(float, vb[i].y);
-        vf[2] = __builtin_bit_cast(float, vb[i].z); vf[3] = __builtin_bit_cast(float, vb[i].w);
-      }
-#pragma unroll
-      for (int r = 0; r < R; ++r)
-#pragma unroll
-        for (int e = 0; e < EPC; ++e) acc[r][e] = fmaf(pr[r], vf[e], acc[r][e]);
-    }
-  };
-
-  auto set_reference = [&](const float(&mx)[R]) {
-#pragma unroll
-    for (int r = 0; r < R; ++r) {
-      m_ref[r] = wave_max(mx[r]);
-      m_use[r] = m_ref[r] == kNegInf ? 0.0f : m_ref[r];
-    }
-  };
-
-  bool overflow = false;  // wave-uniform
-  for (int k0 = 0; k0 < n_mine; k0 += 64) {
-    const int cnt = min(64, n_mine - k0);
-    const int ids = block_ids(k0, cnt);
-
-    // NBUF register sets in flight: block kk + u computes while the next NBUF - 1 load
-    uint4 kb[NBUF][NCK], vb[NBUF][NV];
-    int lb[NBUF];
-    bool okb[NBUF];
-#pragma unroll
-    for (int u = 0; u < NBUF; ++u) issue(ids, cnt, k0, u, kb[u], vb[u], lb[u], okb[u]);
-    if (k0 == 0) {
-      float s0[R];
-      scores(kb[0], lb[0], okb[0], s0);
-      set_reference(s0);
-    }
-    for (int kk = 0; kk < cnt; kk += NBUF) {
-#pragma unroll
-      for (int u = 0; u < NBUF; ++u) {
-        if (kk + u < cnt) {
-          float s[R];
-          scores(kb[u], lb[u], okb[u], s);
-          bool big = false;
-#pragma unroll
-          for (int r = 0; r < R; ++r) big |= s[r] > m_ref[r] + kOverflowSlack;
-          overflow |= __builtin_amdgcn_ballot_w64(big) != 0;
-          accumulate(s, vb[u]);
-        }
-        issue(ids, cnt, k0, kk + u + NBUF, kb[u], vb[u], lb[u], okb[u]);
-      }
-    }
-  }
-
-  if (overflow) {
-    // some weight would have left the safe range: redo this wave's share
-    // exactly, the maximum first and then the weighted sums
-    float mx[R];
-#pragma unroll
-    for (int r = 0; r < R; ++r) {
-      mx[r] = kNegInf;
+      m_ref[r] = kNegInf;
+      m_use[r] = 0.0f;
       lsum[r] = 0.0f;
 #pragma unroll
       for (int e = 0; e < EPC; ++e) acc[r][e] = 0.0f;
     }
+
+    const uint32_t tok_bytes = (uint32_t)a.n_kv * D * sizeof(T);
+    const uint32_t blk_bytes = tok_bytes * kBlockTokens;
+    const uint32_t head_off = (uint32_t)g * D * sizeof(T);
+    const uint32_t k_off = (uint32_t)tk * tok_bytes + head_off + (uint32_t)kq * 16;
+    const uint32_t v_off = (uint32_t)(kRowTokens ? TPV * tv : tv) * tok_bytes + head_off + (uint32_t)vch * 16;
+    const uint32_t v_step = (kRowTokens ? 1u : (uint32_t)TPV) * tok_bytes;  // bytes between value loads i, i + 1
+    const char* kbase = static_cast<const char*>(a.k_cache);
+    const char* vbase = static_cast<const char*>(a.v_cache);
+    const int32_t* __restrict__ table = a.tables + (size_t)b * a.max_blocks;
+    const float scale_log2 = a.scale_log2;
+
+    // this wave's blocks: lo + w + NW * k
+    const int n_mine = hi - lo > w ? (hi - lo - w + NW - 1) / NW : 0;
+
+    // ids of this wave's blocks k0 .. k0 + 63, one per lane
+    auto block_ids = [&](int k0, int cnt) { return lane < cnt ? table[lo + w + NW * (k0 + lane)] : 0; };
+
+    auto issue = [&](int ids, int cnt, int k0, int kk, uint4(&kb)[NCK], uint4(&vb)[NV], int& lblk, bool& ok) {
+      const int phys = __builtin_amdgcn_readlane(ids, kk < cnt ? kk : 0);
+      ok = kk < cnt && (unsigned)phys < (unsigned)a.num_blocks;
+      lblk = lo + w + NW * (k0 + kk);
+      const int valid = min(kBlockTokens, L - lblk * kBlockTokens);
+      const size_t boff = ok ? (size_t)phys * blk_bytes : 0;
+      const uint32_t nrec = ok ? (uint32_t)valid * tok_bytes : 0u;
+      const __amdgpu_buffer_rsrc_t kr =
+          __builtin_amdgcn_make_buffer_rsrc((void*)(kbase + boff), (short)0, (int)nrec, kBufferWord3);
+      const __amdgpu_buffer_rsrc_t vr =
+          __builtin_amdgcn_make_buffer_rsrc((void*)(vbase + boff), (short)0, (int)nrec, kBufferWord3);
+#pragma unroll
+      for (int c = 0; c < NCK; ++c)
+        kb[c] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(kr, k_off + 64 * c, 0, 0));
+#pragma unroll
+      for (int i = 0; i < NV; ++i)
+        vb[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(vr, v_off, i * v_step, 0));
+    };
+
+    // scores of this lane's token for every row, log2 units, -inf where masked
+    auto scores = [&](const uint4(&kb)[NCK], int lblk, bool ok, float(&s)[R]) {
+      const int pos = lblk * kBlockTokens + tk;
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        float x = 0.0f;
+#pragma unroll
+        for (int c = 0; c < NCK; ++c) {
+          if constexpr (kBF16) {
+            x = dot2_bf16(qv[r][c].x, kb[c].x, x);
+            x = dot2_bf16(qv[r][c].y, kb[c].y, x);
+            x = dot2_bf16(qv[r][c].z, kb[c].z, x);
+            x = dot2_bf16(qv[r][c].w, kb[c].w, x);
+          } else {
+            x = fmaf(__builtin_bit_cast(float, qv[r][c].x), __builtin_bit_cast(float, kb[c].x), x);
+            x = fmaf(__builtin_bit_cast(float, qv[r][c].y), __builtin_bit_cast(float, kb[c].y), x);
+            x = fmaf(__builtin_bit_cast(float, qv[r][c].z), __builtin_bit_cast(float, kb[c].z), x);
+            x = fmaf(__builtin_bit_cast(float, qv[r][c].w), __builtin_bit_cast(float, kb[c].w), x);
+          }
+        }
+        const float sr = quad_sum(x) * scale_log2;  // every lane, so the DPP sources are live
+        s[r] = (ok && pos < vis[r]) ? sr : kNegInf;
+      }
+    };
+
+    // weights against the wave's reference, l, and P * V
+    auto accumulate = [&](const float(&s)[R], const uint4(&vb)[NV]) {
+      float p[R];
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        p[r] = fast_exp2(s[r] - m_use[r]);
+        lsum[r] += p[r];
+      }
+#pragma unroll
+      for (int i = 0; i < NV; ++i) {
+        // weights of the token this lane's value load i holds
+        float pr[R];
+        if constexpr (kRowTokens) {
+          bcast_in_row<R>(pr, p, i);
+        } else {
+          const int src = 4 * (tv + TPV * i);
+#pragma unroll
+          for (int r = 0; r < R; ++r) pr[r] = lane_from(p[r], src);
+        }
+        float vf[EPC];
+        if constexpr (kBF16) {
+          vf[0] = bf16_lo(vb[i].x); vf[1] = bf16_hi(vb[i].x);
+          vf[2] = bf16_lo(vb[i].y); vf[3] = bf16_hi(vb[i].y);
+          vf[4] = bf16_lo(vb[i].z); vf[5] = bf16_hi(vb[i].z);
+          vf[6] = bf16_lo(vb[i].w); vf[7] = bf16_hi(vb[i].w);
+        } else {
+          vf[0] = __builtin_bit_cast(float, vb[i].x); vf[1] = __builtin_bit_cast(float, vb[i].y);
+          vf[2] = __builtin_bit_cast(float, vb[i].z); vf[3] = __builtin_bit_cast(float, vb[i].w);
+        }
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+#pragma unroll
+          for (int e = 0; e < EPC; ++e) acc[r][e] = fmaf(pr[r], vf[e], acc[r][e]);
+      }
+    };
+
+    auto set_reference = [&](const float(&mx)[R]) {
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        m_ref[r] = wave_max(mx[r]);
+        m_use[r] = m_ref[r] == kNegInf ? 0.0f : m_ref[r];
+      }
+    };
+
+    bool overflow = false;  // wave-uniform
     for (int k0 = 0; k0 < n_mine; k0 += 64) {
       const int cnt = min(64, n_mine - k0);
       const int ids = block_ids(k0, cnt);
-      for (int kk = 0; kk < cnt; ++kk) {
-        uint4 kb1[NCK], vb1[NV];
-        int lb1;
-        bool ok1;
-        issue(ids, cnt, k0, kk, kb1, vb1, lb1, ok1);
-        float s[R];
-        scores(kb1, lb1, ok1, s);
-#pragma unroll
-        for (int r = 0; r < R; ++r) mx[r] = fmaxf(mx[r], s[r]);
-      }
-    }
-    set_reference(mx);
-    for (int k0 = 0; k0 < n_mine; k0 += 64) {
-      const int cnt = min(64, n_mine - k0);
-      const int ids = block_ids(k0, cnt);
-      for (int kk = 0; kk < cnt; ++kk) {
-        uint4 kb1[NCK], vb1[NV];
-        int lb1;
-        bool ok1;
-        issue(ids, cnt, k0, kk, kb1, vb1, lb1, ok1);
-        float s[R];
-        scores(kb1, lb1, ok1, s);
-        accumulate(s, vb1);
-      }
-    }
-  }
 
-  // ---- wave totals: l over the 16 tokens (each held by 4 lanes), acc over the value token phases
+      // NBUF register sets in flight: block kk + u computes while the next NBUF - 1 load
+      uint4 kb[NBUF][NCK], vb[NBUF][NV];
+      int lb[NBUF];
+      bool okb[NBUF];
 #pragma unroll
-  for (int r = 0; r < R; ++r) {
-    const float lw = wave_sum(lsum[r]) * 0.25f;
+      for (int u = 0; u < NBUF; ++u) issue(ids, cnt, k0, u, kb[u], vb[u], lb[u], okb[u]);
+      if (k0 == 0) {
+        float s0[R];
+        scores(kb[0], lb[0], okb[0], s0);
+        set_reference(s0);
+      }
+      for (int kk = 0; kk < cnt; kk += NBUF) {
 #pragma unroll
-    for (int e = 0; e < EPC; ++e) {
-      float x = acc[r][e];
+        for (int u = 0; u < NBUF; ++u) {
+          if (kk + u < cnt) {
+            float s[R];
+            scores(kb[u], lb[u], okb[u], s);
+            bool big = false;
 #pragma unroll
-      for (int off = NC; off < 64; off <<= 1) x += shfl_xor(x, off);
-      acc[r][e] = x;
+            for (int r = 0; r < R; ++r) big |= s[r] > m_ref[r] + kOverflowSlack;
+            overflow |= __builtin_amdgcn_ballot_w64(big) != 0;
+            accumulate(s, vb[u]);
+          }
+          issue(ids, cnt, k0, kk + u + NBUF, kb[u], vb[u], lb[u], okb[u]);
+        }
+      }
     }
-    if (lane == 0) {
-      s_m[w][r] = m_ref[r];
-      s_l[w][r] = lw;
-    }
-    if (lane < NC) {
-#pragma unroll
-      for (int e = 0; e < EPC; ++e) s_acc[w][r][lane * EPC + e] = acc[r][e];
-    }
-  }
-  __syncthreads();
 
-  // ---- merge the waves, then normalize (single pass) or store the partial (split)
-  for (int idx = threadIdx.x; idx < rows * D; idx += NW * 64) {
-    const int r = idx / D, c = idx % D;
-    float M = s_m[0][r];
+    if (overflow) {
+      // some weight would have left the safe range: redo this wave's share
+      // exactly, the maximum first and then the weighted sums
+      float mx[R];
 #pragma unroll
-    for (int u = 1; u < NW; ++u) M = fmaxf(M, s_m[u][r]);
-    float o = 0.0f, l = 0.0f;
-    if (M != kNegInf) {
+      for (int r = 0; r < R; ++r) {
+        mx[r] = kNegInf;
+        lsum[r] = 0.0f;
 #pragma unroll
-      for (int u = 0; u < NW; ++u) {
-        const float f = fast_exp2(s_m[u][r] - M);
-        l += f * s_l[u][r];
-        o += f * s_acc[u][r][c];
+        for (int e = 0; e < EPC; ++e) acc[r][e] = 0.0f;
+      }
+      for (int k0 = 0; k0 < n_mine; k0 += 64) {
+        const int cnt = min(64, n_mine - k0);
+        const int ids = block_ids(k0, cnt);
+        for (int kk = 0; kk < cnt; ++kk) {
+          uint4 kb1[NCK], vb1[NV];
+          int lb1;
+          bool ok1;
+          issue(ids, cnt, k0, kk, kb1, vb1, lb1, ok1);
+          float s[R];
+          scores(kb1, lb1, ok1, s);
+#pragma unroll
+          for (int r = 0; r < R; ++r) mx[r] = fmaxf(mx[r], s[r]);
+        }
+      }
+      set_reference(mx);
+      for (int k0 = 0; k0 < n_mine; k0 += 64) {
+        const int cnt = min(64, n_mine - k0);
+        const int ids = block_ids(k0, cnt);
+        for (int kk = 0; kk < cnt; ++kk) {
+          uint4 kb1[NCK], vb1[NV];
+          int lb1;
+          bool ok1;
+          issue(ids, cnt, k0, kk, kb1, vb1, lb1, ok1);
+          float s[R];
+          scores(kb1, lb1, ok1, s);
+          accumulate(s, vb1);
+        }
       }
     }
-    const float res = l > 0.0f ? o / l : 0.0f;
-    const int j = r / a.group, hh = r % a.group;
-    const size_t orow = ((size_t)b * a.q_len + j) * a.n_h + (size_t)g * a.group + hh;
-    if (split) {
-      const size_t pi = orow * a.num_parts + part;
-      a.ws_o[pi * D + c] = res;
-      if (c == 0) {
-        a.ws_m[pi] = M;
-        a.ws_l[pi] = l;
+
+    // wave totals: l over the 16 tokens (each held by 4 lanes), acc over the value token phases
+    __syncthreads();  // the previous range's totals have been read
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const float lw = wave_sum(lsum[r]) * 0.25f;
+#pragma unroll
+      for (int e = 0; e < EPC; ++e) {
+        float x = acc[r][e];
+#pragma unroll
+        for (int off = NC; off < 64; off <<= 1) x += shfl_xor(x, off);
+        acc[r][e] = x;
       }
-    } else {
-      store_out<T>(op + orow * D + c, res);
+      if (lane == 0) {
+        sm.m[w][r] = m_ref[r];
+        sm.l[w][r] = lw;
+      }
+      if (lane < NC) {
+#pragma unroll
+        for (int e = 0; e < EPC; ++e) sm.acc[w][r][lane * EPC + e] = acc[r][e];
+      }
     }
+    __syncthreads();
   }
+};
+
+template <typename T, int D, int R, int NW, int NBUF, bool BALANCED>
+__global__ __launch_bounds__(NW * 64) void decode_valu_kernel(DecodeParams a) {
+  __shared__ WaveTotals<T, D, R, NW> sm;
+  ValuAttender<T, D, R, NW, NBUF> at(a, sm);
+  if constexpr (BALANCED) drive_balanced(a, at);
+  else drive_fixed(a, at);
 }
 
 // Blocks in flight per wave: as many as fit next to the query chunks and the
@@ -424,9 +406,14 @@ constexpr int blocks_in_flight() {
 
 template <typename T, int D, int R>
 hipError_t launch_one(const DecodeParams& p, hipStream_t s) {
-  dim3 grid(p.part_blocks > 0 ? p.num_parts : 1, p.n_kv, p.num_seqs);
-  hipLaunchKernelGGL((decode_valu_kernel<T, D, R, kWaves, blocks_in_flight<T, D, R>()>), grid, dim3(kWaves * 64), 0,
-                     s, p);
+  constexpr int NB = blocks_in_flight<T, D, R>();
+  if (p.mode == kBalanced) {
+    hipLaunchKernelGGL((decode_valu_kernel<T, D, R, kWaves, NB, true>), dim3(p.num_wgs), dim3(kWaves * 64), 0, s,
+                       p);
+  } else {
+    dim3 grid(p.mode == kPartitions ? p.num_parts : 1, p.n_kv, p.num_seqs);
+    hipLaunchKernelGGL((decode_valu_kernel<T, D, R, kWaves, NB, false>), grid, dim3(kWaves * 64), 0, s, p);
+  }
   return hipGetLastError();
 }
 

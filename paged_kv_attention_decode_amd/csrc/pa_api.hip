@@ -19,13 +19,27 @@ size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 struct WsLayout {
-  size_t m_off, l_off, o_off, total;
+  size_t m_off, l_off, o_off, total;  // partitions
+  size_t cnt_off, piece_off;           // balanced
   int parts;
 };
 
-bool workspace_layout(int32_t S, int32_t q_len, int32_t n_h, int32_t D, int32_t MB, int32_t bs, int32_t ps,
-                      WsLayout* w) {
-  if (S < 0 || q_len <= 0 || n_h <= 0 || D <= 0 || MB <= 0 || bs <= 0 || ps <= 0 || ps % bs != 0) return false;
+constexpr int kBalancedMaxWGs = 1024;
+
+// partition_size > 0: max_logits[R][P], exp_sums[R][P], partial outputs [R][P][D] (R = rows, P = partitions)
+// partition_size == PA_BALANCED: counters int32[S * n_kv], pieces [2 * kBalancedMaxWGs][rows per KV head][D + 2]
+bool workspace_layout(int32_t S, int32_t q_len, int32_t n_h, int32_t n_kv, int32_t D, int32_t MB, int32_t bs,
+                      int32_t ps, WsLayout* w) {
+  if (S < 0 || q_len <= 0 || n_h <= 0 || n_kv <= 0 || n_h % n_kv != 0 || D <= 0 || MB <= 0 || bs <= 0) return false;
+  *w = WsLayout{};
+  if (ps == PA_BALANCED) {
+    const size_t rows_kv = (size_t)(n_h / n_kv) * q_len;
+    w->cnt_off = 0;
+    w->piece_off = align_up((size_t)S * n_kv * sizeof(int32_t));
+    w->total = w->piece_off + align_up(2 * (size_t)kBalancedMaxWGs * rows_kv * (D + 2) * sizeof(float));
+    return true;
+  }
+  if (ps <= 0 || ps % bs != 0) return false;
   const size_t ctx = (size_t)MB * bs;
   const size_t parts = (ctx + ps - 1) / ps;
   if (parts > 0x7fffffff) return false;
@@ -37,6 +51,16 @@ bool workspace_layout(int32_t S, int32_t q_len, int32_t n_h, int32_t D, int32_t 
   w->o_off = 2 * stats;
   w->total = 2 * stats + align_up(rows * parts * (size_t)D * sizeof(float));
   return true;
+}
+
+// workgroups of a balanced launch: two per compute unit (what the decode
+// kernels keep resident), at most the workspace's capacity
+int balanced_workgroups() {
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) !=
+                                               hipSuccess || cus <= 0)
+    cus = 256;
+  return 2 * cus < kBalancedMaxWGs ? 2 * cus : kBalancedMaxWGs;
 }
 
 pa_status from_hip(hipError_t e) { return e == hipSuccess ? PA_OK : PA_ERR_HIP; }
@@ -53,7 +77,7 @@ const char* pa_status_string(pa_status s) {
     case PA_ERR_UNSUPPORTED:
       return "PA_ERR_UNSUPPORTED: head_dim must be 64 or 128, block_size 16, rows per KV head <= 8 (fp32) or "
              "<= 64 (bf16), dtype PA_F32 or PA_BF16";
-    case PA_ERR_WORKSPACE: return "PA_ERR_WORKSPACE: workspace missing or smaller than pa_decode_workspace_size()";
+    case PA_ERR_WORKSPACE: return "PA_ERR_WORKSPACE: workspace missing, misaligned or smaller than pa_decode_workspace_size()";
     case PA_ERR_HIP: return "PA_ERR_HIP: the HIP runtime reported an error at launch";
   }
   return "unknown pa_status";
@@ -86,10 +110,12 @@ pa_status pa_cache_write(const void* k, const void* v, void* k_cache, void* v_ca
   return from_hip(pa::launch_cache_write(p, static_cast<hipStream_t>(stream)));
 }
 
-size_t pa_decode_workspace_size(int32_t num_seqs, int32_t q_len, int32_t num_q_heads, int32_t head_dim,
-                                int32_t max_blocks_per_seq, int32_t block_size, int32_t partition_size) {
+size_t pa_decode_workspace_size(int32_t num_seqs, int32_t q_len, int32_t num_q_heads, int32_t num_kv_heads,
+                                int32_t head_dim, int32_t max_blocks_per_seq, int32_t block_size,
+                                int32_t partition_size) {
   WsLayout w;
-  if (!workspace_layout(num_seqs, q_len, num_q_heads, head_dim, max_blocks_per_seq, block_size, partition_size, &w))
+  if (!workspace_layout(num_seqs, q_len, num_q_heads, num_kv_heads, head_dim, max_blocks_per_seq, block_size,
+                        partition_size, &w))
     return 0;
   return w.total;
 }
@@ -102,8 +128,8 @@ pa_status pa_decode(void* out, const void* q, const void* k_cache, const void* v
   if (dtype != PA_F32 && dtype != PA_BF16) return PA_ERR_UNSUPPORTED;
   if (block_size != kBlock || (head_dim != 64 && head_dim != 128)) return PA_ERR_UNSUPPORTED;
   if (num_seqs < 0 || q_len < 1 || q_len > 8 || num_q_heads <= 0 || num_kv_heads <= 0 ||
-      num_q_heads % num_kv_heads != 0 || num_blocks <= 0 || max_blocks_per_seq <= 0 || partition_size < 0 ||
-      partition_size % kBlock != 0)
+      num_q_heads % num_kv_heads != 0 || num_blocks <= 0 || max_blocks_per_seq <= 0 ||
+      (partition_size < 0 && partition_size != PA_BALANCED) || (partition_size > 0 && partition_size % kBlock != 0))
     return PA_ERR_SHAPE;
   if (num_seqs > 65535 || num_kv_heads > 65535) return PA_ERR_UNSUPPORTED;
   const int group = num_q_heads / num_kv_heads;
@@ -111,6 +137,7 @@ pa_status pa_decode(void* out, const void* q, const void* k_cache, const void* v
   if (rows > (dtype == PA_F32 ? kMaxRowsF32 : kMaxRowsBF16)) return PA_ERR_UNSUPPORTED;
   if (num_seqs == 0) return PA_OK;
   const bool split = partition_size > 0;
+  const bool balanced = partition_size == PA_BALANCED;
   if (!q || !k_cache || !v_cache || !block_tables || !context_lens || (!split && !out)) return PA_ERR_NULL;
   if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || (out && !aligned16(out))) return PA_ERR_SHAPE;
 
@@ -129,21 +156,31 @@ pa_status pa_decode(void* out, const void* q, const void* k_cache, const void* v
   p.num_blocks = num_blocks;
   p.max_blocks = max_blocks_per_seq;
   p.num_seqs = num_seqs;
+  p.mode = pa::kSinglePass;
   p.part_blocks = 0;
   p.num_parts = 1;
-  if (split) {
+  p.num_wgs = 0;
+  if (split || balanced) {
     WsLayout w;
-    if (!workspace_layout(num_seqs, q_len, num_q_heads, head_dim, max_blocks_per_seq, block_size, partition_size,
-                          &w))
+    if (!workspace_layout(num_seqs, q_len, num_q_heads, num_kv_heads, head_dim, max_blocks_per_seq, block_size,
+                          partition_size, &w))
       return PA_ERR_SHAPE;
     if (!workspace) return PA_ERR_WORKSPACE;
     if (workspace_bytes < w.total || !aligned16(workspace)) return PA_ERR_WORKSPACE;
     char* base = static_cast<char*>(workspace);
-    p.ws_m = reinterpret_cast<float*>(base + w.m_off);
-    p.ws_l = reinterpret_cast<float*>(base + w.l_off);
-    p.ws_o = reinterpret_cast<float*>(base + w.o_off);
-    p.part_blocks = partition_size / kBlock;
-    p.num_parts = w.parts;
+    if (split) {
+      p.mode = pa::kPartitions;
+      p.ws_m = reinterpret_cast<float*>(base + w.m_off);
+      p.ws_l = reinterpret_cast<float*>(base + w.l_off);
+      p.ws_o = reinterpret_cast<float*>(base + w.o_off);
+      p.part_blocks = partition_size / kBlock;
+      p.num_parts = w.parts;
+    } else if (num_seqs <= pa::kBalancedMaxSeqs) {
+      p.mode = pa::kBalanced;
+      p.counters = reinterpret_cast<int*>(base + w.cnt_off);
+      p.pieces = reinterpret_cast<float*>(base + w.piece_off);
+      p.num_wgs = balanced_workgroups();
+    }
   }
   hipStream_t s = static_cast<hipStream_t>(stream);
   static_assert(kMaxRowsBF16 <= kMaxRowsValu, "rows beyond the VALU kernel need the matrix-core kernel");
@@ -163,7 +200,8 @@ pa_status pa_reduce(void* out, const void* workspace, size_t workspace_bytes, co
   if (!out || !context_lens) return PA_ERR_NULL;
   if (!aligned16(out)) return PA_ERR_SHAPE;
   WsLayout w;
-  if (!workspace_layout(num_seqs, q_len, num_q_heads, head_dim, max_blocks_per_seq, block_size, partition_size, &w))
+  if (!workspace_layout(num_seqs, q_len, num_q_heads, 1, head_dim, max_blocks_per_seq, block_size, partition_size,
+                        &w))
     return PA_ERR_SHAPE;
   if (!workspace) return PA_ERR_WORKSPACE;
   if (workspace_bytes < w.total || !aligned16(workspace)) return PA_ERR_WORKSPACE;

@@ -9,20 +9,34 @@ namespace pa {
 
 enum ElemType { kF32 = 0, kBF16 = 1 };
 
+// How a decode call divides the work among workgroups.
+enum DecodeMode {
+  kSinglePass = 0,  // one workgroup per (KV head, sequence); writes out
+  kPartitions = 1,  // one workgroup per (partition, KV head, sequence); writes partials for pa_reduce
+  kBalanced = 2,    // equal block ranges of the flattened (sequence, KV head, block) list; writes out
+};
+
+// largest batch the balanced mode handles (its block prefix over the sequences lives in LDS)
+constexpr int kBalancedMaxSeqs = 4096;
+
 struct DecodeParams {
-  void* out;             // [S*q_len, n_h, D] (single pass only)
+  void* out;             // [S*q_len, n_h, D] (single pass and balanced)
   const void* q;         // [S*q_len, n_h, D]
   const void* k_cache;   // [NB, 16, n_kv, D]
   const void* v_cache;
   const int32_t* tables; // [S, MB]
   const int32_t* lens;   // [S]
-  float* ws_m;           // [S*q_len*n_h, P]  (split only)
-  float* ws_l;           // [S*q_len*n_h, P]
-  float* ws_o;           // [S*q_len*n_h, P, D]
+  float* ws_m;           // partitions: [S*q_len*n_h, P]
+  float* ws_l;           // partitions: [S*q_len*n_h, P]
+  float* ws_o;           // partitions: [S*q_len*n_h, P, D]
+  int* counters;         // balanced: [S * n_kv] arrival counters, zero between calls
+  float* pieces;         // balanced: [2 * num_wgs][rows_per_kv][D + 2] partial (m, l, o) per row
   float scale_log2;      // softmax scale * log2(e)
   int q_len, group, n_h, n_kv, num_blocks, max_blocks;
-  int part_blocks;       // blocks per partition (split), 0 = whole context
-  int num_parts;         // partition stride of the workspace (split), else 1
+  int mode;              // DecodeMode
+  int part_blocks;       // partitions: blocks per partition
+  int num_parts;         // partitions: partition stride of the workspace
+  int num_wgs;           // balanced: workgroups in the grid
   int num_seqs;
 };
 

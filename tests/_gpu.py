@@ -85,9 +85,11 @@ class DeviceProblem:
         p = self.p
         if write and self.new_k is not None:
             pa.cache_write(self.new_k, self.new_v, self.k_cache, self.v_cache, self.slots)
-        if partition_size == 0:
+        if partition_size <= 0:  # one pass or balanced
+            if partition_size < 0 and self.workspace is None:
+                self.workspace = pa.new_workspace(self.q, self.k_cache, self.block_tables, p.q_len, partition_size)
             pa.decode(self.q, self.k_cache, self.v_cache, self.block_tables, self.context_lens, float(p.scale),
-                      p.q_len, 0, out=self.out)
+                      p.q_len, partition_size, out=self.out, workspace=self.workspace)
         else:
             self.workspace = pa.decode(self.q, self.k_cache, self.v_cache, self.block_tables, self.context_lens,
                                        float(p.scale), p.q_len, partition_size, workspace=self.workspace)

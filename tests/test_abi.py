@@ -41,15 +41,19 @@ def test_status_strings(lib):
 
 
 def test_workspace_size_layout(lib):
-    # fp32 max_logits and exp_sums [rows][P], partial outputs [rows][P][d], each region 256-byte aligned
-    S, q_len, n_h, d, MB, ps = 8, 1, 32, 128, 8192, 512
+    # split: fp32 max_logits and exp_sums [rows][P], partial outputs [rows][P][d], each region 256-byte aligned
+    S, q_len, n_h, n_kv, d, MB, ps = 8, 1, 32, 8, 128, 8192, 512
     P = -(-MB * 16 // ps)
     rows = S * q_len * n_h
     stats = -(-rows * P * 4 // 256) * 256
-    assert pa.decode_workspace_size(S, q_len, n_h, d, MB, ps) == 2 * stats + -(-rows * P * d * 4 // 256) * 256
-    assert pa.decode_workspace_size(3, 5, 7, 64, 3, 48) == 2 * 512 + -(-105 * 1 * 64 * 4 // 256) * 256
-    assert pa.decode_workspace_size(S, q_len, n_h, d, MB, 0) == 0
-    assert pa.decode_workspace_size(S, q_len, n_h, d, MB, 24) == 0  # not a multiple of the block size
+    assert pa.decode_workspace_size(S, q_len, n_h, n_kv, d, MB, ps) == 2 * stats + -(-rows * P * d * 4 // 256) * 256
+    assert pa.decode_workspace_size(3, 5, 7, 7, 64, 3, 48) == 2 * 512 + -(-105 * 1 * 64 * 4 // 256) * 256
+    assert pa.decode_workspace_size(S, q_len, n_h, n_kv, d, MB, 0) == 0
+    assert pa.decode_workspace_size(S, q_len, n_h, n_kv, d, MB, 24) == 0  # not a multiple of the block size
+    assert pa.decode_workspace_size(S, q_len, n_h, n_kv, d, MB, -2) == 0
+    # balanced: counters int32[S * n_kv], then 2 * 1024 pieces of (n_h / n_kv) * q_len rows of d + 2 floats
+    got = pa.decode_workspace_size(64, 1, 32, 8, 128, 256, pa.PA_BALANCED)
+    assert got == 64 * 8 * 4 + -(-2 * 1024 * 4 * 130 * 4 // 256) * 256
 
 
 FAKE = ctypes.c_void_p(0x10000)  # aligned, never dereferenced: every call below fails validation first
@@ -78,6 +82,9 @@ def _decode(lib, **kw):
     (dict(n_h=18, n_kv=2), 3),          # 9 rows per KV head in fp32
     (dict(ps=512, ws=None), 4),
     (dict(ps=512, ws=FAKE, wsb=16), 4),
+    (dict(ps=-1, ws=None), 4),
+    (dict(ps=-1, ws=FAKE, wsb=1024), 4),
+    (dict(ps=-2), 2),
     (dict(q=ctypes.c_void_p(0x10008)), 2),  # not 16-byte aligned
 ])
 def test_decode_rejects_invalid_arguments(lib, kw, status):

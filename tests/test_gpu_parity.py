@@ -105,7 +105,7 @@ def test_length_sweep_f32(d, q_len, n_h, n_kv):
     spec = wl.Spec(name="sweep", dtype="f32", num_seqs=len(lens), num_q_heads=n_h, num_kv_heads=n_kv, head_dim=d,
                    lens=("fixed", lens), max_len=64, q_len=q_len, seed=d + q_len)
     p = wl.make_problem(spec)
-    for ps in (0, 16, 32):
+    for ps in (0, 16, 32, -1):
         say(f"sweep f32 d={d} q_len={q_len} heads={n_h}/{n_kv} partition={ps}")
         _, got = run(p, ps)
         assert_parity(got, full_reference(p), "f32", f"sweep ps={ps}", atol=1e-5)
@@ -126,7 +126,7 @@ def test_small_bf16(case):
                    seed=17 + G + d + q_len)
     p = wl.make_problem(spec)
     ref = full_reference(p)
-    for ps in (0, 16, 48, 512):
+    for ps in (0, 16, 48, 512, -1):
         say(f"small bf16 G={G} d={d} q_len={q_len} partition={ps} lens={p.context_lens.tolist()}")
         _, got = run(p, ps)
         assert_parity(got, ref, "bf16", f"partition {ps}")
@@ -137,8 +137,9 @@ def test_many_sequences_single_block():
                    lens=("uniform", 1, 16), max_len=16, seed=5)
     p = wl.make_problem(spec)
     say("300 sequences of 1..16 tokens")
-    _, got = run(p, 0)
-    assert_parity(got, full_reference(p), "bf16", "short")
+    for ps in (0, -1):
+        _, got = run(p, ps)
+        assert_parity(got, full_reference(p), "bf16", f"short ps={ps}")
 
 
 # ---------------------------------------------------------------------------
@@ -148,7 +149,7 @@ INV_SPEC = wl.Spec(name="inv", dtype="bf16", num_seqs=6, num_q_heads=16, num_kv_
                    lens=("uniform", 2, 900), max_len=960, q_len=2, seed=23)
 
 
-@pytest.mark.parametrize("ps", [0, 64])
+@pytest.mark.parametrize("ps", [0, 64, -1])
 def test_physical_permutation_is_bitwise_invariant(ps):
     p = wl.make_problem(INV_SPEC)
     say(f"permutation ps={ps}")
@@ -177,7 +178,7 @@ def test_repeatable_and_batch_independent(ps):
 def test_unread_rows_poisoned_and_garbage_padding():
     clean = wl.make_problem(INV_SPEC)
     dirty = wl.make_problem(INV_SPEC.with_(poison=True, pad="garbage"))
-    for ps in (0, 64):
+    for ps in (0, 64, -1):
         say(f"poison ps={ps}")
         _, a = run(clean, ps)
         _, b = run(dirty, ps)
@@ -204,7 +205,7 @@ def test_future_tokens_do_not_change_earlier_verify_rows():
 def test_values_all_one_give_exactly_one():
     p = wl.make_problem(INV_SPEC)
     p.v_cache[:] = np.uint16(0x3F80)
-    for ps in (0, 64):
+    for ps in (0, 64, -1):
         _, got = run(p, ps)
         assert np.all(got == 1.0), ps
 
@@ -233,7 +234,7 @@ def test_identical_keys_count_probe_fp32(q_len, L):
     for b, Lb in enumerate(lens):
         for t in range(Lb):
             p.v_cache[p.block_tables[b, t // 16], t % 16, 0, t % d] = 1.0
-    for ps in (0, 512):
+    for ps in (0, 512, -1):
         say(f"count probe q_len={q_len} L={L} ps={ps}")
         _, got = run(p, ps)
         for b, Lb in enumerate(lens):
@@ -262,10 +263,40 @@ def test_scores_rising_far_past_the_first_block(dtype, q_len):
             p.k_cache[p.block_tables[b, t // 16], t % 16, 0, 0] = (
                 wl.round_to_bf16_bits(np.array([val]))[0] if dtype == "bf16" else val)
     ref = full_reference(p)
-    for ps in (0, 512):
+    for ps in (0, 512, -1):
         say(f"ramp {dtype} q_len={q_len} ps={ps}")
         _, got = run(p, ps)
         assert_parity(got, ref, dtype, f"ramp ps={ps}")
+
+
+def test_balanced_is_repeatable_and_reuses_its_workspace():
+    """Run-to-run bitwise determinism of the balanced split, whose cut pieces are
+    merged by whichever workgroup arrives last; the workspace counters must be
+    back at zero after every call."""
+    p = wl.make_problem(INV_SPEC.with_(num_seqs=40, lens=("uniform", 2, 3000), max_len=3008))
+    d = DeviceProblem(p)
+    outs = [to_host(d.step(-1).clone()) for _ in range(4)]
+    for o in outs[1:]:
+        assert np.array_equal(outs[0], o)
+    counters = to_host(d.workspace[:4 * p.num_seqs * p.num_kv_heads].clone())
+    assert not counters.any()
+    assert_parity(widen(outs[0], "bf16"), full_reference(p), "bf16", "balanced")
+
+
+def test_balanced_with_empty_and_tiny_contexts():
+    """Zero-length contexts get zero rows; ranges that start and end inside one block."""
+    spec = wl.Spec(name="empty", dtype="bf16", num_seqs=9, num_q_heads=8, num_kv_heads=2, head_dim=128,
+                   lens=("fixed", (1, 40, 1, 3, 900, 1, 16, 17, 1)), max_len=912, seed=13)
+    p = wl.make_problem(spec)
+    ref = full_reference(p)
+    p0 = wl.Problem(**{**p.__dict__})
+    p0.context_lens = p.context_lens.copy()
+    p0.context_lens[[0, 2, 5]] = 0
+    for prob, want_zero in ((p, []), (p0, [0, 2, 5])):
+        _, got = run(prob, -1)
+        keep = [b for b in range(9) if b not in want_zero]
+        assert_parity(got[keep], ref[keep], "bf16", "balanced rows")
+        assert np.all(got[want_zero] == 0)
 
 
 # ---------------------------------------------------------------------------
