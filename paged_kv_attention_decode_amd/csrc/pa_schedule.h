@@ -39,6 +39,14 @@ __device__ __forceinline__ int clamped_len(const DecodeParams& a, int b) {
 
 __device__ __forceinline__ int blocks_of(int L) { return (L + kBlockTokens - 1) / kBlockTokens; }
 
+// stores and loads that are coherent across the whole device (all XCDs)
+__device__ __forceinline__ void coherent_store(float* p, float x) {
+  __hip_atomic_store(p, x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float coherent_load(const float* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 // output row of query row r = j * group + hh of sequence b, KV head g
 __device__ __forceinline__ size_t out_row(const DecodeParams& a, int b, int g, int r) {
   const int j = r / a.group, hh = r % a.group;
@@ -180,37 +188,42 @@ __device__ void drive_balanced(const DecodeParams& a, Attn& at) {
       // a piece: store the partial, then the last arrival merges all pieces
       const int slot = seg0 > B0 ? 2 * wid + 1 : 2 * wid;
       float* mine = a.pieces + (size_t)slot * piece_stride;
+      // The partial goes out with device-coherent stores (written through to
+      // the point of coherence of all XCDs) and every wave waits for them
+      // before the barrier, so the arrival below is ordered after them without
+      // writing back or invalidating a whole L2 (release/acquire fences at
+      // device scope do that, which costs far more than the kernel's work).
       for (int idx = tid; idx < rows * Attn::kD; idx += NT) {
         const int r = idx / Attn::kD, c = idx % Attn::kD;
         float M, l;
         const float res = at.result(r, c, M, l);
-        mine[(size_t)r * (Attn::kD + 2) + c] = res;
+        coherent_store(mine + (size_t)r * (Attn::kD + 2) + c, res);
         if (c == 0) {
-          mine[(size_t)r * (Attn::kD + 2) + Attn::kD] = M;
-          mine[(size_t)r * (Attn::kD + 2) + Attn::kD + 1] = l;
+          coherent_store(mine + (size_t)r * (Attn::kD + 2) + Attn::kD, M);
+          coherent_store(mine + (size_t)r * (Attn::kD + 2) + Attn::kD + 1, l);
         }
       }
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");  // this wave's partial, visible device-wide
+      __builtin_amdgcn_s_waitcnt(0);  // this wave's stores are complete
       __syncthreads();
       const int first = range_of(seg0, T, Wr), last = range_of(seg1 - 1, T, Wr);
       const int npieces = last - first + 1;
       if (tid == 0) {
         int* cnt = a.counters + (size_t)b * a.n_kv + g;
-        const int old = __hip_atomic_fetch_add(cnt, 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+        const int old = __hip_atomic_fetch_add(cnt, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         const int is_last = old == npieces - 1;
         if (is_last) __hip_atomic_store(cnt, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         s_last = is_last;
       }
       __syncthreads();
       if (s_last) {
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");  // the other pieces
+        // the other pieces, read with device-coherent loads (past any stale cache line)
         for (int idx = tid; idx < rows * Attn::kD; idx += NT) {
           const int r = idx / Attn::kD, c = idx % Attn::kD;
           float M = kNegInf;
           for (int k = 0; k < npieces; ++k) {
             const int w2 = first + k;
             const int sl = (k == 0 && seg0 > (long long)w2 * T / Wr) ? 2 * w2 + 1 : 2 * w2;
-            M = fmaxf(M, a.pieces[(size_t)sl * piece_stride + (size_t)r * (Attn::kD + 2) + Attn::kD]);
+            M = fmaxf(M, coherent_load(a.pieces + (size_t)sl * piece_stride + (size_t)r * (Attn::kD + 2) + Attn::kD));
           }
           float o = 0.0f, l = 0.0f;
           if (M != kNegInf) {
@@ -218,8 +231,8 @@ __device__ void drive_balanced(const DecodeParams& a, Attn& at) {
               const int w2 = first + k;
               const int sl = (k == 0 && seg0 > (long long)w2 * T / Wr) ? 2 * w2 + 1 : 2 * w2;
               const float* pc = a.pieces + (size_t)sl * piece_stride + (size_t)r * (Attn::kD + 2);
-              const float f = pc[Attn::kD + 1] * fast_exp2(pc[Attn::kD] - M);
-              o += f * pc[c];
+              const float f = coherent_load(pc + Attn::kD + 1) * fast_exp2(coherent_load(pc + Attn::kD) - M);
+              o += f * coherent_load(pc + c);
               l += f;
             }
           }
