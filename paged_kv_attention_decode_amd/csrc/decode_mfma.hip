@@ -1,0 +1,403 @@
+// Paged decode attention on the matrix cores (bf16), for 9 to 64 query rows per
+// KV head, e.g. the K + 1 tokens of a speculative verify step times the GQA
+// group.  Same computation and contract as the vector-ALU kernel (include/pa.h):
+// for each sequence b, KV head g and query row r = j * group + hh,
+//   out = sum_t softmax_t(scale * q . k_t) v_t   over the positions row r sees,
+// with the causal mask among the q_len new tokens ("07 - Inference",
+// lourdhu02.github.io, section 3: the target scores all K + 1 positions in one
+// pass), reading K and V through the block table one 16-token block at a time
+// ("LLM serving: KV cache, batching, paged attention and quantization",
+// section 3.5).  With rows = group * q_len query rows per KV head, Q K^T and
+// P V are real dense tiles, so they run on MFMA:
+//
+//   scores  S^T = K_blk Q^T per 16-row tile: v_mfma_f32_16x16x32_bf16 with
+//           A = 16 tokens x 32 dims of K (lane l: token l % 16, dims
+//           8 (l / 16) .. + 7 of the current 32), B = the same dims of 16 query
+//           rows; head_dim / 32 steps.  Lane l ends with tokens 4 (l / 16) .. + 3
+//           of row l % 16.
+//   values  O += P V: v_mfma_f32_16x16x16_bf16 with A = P (16 rows x 16 tokens),
+//           whose layout is exactly the score layout above, so the weights
+//           never leave their lanes; B = 16 tokens x 16 value columns.  A lane
+//           loads 8 bytes (4 columns) of each of its 4 tokens and a 4 x 4
+//           v_perm_b32 transpose gives the B operands; MFMA column j of call
+//           (h, e) is value column 4 j + 64 h + e.
+//
+// Memory traffic and the softmax reference follow the vector-ALU kernel: buffer
+// loads through a per-block descriptor whose record count ends at the last
+// context token, NBUF blocks in flight per wave, a per-row reference taken
+// from the wave's first block, a wave-uniform flag for weights beyond
+// 2^kOverflowSlack and an exact two-pass redo when it is raised.  Weights are
+// rounded to bf16 (v_cvt_pk_bf16_f32) for the P V product and the row sums
+// add the same rounded weights, so numerator and denominator agree.  The waves
+// of a workgroup merge one after the other into a single LDS tile.
+#include "pa_device.h"
+#include "pa_kernels.h"
+#include "pa_schedule.h"
+
+namespace pa {
+namespace {
+
+constexpr int kWaves = 4;
+constexpr float kOverflowSlack = 64.0f;  // log2 units
+constexpr int kBufferWord3 = 0x00020000;
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2_t2 __attribute__((ext_vector_type(2)));
+typedef short short4_t __attribute__((ext_vector_type(4)));
+typedef float floatx4_t __attribute__((ext_vector_type(4)));
+typedef float float2_t __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((float2_t){lo, hi}, bf16x2_t2));
+}
+
+template <int R, int D>
+struct MergeTile {
+  float m[R];      // merged row max (log2 units)
+  float l[R];      // merged row sum
+  float wm[R];     // the merging wave's row max
+  float wl[R];     // the merging wave's row sum
+  float acc[R][D];
+};
+
+template <int D, int NT, int NW, int NBUF>
+struct MfmaAttender {
+  static constexpr int kThreads = NW * 64;
+  static constexpr int kD = D;
+  static constexpr int R = 16 * NT;  // rows, padded to whole tiles
+  static constexpr int KS = D / 32;  // score k-steps
+  static constexpr int VH = D / 64;  // value column halves
+  static_assert(D == 64 || D == 128, "head_dim 64 or 128");
+
+  const DecodeParams& a;
+  MergeTile<R, D>& sm;
+  const int lane, w, j, grp;
+
+  __device__ MfmaAttender(const DecodeParams& a_, MergeTile<R, D>& sm_)
+      : a(a_),
+        sm(sm_),
+        lane(threadIdx.x & 63),
+        w(__builtin_amdgcn_readfirstlane(threadIdx.x >> 6)),
+        j(threadIdx.x & 15),
+        grp((threadIdx.x & 63) >> 4) {}
+
+  __device__ void store(size_t idx, float x) {
+    static_cast<uint16_t*>(a.out)[idx] = (uint16_t)f32_to_bf16_bits(x);
+  }
+
+  __device__ float result(int r, int c, float& M, float& l) const {
+    M = sm.m[r];
+    l = sm.l[r];
+    return l > 0.0f ? sm.acc[r][c] / l : 0.0f;
+  }
+
+  __device__ void run(int b, int g, int L, int lo, int hi) {
+    const int rows = a.group * a.q_len;
+
+    // query rows as the B operand of the score MFMA: row 16 t + j, dims 32 ks + 8 grp .. + 7
+    const uint16_t* __restrict__ qp = static_cast<const uint16_t*>(a.q);
+    uint4 qv[NT][KS];
+    int vis[NT];  // positions row 16 t + j may see
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      const int r = 16 * t + j;
+      vis[t] = r < rows ? L - a.q_len + r / a.group + 1 : 0;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) qv[t][ks] = make_uint4(0, 0, 0, 0);
+      if (r < rows) {
+        const uint16_t* qrow = qp + (((size_t)b * a.q_len + r / a.group) * a.n_h + (size_t)g * a.group + r % a.group) * D;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) qv[t][ks] = *reinterpret_cast<const uint4*>(qrow + 32 * ks + 8 * grp);
+      }
+    }
+
+    float m_ref[NT], m_use[NT], lsum[NT];
+    floatx4_t acc[NT][VH][4];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      m_ref[t] = kNegInf;
+      m_use[t] = 0.0f;
+      lsum[t] = 0.0f;
+#pragma unroll
+      for (int h = 0; h < VH; ++h)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[t][h][e] = (floatx4_t){0.0f, 0.0f, 0.0f, 0.0f};
+    }
+
+    const uint32_t tok_bytes = (uint32_t)a.n_kv * D * 2;
+    const uint32_t blk_bytes = tok_bytes * kBlockTokens;
+    const uint32_t head_off = (uint32_t)g * D * 2;
+    const uint32_t k_off = (uint32_t)j * tok_bytes + head_off + (uint32_t)grp * 16;
+    const uint32_t v_off = (uint32_t)(4 * grp) * tok_bytes + head_off + (uint32_t)j * 8;
+    const char* kbase = static_cast<const char*>(a.k_cache);
+    const char* vbase = static_cast<const char*>(a.v_cache);
+    const int32_t* __restrict__ table = a.tables + (size_t)b * a.max_blocks;
+    const float scale_log2 = a.scale_log2;
+    const int n_mine = hi - lo > w ? (hi - lo - w + NW - 1) / NW : 0;
+
+    auto block_ids = [&](int k0, int cnt) { return lane < cnt ? table[lo + w + NW * (k0 + lane)] : 0; };
+
+    // K: KS loads of 16 bytes; V: 4 tokens x VH halves of 8 bytes
+    auto issue = [&](int ids, int cnt, int k0, int kk, uint4(&kb)[KS], uint2(&vb)[4][VH], int& lblk, bool& ok) {
+      const int phys = __builtin_amdgcn_readlane(ids, kk < cnt ? kk : 0);
+      ok = kk < cnt && (unsigned)phys < (unsigned)a.num_blocks;
+      lblk = lo + w + NW * (k0 + kk);
+      const int valid = min(kBlockTokens, L - lblk * kBlockTokens);
+      const size_t boff = ok ? (size_t)phys * blk_bytes : 0;
+      const uint32_t nrec = ok ? (uint32_t)valid * tok_bytes : 0u;
+      const __amdgpu_buffer_rsrc_t kr =
+          __builtin_amdgcn_make_buffer_rsrc((void*)(kbase + boff), (short)0, (int)nrec, kBufferWord3);
+      const __amdgpu_buffer_rsrc_t vr =
+          __builtin_amdgcn_make_buffer_rsrc((void*)(vbase + boff), (short)0, (int)nrec, kBufferWord3);
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+        kb[ks] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(kr, k_off + 64 * ks, 0, 0));
+#pragma unroll
+      for (int v = 0; v < 4; ++v)
+#pragma unroll
+        for (int h = 0; h < VH; ++h)
+          vb[v][h] = __builtin_bit_cast(
+              uint2, __builtin_amdgcn_raw_buffer_load_b64(vr, v_off + 128 * h, v * tok_bytes, 0));
+    };
+
+    // scores: s[t][v] = row 16 t + j against token 4 grp + v, log2 units, -inf where masked
+    auto scores = [&](const uint4(&kb)[KS], int lblk, bool ok, floatx4_t(&s)[NT]) {
+      const int pos0 = lblk * kBlockTokens + 4 * grp;
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        floatx4_t x = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+          x = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kb[ks]),
+                                                      __builtin_bit_cast(bf16x8_t, qv[t][ks]), x, 0, 0, 0);
+#pragma unroll
+        for (int v = 0; v < 4; ++v) s[t][v] = (ok && pos0 + v < vis[t]) ? x[v] * scale_log2 : kNegInf;
+      }
+    };
+
+    auto accumulate = [&](const floatx4_t(&s)[NT], const uint2(&vb)[4][VH]) {
+      // B operands of P V: column 4 j + 64 h + e of the 4 tokens, bf16 pairs (tokens 0,1), (2,3)
+      uint2 vt[VH][4];
+#pragma unroll
+      for (int h = 0; h < VH; ++h) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
+          const uint32_t w01 = (e < 2) ? 0 : 1;
+          vt[h][e].x = __builtin_amdgcn_perm(w01 ? vb[1][h].y : vb[1][h].x, w01 ? vb[0][h].y : vb[0][h].x, sel);
+          vt[h][e].y = __builtin_amdgcn_perm(w01 ? vb[3][h].y : vb[3][h].x, w01 ? vb[2][h].y : vb[2][h].x, sel);
+        }
+      }
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        float p[4];
+#pragma unroll
+        for (int v = 0; v < 4; ++v) p[v] = fast_exp2(s[t][v] - m_use[t]);
+        uint2 pa2;
+        pa2.x = pack_bf16(p[0], p[1]);
+        pa2.y = pack_bf16(p[2], p[3]);
+        // the row sum adds the same rounded weights the product uses
+        lsum[t] += (bf16_lo(pa2.x) + bf16_hi(pa2.x)) + (bf16_lo(pa2.y) + bf16_hi(pa2.y));
+#pragma unroll
+        for (int h = 0; h < VH; ++h)
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            acc[t][h][e] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(
+                __builtin_bit_cast(short4_t, pa2), __builtin_bit_cast(short4_t, vt[h][e]), acc[t][h][e], 0, 0, 0);
+      }
+    };
+
+    // per-row reference: the row's maximum over the block (lanes j, j+16, j+32, j+48 share a row)
+    auto set_reference = [&](const floatx4_t(&mx)[NT]) {
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        float x = fmaxf(fmaxf(mx[t][0], mx[t][1]), fmaxf(mx[t][2], mx[t][3]));
+        x = fmaxf(x, shfl_xor(x, 16));
+        x = fmaxf(x, shfl_xor(x, 32));
+        m_ref[t] = x;
+        m_use[t] = x == kNegInf ? 0.0f : x;
+      }
+    };
+
+    bool overflow = false;  // wave-uniform
+    for (int k0 = 0; k0 < n_mine; k0 += 64) {
+      const int cnt = min(64, n_mine - k0);
+      const int ids = block_ids(k0, cnt);
+      uint4 kb[NBUF][KS];
+      uint2 vb[NBUF][4][VH];
+      int lb[NBUF];
+      bool okb[NBUF];
+#pragma unroll
+      for (int u = 0; u < NBUF; ++u) issue(ids, cnt, k0, u, kb[u], vb[u], lb[u], okb[u]);
+      if (k0 == 0) {
+        floatx4_t s0[NT];
+        scores(kb[0], lb[0], okb[0], s0);
+        set_reference(s0);
+      }
+      for (int kk = 0; kk < cnt; kk += NBUF) {
+#pragma unroll
+        for (int u = 0; u < NBUF; ++u) {
+          if (kk + u < cnt) {
+            floatx4_t s[NT];
+            scores(kb[u], lb[u], okb[u], s);
+            bool big = false;
+#pragma unroll
+            for (int t = 0; t < NT; ++t)
+#pragma unroll
+              for (int v = 0; v < 4; ++v) big |= s[t][v] > m_ref[t] + kOverflowSlack;
+            overflow |= __builtin_amdgcn_ballot_w64(big) != 0;
+            accumulate(s, vb[u]);
+          }
+          issue(ids, cnt, k0, kk + u + NBUF, kb[u], vb[u], lb[u], okb[u]);
+        }
+      }
+    }
+
+    if (overflow) {
+      // exact redo of this wave's share: row maxima first, then the weighted sums
+      floatx4_t mx[NT];
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        mx[t] = (floatx4_t){kNegInf, kNegInf, kNegInf, kNegInf};
+        lsum[t] = 0.0f;
+#pragma unroll
+        for (int h = 0; h < VH; ++h)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) acc[t][h][e] = (floatx4_t){0.0f, 0.0f, 0.0f, 0.0f};
+      }
+      for (int k0 = 0; k0 < n_mine; k0 += 64) {
+        const int cnt = min(64, n_mine - k0);
+        const int ids = block_ids(k0, cnt);
+        for (int kk = 0; kk < cnt; ++kk) {
+          uint4 kb1[KS];
+          uint2 vb1[4][VH];
+          int lb1;
+          bool ok1;
+          issue(ids, cnt, k0, kk, kb1, vb1, lb1, ok1);
+          floatx4_t s[NT];
+          scores(kb1, lb1, ok1, s);
+#pragma unroll
+          for (int t = 0; t < NT; ++t)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) mx[t][v] = fmaxf(mx[t][v], s[t][v]);
+        }
+      }
+      set_reference(mx);
+      for (int k0 = 0; k0 < n_mine; k0 += 64) {
+        const int cnt = min(64, n_mine - k0);
+        const int ids = block_ids(k0, cnt);
+        for (int kk = 0; kk < cnt; ++kk) {
+          uint4 kb1[KS];
+          uint2 vb1[4][VH];
+          int lb1;
+          bool ok1;
+          issue(ids, cnt, k0, kk, kb1, vb1, lb1, ok1);
+          floatx4_t s[NT];
+          scores(kb1, lb1, ok1, s);
+          accumulate(s, vb1);
+        }
+      }
+    }
+
+    // row sums over the 4 token groups; lanes j, j+16, j+32, j+48 then hold row 16 t + j
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      float x = lsum[t];
+      x += shfl_xor(x, 16);
+      x += shfl_xor(x, 32);
+      lsum[t] = x;
+    }
+
+    // merge the waves one after the other into the LDS tile
+    __syncthreads();  // the previous range's tile has been read
+    for (int u = 0; u < NW; ++u) {
+      if (w == u) {
+        if (grp == 0) {
+#pragma unroll
+          for (int t = 0; t < NT; ++t) {
+            sm.wm[16 * t + j] = m_ref[t];
+            sm.wl[16 * t + j] = lsum[t];
+          }
+        }
+        wave_lds_sync();
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+#pragma unroll
+          for (int v = 0; v < 4; ++v) {
+            const int r = 16 * t + 4 * grp + v;
+            const float mw = sm.wm[r];
+            float f_old = 0.0f, f_new = 1.0f;
+            if (u > 0) {
+              const float mo = sm.m[r];
+              const float M = fmaxf(mo, mw);
+              f_old = M == kNegInf ? 0.0f : fast_exp2(mo - M);
+              f_new = M == kNegInf ? 0.0f : fast_exp2(mw - M);
+            }
+#pragma unroll
+            for (int h = 0; h < VH; ++h)
+#pragma unroll
+              for (int e = 0; e < 4; ++e) {
+                float& dst = sm.acc[r][4 * j + 64 * h + e];
+                dst = (u > 0 ? dst * f_old : 0.0f) + acc[t][h][e][v] * f_new;
+              }
+          }
+        }
+        wave_lds_sync();
+        if (grp == 0) {
+#pragma unroll
+          for (int t = 0; t < NT; ++t) {
+            const int r = 16 * t + j;
+            if (u == 0) {
+              sm.m[r] = m_ref[t];
+              sm.l[r] = lsum[t];
+            } else {
+              const float mo = sm.m[r];
+              const float M = fmaxf(mo, m_ref[t]);
+              const float f_old = M == kNegInf ? 0.0f : fast_exp2(mo - M);
+              const float f_new = M == kNegInf ? 0.0f : fast_exp2(m_ref[t] - M);
+              sm.l[r] = sm.l[r] * f_old + lsum[t] * f_new;
+              sm.m[r] = M;
+            }
+          }
+        }
+      }
+      __syncthreads();
+    }
+  }
+};
+
+template <int D, int NT, int NW, int NBUF, bool BALANCED>
+__global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(DecodeParams a) {
+  __shared__ MergeTile<16 * NT, D> sm;
+  MfmaAttender<D, NT, NW, NBUF> at(a, sm);
+  if constexpr (BALANCED) drive_balanced(a, at);
+  else drive_fixed(a, at);
+}
+
+template <int D, int NT>
+hipError_t launch_tiles(const DecodeParams& p, hipStream_t s) {
+  constexpr int NB = NT >= 3 ? 2 : 3;  // blocks in flight per wave
+  if (p.mode == kBalanced) {
+    hipLaunchKernelGGL((decode_mfma_kernel<D, NT, kWaves, NB, true>), dim3(p.num_wgs), dim3(kWaves * 64), 0, s, p);
+  } else {
+    dim3 grid(p.mode == kPartitions ? p.num_parts : 1, p.n_kv, p.num_seqs);
+    hipLaunchKernelGGL((decode_mfma_kernel<D, NT, kWaves, NB, false>), grid, dim3(kWaves * 64), 0, s, p);
+  }
+  return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_rows(const DecodeParams& p, int rows, hipStream_t s) {
+  if (rows <= 16) return launch_tiles<D, 1>(p, s);
+  if (rows <= 32) return launch_tiles<D, 2>(p, s);
+  if (rows <= 48) return launch_tiles<D, 3>(p, s);
+  return launch_tiles<D, 4>(p, s);
+}
+
+}  // namespace
+
+hipError_t launch_decode_mfma(const DecodeParams& p, int head_dim, int rows_per_kv, hipStream_t s) {
+  return head_dim == 64 ? launch_rows<64>(p, rows_per_kv, s) : launch_rows<128>(p, rows_per_kv, s);
+}
+
+}  // namespace pa

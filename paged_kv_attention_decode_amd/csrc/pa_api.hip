@@ -11,8 +11,14 @@ namespace {
 constexpr int kBlock = 16;
 constexpr size_t kAlign = 256;
 constexpr int kMaxRowsF32 = 8;
-constexpr int kMaxRowsBF16 = 8;  // raised to 64 once the matrix-core kernel is in
-constexpr int kMaxRowsValu = 8;  // beyond this the matrix-core kernel takes bf16 inputs
+constexpr int kMaxRowsBF16 = 64;
+constexpr int kMaxRowsValu = 8;  // the vector-ALU kernel's limit
+// bf16 with at least this many rows per KV head runs on the matrix cores
+#ifndef PA_MFMA_MIN_ROWS
+#define PA_MFMA_MIN_ROWS 8
+#endif
+constexpr int kMfmaMinRows = PA_MFMA_MIN_ROWS;
+static_assert(kMfmaMinRows <= kMaxRowsValu + 1, "every row count needs a kernel");
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
@@ -183,7 +189,7 @@ pa_status pa_decode(void* out, const void* q, const void* k_cache, const void* v
     }
   }
   hipStream_t s = static_cast<hipStream_t>(stream);
-  static_assert(kMaxRowsBF16 <= kMaxRowsValu, "rows beyond the VALU kernel need the matrix-core kernel");
+  if (dtype == PA_BF16 && rows >= kMfmaMinRows) return from_hip(pa::launch_decode_mfma(p, head_dim, rows, s));
   return from_hip(pa::launch_decode_valu(p, dtype == PA_F32 ? pa::kF32 : pa::kBF16, head_dim, rows, s));
 }
 

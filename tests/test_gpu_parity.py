@@ -115,6 +115,9 @@ SMALL_BF16 = [
     dict(G=1, d=128, q_len=1), dict(G=2, d=128, q_len=1), dict(G=4, d=128, q_len=1), dict(G=8, d=128, q_len=1),
     dict(G=4, d=64, q_len=1), dict(G=8, d=64, q_len=1), dict(G=4, d=128, q_len=2), dict(G=1, d=128, q_len=5),
     dict(G=3, d=128, q_len=1),
+    # 8 to 64 rows per KV head: the matrix-core kernel, 1 to 4 row tiles
+    dict(G=8, d=128, q_len=2), dict(G=2, d=128, q_len=5), dict(G=8, d=128, q_len=5), dict(G=8, d=64, q_len=5),
+    dict(G=5, d=128, q_len=7), dict(G=16, d=128, q_len=4), dict(G=16, d=64, q_len=4), dict(G=12, d=128, q_len=5),
 ]
 
 
@@ -149,19 +152,26 @@ INV_SPEC = wl.Spec(name="inv", dtype="bf16", num_seqs=6, num_q_heads=16, num_kv_
                    lens=("uniform", 2, 900), max_len=960, q_len=2, seed=23)
 
 
+# 40 rows per KV head (8 query heads per KV head, 5 query tokens)
+INV_SPEC_WIDE = INV_SPEC.with_(num_q_heads=32, num_kv_heads=4, q_len=5, lens=("uniform", 5, 900), seed=29)
+
+
+@pytest.mark.parametrize("wide", [False, True], ids=["rows8", "rows40"])
 @pytest.mark.parametrize("ps", [0, 64, -1])
-def test_physical_permutation_is_bitwise_invariant(ps):
-    p = wl.make_problem(INV_SPEC)
+def test_physical_permutation_is_bitwise_invariant(ps, wide):
+    p = wl.make_problem(INV_SPEC_WIDE if wide else INV_SPEC)
     say(f"permutation ps={ps}")
     _, a = run(p, ps)
     _, b = run(wl.permute_physical(p, 99), ps)
     assert np.array_equal(a, b)
 
 
+@pytest.mark.parametrize("wide", [False, True], ids=["rows8", "rows40"])
 @pytest.mark.parametrize("ps", [0, 64])
-def test_repeatable_and_batch_independent(ps):
-    p = wl.make_problem(INV_SPEC)
-    say(f"repeat / batch ps={ps}")
+def test_repeatable_and_batch_independent(ps, wide):
+    p = wl.make_problem(INV_SPEC_WIDE if wide else INV_SPEC)
+    ql = p.q_len
+    say(f"repeat / batch ps={ps} rows={p.spec.group * ql}")
     d = DeviceProblem(p)
     o1 = to_host(d.step(ps).clone())
     o2 = to_host(d.step(ps).clone())
@@ -169,15 +179,17 @@ def test_repeatable_and_batch_independent(ps):
     # sequence 3 alone
     b = 3
     one = wl.Problem(spec=p.spec.with_(num_seqs=1), context_lens=p.context_lens[b:b + 1].copy(),
-                     block_tables=p.block_tables[b:b + 1].copy(), q=p.q[b * 2:(b + 1) * 2].copy(),
+                     block_tables=p.block_tables[b:b + 1].copy(), q=p.q[b * ql:(b + 1) * ql].copy(),
                      k_cache=p.k_cache, v_cache=p.v_cache, scale=p.scale)
     _, alone = run(one, ps)
-    assert np.array_equal(widen(o1[b * 2:(b + 1) * 2], "bf16"), alone)
+    assert np.array_equal(widen(o1[b * ql:(b + 1) * ql], "bf16"), alone)
 
 
-def test_unread_rows_poisoned_and_garbage_padding():
-    clean = wl.make_problem(INV_SPEC)
-    dirty = wl.make_problem(INV_SPEC.with_(poison=True, pad="garbage"))
+@pytest.mark.parametrize("wide", [False, True], ids=["rows8", "rows40"])
+def test_unread_rows_poisoned_and_garbage_padding(wide):
+    spec = INV_SPEC_WIDE if wide else INV_SPEC
+    clean = wl.make_problem(spec)
+    dirty = wl.make_problem(spec.with_(poison=True, pad="garbage"))
     for ps in (0, 64, -1):
         say(f"poison ps={ps}")
         _, a = run(clean, ps)
@@ -186,20 +198,21 @@ def test_unread_rows_poisoned_and_garbage_padding():
         assert np.array_equal(a, b)
 
 
-def test_future_tokens_do_not_change_earlier_verify_rows():
-    spec = INV_SPEC.with_(q_len=2, num_q_heads=8, num_kv_heads=4)
+@pytest.mark.parametrize("q_len,n_h", [(2, 8), (5, 32)], ids=["rows4", "rows40"])
+def test_future_tokens_do_not_change_earlier_verify_rows(q_len, n_h):
+    spec = INV_SPEC.with_(q_len=q_len, num_q_heads=n_h, num_kv_heads=4, lens=("uniform", q_len, 900))
     p = wl.make_problem(spec)
     _, base = run(p, 0)
     q = wl.make_problem(spec)
     for b in range(q.num_seqs):
-        t = int(q.context_lens[b]) - 1  # visible to query token 1 only
+        t = int(q.context_lens[b]) - 1  # visible to the last query token only
         q.k_cache[q.block_tables[b, t // 16], t % 16] = np.uint16(0x4100)
         q.v_cache[q.block_tables[b, t // 16], t % 16] = np.uint16(0xC100)
     _, pert = run(q, 0)
-    rows0 = [b * 2 for b in range(p.num_seqs)]
-    rows1 = [b * 2 + 1 for b in range(p.num_seqs)]
-    assert np.array_equal(base[rows0], pert[rows0])
-    assert not np.array_equal(base[rows1], pert[rows1])
+    early = [b * q_len + j for b in range(p.num_seqs) for j in range(q_len - 1)]
+    last = [b * q_len + q_len - 1 for b in range(p.num_seqs)]
+    assert np.array_equal(base[early], pert[early])
+    assert not np.array_equal(base[last], pert[last])
 
 
 def test_values_all_one_give_exactly_one():
@@ -210,15 +223,18 @@ def test_values_all_one_give_exactly_one():
         assert np.all(got == 1.0), ps
 
 
-def test_one_token_context_returns_v_exactly():
-    spec = wl.Spec(name="one", dtype="bf16", num_seqs=5, num_q_heads=8, num_kv_heads=2, head_dim=128,
+@pytest.mark.parametrize("n_h", [8, 16, 64], ids=["rows4", "rows8", "rows32"])
+def test_one_token_context_returns_v_exactly(n_h):
+    spec = wl.Spec(name="one", dtype="bf16", num_seqs=5, num_q_heads=n_h, num_kv_heads=2, head_dim=128,
                    lens=("fixed", (1, 1, 1, 1, 1)), max_len=16, seed=3)
     p = wl.make_problem(spec)
-    _, got = run(p, 0)
-    for b in range(5):
-        for h in range(8):
-            expect = widen(p.v_cache[p.block_tables[b, 0], 0, h // 4], "bf16")
-            assert np.array_equal(got[b, h], expect)
+    G = n_h // 2
+    for ps in (0, -1):
+        _, got = run(p, ps)
+        for b in range(5):
+            for h in range(n_h):
+                expect = widen(p.v_cache[p.block_tables[b, 0], 0, h // G], "bf16")
+                assert np.array_equal(got[b, h], expect), (ps, b, h)
 
 
 @pytest.mark.parametrize("q_len,L", [(1, 300), (5, 77), (1, 20000)])
@@ -244,13 +260,13 @@ def test_identical_keys_count_probe_fp32(q_len, L):
                 np.testing.assert_allclose(got[b * q_len + j, 0], expect, rtol=2e-6, atol=0)
 
 
-@pytest.mark.parametrize("dtype", ["f32", "bf16"])
-@pytest.mark.parametrize("q_len", [1, 2])
-def test_scores_rising_far_past_the_first_block(dtype, q_len):
+@pytest.mark.parametrize("dtype,q_len,n_h", [("f32", 1, 2), ("f32", 2, 2), ("bf16", 1, 2), ("bf16", 2, 2),
+                                             ("bf16", 5, 2), ("bf16", 5, 8)])
+def test_scores_rising_far_past_the_first_block(dtype, q_len, n_h):
     """Scores grow by ~0.1 per position, so weights relative to a wave's first
     block exceed 2^64 and the kernel must take its exact two-pass path."""
     d = 64
-    spec = wl.Spec(name="ramp", dtype=dtype, num_seqs=3, num_q_heads=2, num_kv_heads=1, head_dim=d,
+    spec = wl.Spec(name="ramp", dtype=dtype, num_seqs=3, num_q_heads=n_h, num_kv_heads=1, head_dim=d,
                    lens=("fixed", (1000, 700, 40)), max_len=1024, q_len=q_len, seed=31)
     p = wl.make_problem(spec)
     p.q[:] = 0
@@ -264,7 +280,7 @@ def test_scores_rising_far_past_the_first_block(dtype, q_len):
                 wl.round_to_bf16_bits(np.array([val]))[0] if dtype == "bf16" else val)
     ref = full_reference(p)
     for ps in (0, 512, -1):
-        say(f"ramp {dtype} q_len={q_len} ps={ps}")
+        say(f"ramp {dtype} q_len={q_len} heads={n_h} ps={ps}")
         _, got = run(p, ps)
         assert_parity(got, ref, dtype, f"ramp ps={ps}")
 
@@ -310,8 +326,6 @@ def test_full_size_sampled_rows(name):
     import bench
 
     spec = wl.CONFIGS[name]
-    if spec.group * spec.q_len > 8:
-        pytest.skip("more than 8 query rows per KV head needs the matrix-core kernel, not built yet")
     say(f"{name}: generating")
     p = wl.make_problem(spec)
     ps = bench.partition_for(p)
