@@ -36,19 +36,32 @@ import workloads as wl  # noqa: E402
 HBM_PEAK_GBPS = 8000.0
 DEFAULT_CONFIG = "llama3-8b-decode"
 METRIC = "decode tokens/s and achieved KV HBM GB/s (% of MI355X peak) per pa_decode call"
-KERNEL_SOURCES = ("decode_valu.hip", "pa_device.h")
+KERNEL_SOURCES = ("decode_valu.hip", "decode_mfma.hip", "pa_schedule.h", "pa_kernels.h", "pa_device.h")
+
+# Context split per workload, the fastest measured on MI355X (kernel trace):
+# one pass where every (sequence, KV head) already gives two workgroups per CU,
+# the balanced split where ragged contexts leave CUs idle, and the workload's
+# own partition size where it names one (the FlashDecoding-style split + reduce).
+LAUNCH = {
+    "tiny-f32": 0,
+    "llama3-8b-decode": -1,
+    "llama3-70b-decode": 0,
+    "spec-verify": 0,
+}
 
 
 def partition_for(p: wl.Problem) -> int:
-    """Launch configuration: the context split used for each workload.
-
-    Split into 512-token partitions (32 blocks, one workgroup each) whenever a
-    context is longer than one partition, so that the grid has thousands of
-    workgroups and ragged lengths balance; short-context batches run in one pass.
-    """
+    """Launch configuration: the context split used for each workload."""
     if p.partition_size:
         return p.partition_size
-    return 512 if int(p.context_lens.max()) > 512 else 0
+    return LAUNCH.get(p.spec.name, 0)
+
+
+def decode_kernel_name(p: wl.Problem, partition: int) -> str:
+    rows = p.spec.group * p.q_len
+    kind = "decode_mfma_kernel" if p.dtype == "bf16" and rows >= 8 else "decode_valu_kernel"
+    mode = "balanced" if partition < 0 else ("partitions" if partition > 0 else "one pass")
+    return f"{kind} ({p.dtype}, head_dim {p.head_dim}, {rows} rows per KV head, {mode})"
 
 
 def kernel_source_hash() -> str:
@@ -120,9 +133,10 @@ def load_traffic(workload: str, decode_s: float):
     return per_launch / decode_s / 1e9, per_launch
 
 
-def cpu_baseline(p: wl.Problem, gpu_out, budget_s: float = 12.0):
-    """The oracle, untuned, on the first sequences of the same workload until the
-    time budget is spent; scaled to tokens/s of the whole batch."""
+def cpu_baseline(p: wl.Problem, gpu_out, budget_s: float = 10.0):
+    """The oracle, untuned, on the same workload: the cache write of the batch's
+    new tokens once, then attention sequence by sequence (cycling over the batch)
+    until the time budget is spent; scaled to tokens/s of whole steps."""
     import oracle
     from threadpoolctl import threadpool_info
 
@@ -133,13 +147,16 @@ def cpu_baseline(p: wl.Problem, gpu_out, budget_s: float = 12.0):
     n = 0
     worst = 0.0
     t0 = time.perf_counter()
-    while n < p.num_seqs and time.perf_counter() - t0 < budget_s:
-        rows = [(n, j, h) for j in range(p.q_len) for h in range(p.num_q_heads)]
+    while n < p.num_seqs or time.perf_counter() - t0 < budget_s:
+        b = n % p.num_seqs
+        rows = [(b, j, h) for j in range(p.q_len) for h in range(p.num_q_heads)]
         ref = oracle.paged_decode_rows(p.q, kc, vc, p.block_tables, p.context_lens, p.scale, p.q_len, p.dtype, rows)
-        if gpu_out is not None:
-            got = np.stack([gpu_out[n * p.q_len + j, h] for (_, j, h) in rows])
+        if gpu_out is not None and n < p.num_seqs:
+            got = np.stack([gpu_out[b * p.q_len + j, h] for (_, j, h) in rows])
             worst = max(worst, float(np.max(np.abs(got - ref))))
         n += 1
+        if n >= p.num_seqs and time.perf_counter() - t0 >= budget_s:
+            break
     t_attn = time.perf_counter() - t0
     est = t_write + t_attn * p.num_seqs / n
     threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
@@ -148,9 +165,10 @@ def cpu_baseline(p: wl.Problem, gpu_out, budget_s: float = 12.0):
         "unit": "tokens/s",
         "cores": int(threads),
         "kind": "oracle",
-        "sample": (f"fp64 NumPy oracle: cache write of all {len(p.slot_mapping) if p.slot_mapping is not None else 0} "
-                   f"new tokens ({t_write:.2f} s) plus attention of the first {n} of {p.num_seqs} sequences "
-                   f"x {p.num_q_heads} heads ({t_attn:.2f} s), scaled to the whole batch"),
+        "sample": (f"fp64 NumPy oracle on the same workload: cache write of all "
+                   f"{len(p.slot_mapping) if p.slot_mapping is not None else 0} new tokens ({t_write:.2f} s), then "
+                   f"attention of {n} sequences x {p.num_q_heads} heads x {p.q_len} query tokens, cycling over the "
+                   f"batch of {p.num_seqs} ({t_attn:.2f} s); tokens/s of whole steps"),
         "max_abs_vs_gpu": worst,
     }
 
@@ -163,7 +181,8 @@ def main(argv=None):
     ap.add_argument("--config", default=DEFAULT_CONFIG, choices=list(wl.CONFIGS))
     ap.add_argument("--partition", type=int, default=None, help="override the context split (0 = one pass)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the cpu_baseline leg")
-    ap.add_argument("--cold", type=int, default=20, help="launches timed one by one after a 1 GiB cache flush")
+    ap.add_argument("--cold", type=int, default=0,
+                    help="also time this many decode launches one by one, each after a 1 GiB cache flush")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a 1 GiB device copy (for scaling memory counters)")
     args = ap.parse_args(argv)
@@ -189,26 +208,39 @@ def main(argv=None):
         r.step()
     torch.cuda.synchronize()
 
+    # The timed region: K whole steps, one event pair around each decode launch
+    # (every timing event costs a few microseconds of GPU time, so there are no
+    # others inside the region).
     K = args.steps
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(K)]
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for k in range(K):
-        e = ev[k]
-        e[0].record()
         r.write()
-        e[1].record()
+        ev[k][0].record()
         r.decode()
-        e[2].record()
+        ev[k][1].record()
         r.reduce()
-        e[3].record()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_per_step = (t1 - t0) * 1e3 / K
-    write_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
-    decode_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in ev]))
-    reduce_ms = float(np.mean([e[2].elapsed_time(e[3]) for e in ev]))
-    gpu_ms = float(np.mean([e[0].elapsed_time(e[3]) for e in ev]))
+    decode_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+
+    # breakdown of the other two calls, from a separate untimed pass of whole
+    # steps (event-bracketed, so each figure includes one timing event's cost)
+    nb = min(K, 20)
+    bev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(nb)]
+    for k in range(nb):
+        bev[k][0].record()
+        r.write()
+        bev[k][1].record()
+        r.decode()
+        bev[k][2].record()
+        r.reduce()
+        bev[k][3].record()
+    torch.cuda.synchronize()
+    write_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in bev]))
+    reduce_ms = float(np.mean([e[2].elapsed_time(e[3]) for e in bev])) if partition > 0 else 0.0
 
     # cold-cache decode launches: a 1 GiB write between launches evicts L2 and MALL
     cold_ms = None
@@ -247,7 +279,7 @@ def main(argv=None):
     roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBPS, 4),
             "traffic": round(traffic, 1) if isinstance(traffic, float) else None,
-            "kernel": "decode_valu_kernel<bf16,128,4>" if p.dtype == "bf16" else "decode_valu_kernel",
+            "kernel": decode_kernel_name(p, partition),
             "algorithmic_bytes_per_launch": kv_bytes,
             "avg_launch_us": round(decode_ms * 1e3, 2)}
     if isinstance(traffic_bytes, str):
@@ -277,7 +309,7 @@ def main(argv=None):
         },
         "kv_hbm_gbps_step": round(kv_bytes / (ms_per_step / 1e3) / 1e9, 1),
         "breakdown_us": {"cache_write": round(write_ms * 1e3, 2), "decode": round(decode_ms * 1e3, 2),
-                         "reduce": round(reduce_ms * 1e3, 2), "gpu_step": round(gpu_ms * 1e3, 2),
+                         "reduce": round(reduce_ms * 1e3, 2),
                          "decode_plus_reduce_cold": None if cold_ms is None else round(cold_ms * 1e3, 2)},
         "roofline": roof,
         "outputs_finite": finite,
