@@ -25,7 +25,7 @@ BLOCK_SIZE = 16
 
 
 def to_f64(a: np.ndarray, dtype: str) -> np.ndarray:
-    """Exact widening of stored values to float64."""
+    """Exact widening of stored values to float64 (bf16 is the upper half of an fp32 bit pattern)."""
     if dtype == "f32":
         return np.asarray(a, dtype=np.float32).astype(np.float64)
     if dtype == "bf16":
@@ -35,12 +35,23 @@ def to_f64(a: np.ndarray, dtype: str) -> np.ndarray:
 
 
 def kv_head_of(h: int, group: int) -> int:
-    """Grouped-query attention: consecutive groups of `group` query heads share a KV head."""
+    """Grouped-query attention: consecutive groups of `group` query heads share a KV head.
+
+    The pages say only that n_h / n_kv query heads share one key/value head
+    (learn.mohebi.ai lesson 13, section 3 notation; "07 - Inference",
+    lourdhu02.github.io, section 1); contiguous groups are the reading taken.
+    """
     return h // group
 
 
 def visible_tokens(context_len: int, q_len: int, j: int) -> int:
-    """How many tokens query token j may attend to under the causal mask among the q_len newest."""
+    """How many tokens query token j may attend to under the causal mask among the q_len newest.
+
+    The target scores every draft position in one pass under a causal mask
+    ("LLM serving: continuous batching & PagedAttention", systemcraft.online,
+    section 8, item 1; "07 - Inference", lourdhu02.github.io, section 3).
+    context_len counts the new tokens, which are written before attention.
+    """
     return context_len - q_len + j + 1
 
 
@@ -50,7 +61,9 @@ def gather_sequence(cache: np.ndarray, table_row: np.ndarray, context_len: int,
 
     Logical token t lives in row t % block_size of physical block
     table_row[t // block_size]; table entries past the last used block are
-    never looked at.
+    never looked at.  Logical block i holds tokens 16i .. 16i+15 and the
+    kernel follows the block table one block at a time (learn.mohebi.ai
+    lesson 13, section 3.5).
     """
     nblk = -(-context_len // block_size)
     blocks = [cache[int(table_row[i])] for i in range(nblk)]
@@ -58,14 +71,23 @@ def gather_sequence(cache: np.ndarray, table_row: np.ndarray, context_len: int,
 
 
 def softmax_weights(scores: np.ndarray) -> np.ndarray:
-    """softmax over a 1-D score vector (max subtracted for range, normalized by the sum)."""
+    """softmax over a 1-D score vector (max subtracted for range, normalized by the sum).
+
+    The plain definition that the online softmax reproduces exactly
+    ("07 - Inference", lourdhu02.github.io, section 5.1).
+    """
     m = scores.max()
     w = np.exp(scores - m)
     return w / w.sum()
 
 
 def attend_row(q_vec: np.ndarray, K: np.ndarray, V: np.ndarray, scale: float) -> np.ndarray:
-    """One query row: softmax(scale * K q) weighted sum of V.  K, V are [n, d] float64."""
+    """One query row: softmax(scale * K q) weighted sum of V.  K, V are [n, d] float64.
+
+    Decode attention per query head: q^T K over the cached keys, then the
+    weighted sum of the values (learn.mohebi.ai lesson 13, section 3.3, proof
+    step 4).  The scale is an explicit argument; the pages do not print it.
+    """
     s = scale * (K @ q_vec)
     p = softmax_weights(s)
     return p @ V
@@ -105,7 +127,12 @@ class _SeqCache:
 
 def paged_decode_rows(q, k_cache, v_cache, block_tables, context_lens, scale, q_len, dtype, rows,
                       block_size: int = BLOCK_SIZE) -> np.ndarray:
-    """Attention output for the listed (b, j, h) rows only, [len(rows), d] float64."""
+    """Attention output for the listed (b, j, h) rows only, [len(rows), d] float64.
+
+    Plain attention over the block-table-gathered keys and values: paging only
+    changes where a token is stored (learn.mohebi.ai lesson 13, section 3.5),
+    so each row is attend_row over its visible prefix.
+    """
     S, n_h, n_kv, d, G = _check(q, k_cache, v_cache, block_tables, context_lens, q_len)
     scale64 = float(np.float32(scale))
     seqs = _SeqCache(k_cache, v_cache, block_tables, context_lens, dtype, block_size)
@@ -121,7 +148,7 @@ def paged_decode_rows(q, k_cache, v_cache, block_tables, context_lens, scale, q_
 
 def paged_decode(q, k_cache, v_cache, block_tables, context_lens, scale, q_len, dtype,
                  block_size: int = BLOCK_SIZE) -> np.ndarray:
-    """Full output [num_seqs * q_len, num_q_heads, head_dim] in float64."""
+    """Full output [num_seqs * q_len, num_q_heads, head_dim] in float64 (every row of paged_decode_rows)."""
     S, n_h, n_kv, d, G = _check(q, k_cache, v_cache, block_tables, context_lens, q_len)
     rows = [(b, j, h) for b in range(S) for j in range(q_len) for h in range(n_h)]
     flat = paged_decode_rows(q, k_cache, v_cache, block_tables, context_lens, scale, q_len, dtype, rows,
@@ -135,6 +162,9 @@ def paged_decode(q, k_cache, v_cache, block_tables, context_lens, scale, q_len, 
 
 def partition_partials(q_vec, K, V, scale: float, n_visible: int, context_len: int, partition_size: int):
     """Partials (m, l, acc) of one query row for partitions [p*ps, (p+1)*ps) of [0, context_len).
+
+    FlashDecoding: chunks of the context each give a partial (m, l, acc)
+    ("07 - Inference", lourdhu02.github.io, section 5.3).
 
     m is the partition's largest score, l the sum of exp(score - m), acc the
     exp(score - m)-weighted sum of its value rows.  Tokens past n_visible are
@@ -159,7 +189,9 @@ def partition_partials(q_vec, K, V, scale: float, n_visible: int, context_len: i
 
 def merge_partials(ms: np.ndarray, ls: np.ndarray, accs: np.ndarray) -> np.ndarray:
     """Combine partials with the online-softmax rescaling: every partition is
-    rescaled to the global maximum M by exp(m_p - M), then sum(acc) / sum(l)."""
+    rescaled to the global maximum M by exp(m_p - M), then sum(acc) / sum(l)
+    ("07 - Inference", lourdhu02.github.io, sections 5.1 and 5.3: the merge
+    uses the same rescaling rule and is exact)."""
     live = ls > 0
     M = ms[live].max()
     f = np.where(live, np.exp(np.where(live, ms, M) - M), 0.0)
@@ -168,7 +200,8 @@ def merge_partials(ms: np.ndarray, ls: np.ndarray, accs: np.ndarray) -> np.ndarr
 
 def paged_decode_split(q, k_cache, v_cache, block_tables, context_lens, scale, q_len, dtype,
                        partition_size: int, rows=None, block_size: int = BLOCK_SIZE) -> np.ndarray:
-    """Same result as paged_decode, computed through per-partition partials and the merge."""
+    """Same result as paged_decode, computed through per-partition partials and the merge
+    ("07 - Inference", lourdhu02.github.io, section 5.3)."""
     S, n_h, n_kv, d, G = _check(q, k_cache, v_cache, block_tables, context_lens, q_len)
     scale64 = float(np.float32(scale))
     if rows is None:
@@ -195,7 +228,11 @@ def cache_write(k_cache, v_cache, k, v, slot_mapping, block_size: int = BLOCK_SI
     """Copies of the caches with token t's K/V rows stored at flat slot slot_mapping[t].
 
     A slot is physical_block * block_size + row; a negative slot means the
-    token is not stored.  The rows are copied as raw bits.
+    token is not stored.  The rows are copied as raw bits.  New tokens are
+    appended in place into the sequence's current block ("LLM Inference
+    Serving", systeminternals.dev, the passage on the block manager), and
+    logical block i covers tokens 16i .. 16i+15 (learn.mohebi.ai lesson 13,
+    section 3.5).
     """
     NB = k_cache.shape[0]
     kc = k_cache.copy()
@@ -216,4 +253,5 @@ def cache_write(k_cache, v_cache, k, v, slot_mapping, block_size: int = BLOCK_SI
 
 
 def block_count(context_len: int, block_size: int = BLOCK_SIZE) -> int:
+    """Blocks a context of context_len tokens occupies (learn.mohebi.ai lesson 13, section 3.5)."""
     return int(math.ceil(context_len / block_size))
