@@ -135,8 +135,14 @@ pa_status pa_cache_write(const void* k, const void* v, void* k_cache, void* v_ca
  *                 before it serves a balanced call.  Calls sharing one workspace
  *                 must not overlap in time.
  *
- * Results depend only on the logical contents (bitwise deterministic from run
- * to run, independent of the physical block ids and of the other sequences).
+ * Results are bitwise deterministic from run to run and independent of the
+ * physical block ids.  In the one-pass and split modes a sequence's result
+ * also does not depend on the other sequences of the batch; in PA_BALANCED
+ * mode the cut points follow the whole batch's context lengths, so a
+ * sequence's result may differ in the last bits with the batch around it.
+ * bf16 with 8 or more rows per KV head runs on the matrix cores, which round
+ * the softmax weights to bf16 before the weighted sum of V (the row sums add
+ * the same rounded weights); every other case keeps the weights in fp32.
  */
 pa_status pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache,
                     const int32_t* block_tables, const int32_t* context_lens, float scale, int32_t q_len,
