@@ -45,7 +45,7 @@ KERNEL_SOURCES = ("decode_valu.hip", "decode_mfma.hip", "pa_schedule.h", "pa_ker
 LAUNCH = {
     "tiny-f32": 0,
     "llama3-8b-decode": -1,
-    "llama3-70b-decode": 0,
+    "llama3-70b-decode": -1,
     "spec-verify": 0,
 }
 

@@ -115,15 +115,17 @@ pa_status pa_cache_write(const void* k, const void* v, void* k_cache, void* v_ca
  *                 <= 64 for PA_BF16.
  *   partition_size
  *                 0: one pass, one workgroup per (KV head, sequence); writes out.
- *                 PA_BALANCED (-1): writes out; the (sequence, KV head, block)
- *                 work is cut into equal ranges, one per workgroup, so ragged
- *                 context lengths keep every compute unit equally busy; a
+ *                 PA_BALANCED (-1): writes out; the (sequence, block) work is
+ *                 cut into equal ranges, each taken by one workgroup per KV head,
+ *                 so ragged context lengths keep every compute unit equally busy
+ *                 and the heads of a token row are read together; a
  *                 (sequence, head) cut between ranges is merged inside the call
  *                 with the rescaling rule, in a fixed order.  Needs a workspace
  *                 whose first 4 * num_seqs * num_kv_heads bytes are zero before
  *                 the first such call; every balanced call leaves them zero, so
  *                 one workspace serves any number of calls.  Batches of more than
- *                 4096 sequences fall back to the one-pass mode.
+ *                 4096 sequences, or more than 1024 KV heads, fall back to the
+ *                 one-pass mode.
  *                 Otherwise a positive multiple of block_size: the context is
  *                 split into partitions [p*partition_size, (p+1)*partition_size),
  *                 and for every query row the partition's partial result is

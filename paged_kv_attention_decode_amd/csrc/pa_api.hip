@@ -59,14 +59,18 @@ bool workspace_layout(int32_t S, int32_t q_len, int32_t n_h, int32_t n_kv, int32
   return true;
 }
 
-// workgroups of a balanced launch: two per compute unit (what the decode
-// kernels keep resident), at most the workspace's capacity
-int balanced_workgroups() {
+// workgroups of a balanced launch: about two per compute unit (what the decode
+// kernels keep resident), a whole number of ranges of num_kv_heads workgroups
+// each, at most the workspace's capacity; 0 when even one range does not fit
+int balanced_workgroups(int n_kv) {
   int dev = 0, cus = 0;
   if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) !=
                                                hipSuccess || cus <= 0)
     cus = 256;
-  return 2 * cus < kBalancedMaxWGs ? 2 * cus : kBalancedMaxWGs;
+  int ranges = 2 * cus / n_kv;
+  if (ranges < 1) ranges = 1;
+  if ((long long)ranges * n_kv > kBalancedMaxWGs) ranges = kBalancedMaxWGs / n_kv;
+  return ranges * n_kv;
 }
 
 pa_status from_hip(hipError_t e) { return e == hipSuccess ? PA_OK : PA_ERR_HIP; }
@@ -181,11 +185,11 @@ pa_status pa_decode(void* out, const void* q, const void* k_cache, const void* v
       p.ws_o = reinterpret_cast<float*>(base + w.o_off);
       p.part_blocks = partition_size / kBlock;
       p.num_parts = w.parts;
-    } else if (num_seqs <= pa::kBalancedMaxSeqs) {
+    } else if (num_seqs <= pa::kBalancedMaxSeqs && balanced_workgroups(num_kv_heads) > 0) {
       p.mode = pa::kBalanced;
       p.counters = reinterpret_cast<int*>(base + w.cnt_off);
       p.pieces = reinterpret_cast<float*>(base + w.piece_off);
-      p.num_wgs = balanced_workgroups();
+      p.num_wgs = balanced_workgroups(num_kv_heads);
     }
   }
   hipStream_t s = static_cast<hipStream_t>(stream);

@@ -15,15 +15,18 @@
 //                (m, l, o) of every query row goes to the workspace for pa_reduce
 //                (FlashDecoding's split, "07 - Inference", lourdhu02.github.io,
 //                section 5.3);
-//   balanced     the flattened list of (sequence, KV head, block) work is cut into
-//                equal contiguous ranges, one per workgroup, so every workgroup
-//                (and every CU) streams the same number of blocks whatever the
-//                context lengths.  A (sequence, head) that one range covers whole
-//                is written directly; one cut between ranges leaves a partial
-//                (m, l, o) per piece, and the last workgroup to finish a piece
-//                (an arrival counter per (sequence, head)) merges the pieces in
-//                their fixed order with the same rescaling rule and resets the
-//                counter, so results do not depend on arrival order.
+//   balanced     the flattened list of (sequence, block) work is cut into equal
+//                contiguous ranges; each range goes to num_kv_heads adjacent
+//                workgroups, one per KV head, so every workgroup (and every CU)
+//                streams the same number of blocks whatever the context lengths,
+//                and the heads of one token row are read close together in time
+//                (one DRAM page instead of num_kv_heads scattered visits).  A
+//                (sequence, head) that one range covers whole is written
+//                directly; one cut between ranges leaves a partial (m, l, o) per
+//                piece, and the last workgroup to finish a piece (an arrival
+//                counter per (sequence, head)) merges the pieces in their fixed
+//                order with the same rescaling rule and resets the counter, so
+//                results do not depend on arrival order.
 #pragma once
 
 #include "pa_device.h"
@@ -113,6 +116,74 @@ __device__ __forceinline__ int range_of(long long x, long long T, int W) {
   return (int)(((x + 1) * W + T - 1) / T) - 1;
 }
 
+// How T blocks are cut into W equal contiguous ranges
+// [floor(r T / W), floor((r + 1) T / W)); with W <= T none is empty.
+struct Ranges {
+  long long T;
+  int W;
+  __device__ Ranges(long long T_, int W_) : T(T_), W(W_) {}
+  __device__ long long start(int r) const { return (long long)r * T / W; }
+  __device__ int of(long long x) const { return range_of(x, T, W); }  // the range holding block x
+};
+
+// The last arrival's merge of the npieces partials of (sequence b, head g), in
+// range order: the loads of a batch of pieces are all issued before any is
+// used (each goes past the caches to the point of coherence, so one at a time
+// would cost a full memory round trip per piece).
+template <class Attn, class SlotOf>
+__device__ void merge_pieces(const DecodeParams& a, Attn& at, int b, int g, int first, int npieces,
+                             bool first_at_end, SlotOf slot_of) {
+  constexpr int kBatch = 8;
+  const int rows = a.group * a.q_len;
+  const size_t piece_stride = (size_t)rows * (Attn::kD + 2);
+  for (int idx = threadIdx.x; idx < rows * Attn::kD; idx += Attn::kThreads) {
+    const int r = idx / Attn::kD, c = idx % Attn::kD;
+    const size_t off = (size_t)r * (Attn::kD + 2);
+    float M = kNegInf;
+    for (int k0 = 0; k0 < npieces; k0 += kBatch) {
+      float m[kBatch], l[kBatch];
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) {
+        m[u] = kNegInf;
+        l[u] = 0.0f;
+        if (k0 + u < npieces) {
+          const float* pc = a.pieces + slot_of(first + k0 + u, k0 + u == 0 && first_at_end) * piece_stride + off;
+          m[u] = coherent_load(pc + Attn::kD);
+          l[u] = coherent_load(pc + Attn::kD + 1);
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u)
+        if (l[u] > 0.0f) M = fmaxf(M, m[u]);  // a piece where the row sees nothing carries no weight
+    }
+    float o = 0.0f, lsum = 0.0f;
+    if (M != kNegInf) {
+      for (int k0 = 0; k0 < npieces; k0 += kBatch) {
+        float m[kBatch], l[kBatch], x[kBatch];
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) {
+          m[u] = kNegInf;
+          l[u] = 0.0f;
+          x[u] = 0.0f;
+          if (k0 + u < npieces) {
+            const float* pc = a.pieces + slot_of(first + k0 + u, k0 + u == 0 && first_at_end) * piece_stride + off;
+            m[u] = coherent_load(pc + Attn::kD);
+            l[u] = coherent_load(pc + Attn::kD + 1);
+            x[u] = coherent_load(pc + c);
+          }
+        }
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) {
+          const float f = l[u] > 0.0f ? l[u] * fast_exp2(m[u] - M) : 0.0f;
+          o += f * x[u];
+          lsum += f;
+        }
+      }
+    }
+    at.store(out_row(a, b, g, r) * Attn::kD + c, lsum > 0.0f ? o / lsum : 0.0f);
+  }
+}
+
 template <class Attn>
 __device__ void drive_balanced(const DecodeParams& a, Attn& at) {
   __shared__ int s_prefix[kBalancedMaxSeqs + 1];  // blocks of sequences before b
@@ -154,45 +225,67 @@ __device__ void drive_balanced(const DecodeParams& a, Attn& at) {
     }
   }
 
-  const long long T = (long long)a.n_kv * s_prefix[S];
-  if (T == 0) return;
-  // ranges [floor(w T / Wr), floor((w + 1) T / Wr)); with Wr <= T none is empty,
-  // so the pieces of a cut (sequence, head) come from consecutive workgroups
-  const int Wr = T < W ? (int)T : W;
-  if (wid >= Wr) return;
-  const long long B0 = (long long)wid * T / Wr, B1 = (long long)(wid + 1) * T / Wr;
+  // ranges over the (sequence, block) list, one workgroup per (range, KV head)
+  const int n_kv = a.n_kv;
+  const long long T = s_prefix[S];
+  const int Wh = W / n_kv;  // ranges
+  if (T == 0 || wid >= Wh * n_kv) return;
+  // ranges [floor(r T / Wr), floor((r + 1) T / Wr)); with Wr <= T none is empty,
+  // so the pieces of a cut sequence come from consecutive ranges
+  const int Wr = T < Wh ? (int)T : Wh;
+  const int rid = wid / n_kv, g = wid % n_kv;
+  if (rid >= Wr) return;
+  const Ranges rg(T, Wr);
+  const long long B0 = rg.start(rid), B1 = rg.start(rid + 1);
 
-  // the sequence holding flat block B0: largest b with n_kv * prefix[b] <= B0
-  const int X = (int)(B0 / a.n_kv);
-  int lo = 0, hi = S;  // invariant: prefix[lo] <= X < prefix[hi] (prefix[S] > X since B0 < T)
+  // the sequence holding flat block B0: largest b with prefix[b] <= B0
+  int lo = 0, hi = S;  // invariant: prefix[lo] <= B0 < prefix[hi] (prefix[S] > B0 since B0 < T)
   while (hi - lo > 1) {
     const int mid = (lo + hi) / 2;
-    if (s_prefix[mid] <= X) lo = mid;
+    if (s_prefix[mid] <= B0) lo = mid;
     else hi = mid;
   }
   int b = lo;
-  int nb = s_prefix[b + 1] - s_prefix[b];
-  int g = (int)((B0 - (long long)a.n_kv * s_prefix[b]) / nb);
   const int rows = a.group * a.q_len;
   const size_t piece_stride = (size_t)rows * (Attn::kD + 2);
+  // piece slots: two per workgroup, the one at its range's start and the one at its end
+  auto slot_of = [&](int r, bool at_end) { return (size_t)(2 * (r * n_kv + g) + (at_end ? 1 : 0)); };
+
+  // a piece's arrival: wait until this workgroup's stores are complete, count
+  // it, and let the last of its pieces merge them all
+  auto arrive = [&](int bb, long long seg0, long long seg1) {
+    __builtin_amdgcn_s_waitcnt(0);  // this wave's stores are complete
+    __syncthreads();
+    const int first = rg.of(seg0), last = rg.of(seg1 - 1);
+    const int npieces = last - first + 1;
+    if (tid == 0) {
+      int* cnt = a.counters + (size_t)bb * n_kv + g;
+      const int old = __hip_atomic_fetch_add(cnt, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      const int is_last = old == npieces - 1;
+      if (is_last) __hip_atomic_store(cnt, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      s_last = is_last;
+    }
+    __syncthreads();
+    if (s_last) merge_pieces(a, at, bb, g, first, npieces, seg0 > rg.start(first), slot_of);
+    __syncthreads();
+  };
 
   while (true) {
-    const long long seg0 = (long long)a.n_kv * s_prefix[b] + (long long)g * nb;  // flat index of block 0
-    const long long seg1 = seg0 + nb;
+    const long long seg0 = s_prefix[b], seg1 = s_prefix[b + 1];
+    const int nb = (int)(seg1 - seg0);
     const int blo = (int)((B0 > seg0 ? B0 : seg0) - seg0);
     const int bhi = (int)((B1 < seg1 ? B1 : seg1) - seg0);
     at.run(b, g, clamped_len(a, b), blo, bhi);
     if (blo == 0 && bhi == nb) {
       write_final(a, at, b, g);
     } else {
-      // a piece: store the partial, then the last arrival merges all pieces
-      const int slot = seg0 > B0 ? 2 * wid + 1 : 2 * wid;
-      float* mine = a.pieces + (size_t)slot * piece_stride;
-      // The partial goes out with device-coherent stores (written through to
-      // the point of coherence of all XCDs) and every wave waits for them
-      // before the barrier, so the arrival below is ordered after them without
-      // writing back or invalidating a whole L2 (release/acquire fences at
-      // device scope do that, which costs far more than the kernel's work).
+      // a piece: its partial goes out with device-coherent stores (written
+      // through to the point of coherence of all XCDs) and its arrival is
+      // ordered after them by waiting for the stores, not by a device-scope
+      // release fence, which would write back a whole L2.  Arriving at once
+      // (rather than at the range's end) keeps the round trips in the middle
+      // of the range, where the CU's other workgroup keeps the memory busy.
+      float* mine = a.pieces + slot_of(rid, seg0 > B0) * piece_stride;
       for (int idx = tid; idx < rows * Attn::kD; idx += NT) {
         const int r = idx / Attn::kD, c = idx % Attn::kD;
         float M, l;
@@ -203,53 +296,13 @@ __device__ void drive_balanced(const DecodeParams& a, Attn& at) {
           coherent_store(mine + (size_t)r * (Attn::kD + 2) + Attn::kD + 1, l);
         }
       }
-      __builtin_amdgcn_s_waitcnt(0);  // this wave's stores are complete
-      __syncthreads();
-      const int first = range_of(seg0, T, Wr), last = range_of(seg1 - 1, T, Wr);
-      const int npieces = last - first + 1;
-      if (tid == 0) {
-        int* cnt = a.counters + (size_t)b * a.n_kv + g;
-        const int old = __hip_atomic_fetch_add(cnt, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        const int is_last = old == npieces - 1;
-        if (is_last) __hip_atomic_store(cnt, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        s_last = is_last;
-      }
-      __syncthreads();
-      if (s_last) {
-        // the other pieces, read with device-coherent loads (past any stale cache line)
-        for (int idx = tid; idx < rows * Attn::kD; idx += NT) {
-          const int r = idx / Attn::kD, c = idx % Attn::kD;
-          float M = kNegInf;
-          for (int k = 0; k < npieces; ++k) {
-            const int w2 = first + k;
-            const int sl = (k == 0 && seg0 > (long long)w2 * T / Wr) ? 2 * w2 + 1 : 2 * w2;
-            M = fmaxf(M, coherent_load(a.pieces + (size_t)sl * piece_stride + (size_t)r * (Attn::kD + 2) + Attn::kD));
-          }
-          float o = 0.0f, l = 0.0f;
-          if (M != kNegInf) {
-            for (int k = 0; k < npieces; ++k) {
-              const int w2 = first + k;
-              const int sl = (k == 0 && seg0 > (long long)w2 * T / Wr) ? 2 * w2 + 1 : 2 * w2;
-              const float* pc = a.pieces + (size_t)sl * piece_stride + (size_t)r * (Attn::kD + 2);
-              const float f = coherent_load(pc + Attn::kD + 1) * fast_exp2(coherent_load(pc + Attn::kD) - M);
-              o += f * coherent_load(pc + c);
-              l += f;
-            }
-          }
-          at.store(out_row(a, b, g, r) * Attn::kD + c, l > 0.0f ? o / l : 0.0f);
-        }
-      }
-      __syncthreads();
+      arrive(b, seg0, seg1);
     }
     if (seg1 >= B1) break;
-    // next (sequence, head) with blocks
-    if (++g == a.n_kv) {
-      g = 0;
-      do {
-        ++b;
-      } while (s_prefix[b + 1] == s_prefix[b]);
-      nb = s_prefix[b + 1] - s_prefix[b];
-    }
+    // next sequence with blocks
+    do {
+      ++b;
+    } while (s_prefix[b + 1] == s_prefix[b]);
   }
 }
 
