@@ -67,7 +67,10 @@ int balanced_workgroups(int n_kv) {
   if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) !=
                                                hipSuccess || cus <= 0)
     cus = 256;
-  int ranges = 2 * cus / n_kv;
+#ifndef PA_WGS_PER_CU
+#define PA_WGS_PER_CU 2
+#endif
+  int ranges = PA_WGS_PER_CU * cus / n_kv;
   if (ranges < 1) ranges = 1;
   if ((long long)ranges * n_kv > kBalancedMaxWGs) ranges = kBalancedMaxWGs / n_kv;
   return ranges * n_kv;
