@@ -58,6 +58,10 @@ struct MergeTile {
   float wm[R];     // the merging wave's row max
   float wl[R];     // the merging wave's row sum
   float acc[R][D];
+  // the query rows of the current range (bf16), read as score B operands; each
+  // row is padded by 16 bytes so the 16 rows one read touches fall in different
+  // banks
+  uint16_t q[R][D + 8];
 };
 
 template <int D, int NT, int NW, int NBUF>
@@ -94,21 +98,24 @@ struct MfmaAttender {
   __device__ void run(int b, int g, int L, int lo, int hi) {
     const int rows = a.group * a.q_len;
 
-    // query rows as the B operand of the score MFMA: row 16 t + j, dims 32 ks + 8 grp .. + 7
+    // The query rows go to LDS, not registers (three tiles would hold 48 VGPRs
+    // for the whole range): the score MFMA of tile t, step ks reads its B
+    // operand, row 16 t + j, dims 32 ks + 8 grp .. + 7, from there.
     const uint16_t* __restrict__ qp = static_cast<const uint16_t*>(a.q);
-    uint4 qv[NT][KS];
+    for (int idx = threadIdx.x; idx < R * (D / 8); idx += kThreads) {
+      const int r = idx / (D / 8), c8 = idx % (D / 8);
+      uint4 v = make_uint4(0, 0, 0, 0);
+      if (r < rows)
+        v = *reinterpret_cast<const uint4*>(
+            qp + (((size_t)b * a.q_len + r / a.group) * a.n_h + (size_t)g * a.group + r % a.group) * D + 8 * c8);
+      *reinterpret_cast<uint4*>(&sm.q[r][8 * c8]) = v;
+    }
+    __syncthreads();
     int vis[NT];  // positions row 16 t + j may see
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
       const int r = 16 * t + j;
       vis[t] = r < rows ? L - a.q_len + r / a.group + 1 : 0;
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) qv[t][ks] = make_uint4(0, 0, 0, 0);
-      if (r < rows) {
-        const uint16_t* qrow = qp + (((size_t)b * a.q_len + r / a.group) * a.n_h + (size_t)g * a.group + r % a.group) * D;
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) qv[t][ks] = *reinterpret_cast<const uint4*>(qrow + 32 * ks + 8 * grp);
-      }
     }
 
     float m_ref[NT], m_use[NT], lsum[NT];
@@ -163,13 +170,18 @@ struct MfmaAttender {
     // scores: s[t][v] = row 16 t + j against token 4 grp + v, log2 units, -inf where masked
     auto scores = [&](const uint4(&kb)[KS], int lblk, bool ok, floatx4_t(&s)[NT]) {
       const int pos0 = lblk * kBlockTokens + 4 * grp;
+      // keep the compiler from hoisting the query reads out of the block loop
+      // into registers, which is what the LDS copy avoids
+      asm volatile("" ::: "memory");
 #pragma unroll
       for (int t = 0; t < NT; ++t) {
         floatx4_t x = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks)
+        for (int ks = 0; ks < KS; ++ks) {
+          const uint4 qb = *reinterpret_cast<const uint4*>(&sm.q[16 * t + j][32 * ks + 8 * grp]);
           x = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kb[ks]),
-                                                      __builtin_bit_cast(bf16x8_t, qv[t][ks]), x, 0, 0, 0);
+                                                      __builtin_bit_cast(bf16x8_t, qb), x, 0, 0, 0);
+        }
 #pragma unroll
         for (int v = 0; v < 4; ++v) s[t][v] = (ok && pos0 + v < vis[t]) ? x[v] * scale_log2 : kNegInf;
       }
@@ -367,7 +379,11 @@ struct MfmaAttender {
 };
 
 template <int D, int NT, int NW, int NBUF, bool BALANCED>
-__global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(DecodeParams a) {
+// Up to three row tiles the kernel is asked for two waves per SIMD: without
+// the bound the allocator keeps values hoisted out of a balanced range's loop
+// over sequences and lands at one wave per SIMD, while with it everything fits
+// without spilling (four tiles would spill, so they keep one wave).
+__global__ __launch_bounds__(NW * 64, NT <= 3 ? 2 : 1) void decode_mfma_kernel(DecodeParams a) {
   __shared__ MergeTile<16 * NT, D> sm;
   MfmaAttender<D, NT, NW, NBUF> at(a, sm);
   if constexpr (BALANCED) drive_balanced(a, at);
@@ -376,9 +392,15 @@ __global__ __launch_bounds__(NW * 64) void decode_mfma_kernel(DecodeParams a) {
 
 template <int D, int NT>
 hipError_t launch_tiles(const DecodeParams& p, hipStream_t s) {
-  constexpr int NB = NT >= 3 ? 2 : 3;  // blocks in flight per wave
+  constexpr int NB = NT >= 3 ? 2 : 3;  // blocks in flight per wave, fixed schedules
   if (p.mode == kBalanced) {
-    hipLaunchKernelGGL((decode_mfma_kernel<D, NT, kWaves, NB, true>), dim3(p.num_wgs), dim3(kWaves * 64), 0, s, p);
+    // one block in flight per wave, as in the vector-ALU kernel: cheaper
+    // pipeline restarts at the sequences a range crosses (70B layer: 221 us
+    // against 239 us with three)
+    static const int resident = resident_per_cu(decode_mfma_kernel<D, NT, kWaves, 1, true>, kWaves * 64);
+    DecodeParams q = p;
+    q.num_wgs = balanced_workgroups(resident, p.n_kv);
+    hipLaunchKernelGGL((decode_mfma_kernel<D, NT, kWaves, 1, true>), dim3(q.num_wgs), dim3(kWaves * 64), 0, s, q);
   } else {
     dim3 grid(p.mode == kPartitions ? p.num_parts : 1, p.n_kv, p.num_seqs);
     hipLaunchKernelGGL((decode_mfma_kernel<D, NT, kWaves, NB, false>), grid, dim3(kWaves * 64), 0, s, p);

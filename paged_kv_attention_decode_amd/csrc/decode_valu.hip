@@ -417,8 +417,12 @@ hipError_t launch_one(const DecodeParams& p, hipStream_t s) {
     // memory system (lower loaded latency) makes each restart cheaper; the
     // steady state stays at the same bandwidth (measured on the 8B layer:
     // 122 us against 126 us with three blocks).
-    hipLaunchKernelGGL((decode_valu_kernel<T, D, R, kWaves, kBalancedBlocksInFlight, true>), dim3(p.num_wgs),
-                       dim3(kWaves * 64), 0, s, p);
+    static const int resident =
+        resident_per_cu(decode_valu_kernel<T, D, R, kWaves, kBalancedBlocksInFlight, true>, kWaves * 64);
+    DecodeParams q = p;
+    q.num_wgs = balanced_workgroups(resident, p.n_kv);
+    hipLaunchKernelGGL((decode_valu_kernel<T, D, R, kWaves, kBalancedBlocksInFlight, true>), dim3(q.num_wgs),
+                       dim3(kWaves * 64), 0, s, q);
   } else {
     dim3 grid(p.mode == kPartitions ? p.num_parts : 1, p.n_kv, p.num_seqs);
     hipLaunchKernelGGL((decode_valu_kernel<T, D, R, kWaves, NB, false>), grid, dim3(kWaves * 64), 0, s, p);

@@ -30,7 +30,6 @@ struct WsLayout {
   int parts;
 };
 
-constexpr int kBalancedMaxWGs = 1024;
 
 // partition_size > 0: max_logits[R][P], exp_sums[R][P], partial outputs [R][P][D] (R = rows, P = partitions)
 // partition_size == PA_BALANCED: counters int32[S * n_kv], pieces [2 * kBalancedMaxWGs][rows per KV head][D + 2]
@@ -42,7 +41,7 @@ bool workspace_layout(int32_t S, int32_t q_len, int32_t n_h, int32_t n_kv, int32
     const size_t rows_kv = (size_t)(n_h / n_kv) * q_len;
     w->cnt_off = 0;
     w->piece_off = align_up((size_t)S * n_kv * sizeof(int32_t));
-    w->total = w->piece_off + align_up(2 * (size_t)kBalancedMaxWGs * rows_kv * (D + 2) * sizeof(float));
+    w->total = w->piece_off + align_up(2 * (size_t)pa::kBalancedMaxWGs * rows_kv * (D + 2) * sizeof(float));
     return true;
   }
   if (ps <= 0 || ps % bs != 0) return false;
@@ -57,23 +56,6 @@ bool workspace_layout(int32_t S, int32_t q_len, int32_t n_h, int32_t n_kv, int32
   w->o_off = 2 * stats;
   w->total = 2 * stats + align_up(rows * parts * (size_t)D * sizeof(float));
   return true;
-}
-
-// workgroups of a balanced launch: about two per compute unit (what the decode
-// kernels keep resident), a whole number of ranges of num_kv_heads workgroups
-// each, at most the workspace's capacity; 0 when even one range does not fit
-int balanced_workgroups(int n_kv) {
-  int dev = 0, cus = 0;
-  if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) !=
-                                               hipSuccess || cus <= 0)
-    cus = 256;
-#ifndef PA_WGS_PER_CU
-#define PA_WGS_PER_CU 2
-#endif
-  int ranges = PA_WGS_PER_CU * cus / n_kv;
-  if (ranges < 1) ranges = 1;
-  if ((long long)ranges * n_kv > kBalancedMaxWGs) ranges = kBalancedMaxWGs / n_kv;
-  return ranges * n_kv;
 }
 
 pa_status from_hip(hipError_t e) { return e == hipSuccess ? PA_OK : PA_ERR_HIP; }
@@ -188,11 +170,10 @@ pa_status pa_decode(void* out, const void* q, const void* k_cache, const void* v
       p.ws_o = reinterpret_cast<float*>(base + w.o_off);
       p.part_blocks = partition_size / kBlock;
       p.num_parts = w.parts;
-    } else if (num_seqs <= pa::kBalancedMaxSeqs && balanced_workgroups(num_kv_heads) > 0) {
+    } else if (num_seqs <= pa::kBalancedMaxSeqs && num_kv_heads <= pa::kBalancedMaxWGs) {
       p.mode = pa::kBalanced;
       p.counters = reinterpret_cast<int*>(base + w.cnt_off);
       p.pieces = reinterpret_cast<float*>(base + w.piece_off);
-      p.num_wgs = balanced_workgroups(num_kv_heads);
     }
   }
   hipStream_t s = static_cast<hipStream_t>(stream);

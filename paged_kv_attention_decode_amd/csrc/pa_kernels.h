@@ -18,6 +18,38 @@ enum DecodeMode {
 
 // largest batch the balanced mode handles (its block prefix over the sequences lives in LDS)
 constexpr int kBalancedMaxSeqs = 4096;
+// most workgroups of a balanced launch (the workspace holds two pieces per workgroup)
+constexpr int kBalancedMaxWGs = 1024;
+
+// most workgroups per compute unit in a balanced launch: more ranges than two
+// per CU measured slower (70B layer: 234 us at three per CU against 221 us)
+constexpr int kBalancedMaxPerCU = 2;
+
+// Workgroups of a balanced launch: as many as stay resident together
+// (resident_per_cu per compute unit, the kernel's occupancy, at most
+// kBalancedMaxPerCU), so that no range waits for a second round; a whole
+// number of ranges of n_kv workgroups, at least one, at most kBalancedMaxWGs
+// (n_kv <= kBalancedMaxWGs is checked before).
+inline int balanced_workgroups(int resident_per_cu, int n_kv) {
+  if (resident_per_cu > kBalancedMaxPerCU) resident_per_cu = kBalancedMaxPerCU;
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) !=
+                                               hipSuccess || cus <= 0)
+    cus = 256;
+  if (resident_per_cu < 1) resident_per_cu = 1;
+  int ranges = resident_per_cu * cus / n_kv;
+  if (ranges < 1) ranges = 1;
+  if ((long long)ranges * n_kv > kBalancedMaxWGs) ranges = kBalancedMaxWGs / n_kv;
+  return ranges * n_kv;
+}
+
+// workgroups of `kernel` (threads each) one compute unit keeps resident
+template <class Kernel>
+int resident_per_cu(Kernel kernel, int threads) {
+  int n = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kernel, threads, 0) != hipSuccess || n < 1) n = 1;
+  return n;
+}
 
 struct DecodeParams {
   void* out;             // [S*q_len, n_h, D] (single pass and balanced)
@@ -36,7 +68,7 @@ struct DecodeParams {
   int mode;              // DecodeMode
   int part_blocks;       // partitions: blocks per partition
   int num_parts;         // partitions: partition stride of the workspace
-  int num_wgs;           // balanced: workgroups in the grid
+  int num_wgs;           // balanced: workgroups in the grid (set by the launcher)
   int num_seqs;
 };
 
