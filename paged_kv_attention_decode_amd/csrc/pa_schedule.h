@@ -78,9 +78,42 @@ __device__ void write_zeros(const DecodeParams& a, Attn& at, int b, int g) {
 
 // ---- single pass and partitions: grid (partitions or 1, n_kv, num_seqs)
 
+// largest batch whose one-pass launch runs the longest sequences first
+constexpr int kLongestFirstMaxSeqs = 256;
+
+// The sequence of rank z in descending block count (ties by index).  The
+// hardware hands out workgroups in launch order; when the grid needs more
+// than one round of resident workgroups, starting the longest sequences first
+// keeps a long one from starting last and running alone at the end (longest
+// processing time first).  Every workgroup ranks the whole batch in LDS, which
+// costs O(S^2 / threads) compares, so only batches up to
+// kLongestFirstMaxSeqs are reordered.
+template <int NT>
+__device__ int sequence_of_rank(const DecodeParams& a, int z) {
+  __shared__ int s_blocks[kLongestFirstMaxSeqs];
+  __shared__ int s_pick;
+  const int S = a.num_seqs;
+  for (int i = threadIdx.x; i < S; i += NT) s_blocks[i] = blocks_of(clamped_len(a, i));
+  __syncthreads();
+  for (int c = threadIdx.x; c < S; c += NT) {
+    const int mine = s_blocks[c];
+    int rank = 0;
+    for (int i = 0; i < S; ++i) {
+      const int o = s_blocks[i];
+      rank += (o > mine) | ((o == mine) & (i < c));
+    }
+    if (rank == z) s_pick = c;
+  }
+  __syncthreads();
+  return s_pick;
+}
+
 template <class Attn>
 __device__ void drive_fixed(const DecodeParams& a, Attn& at) {
-  const int part = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  const int part = blockIdx.x, g = blockIdx.y;
+  const int b = a.mode == kSinglePass && a.num_seqs <= kLongestFirstMaxSeqs
+                    ? sequence_of_rank<Attn::kThreads>(a, (int)blockIdx.z)
+                    : (int)blockIdx.z;
   const int L = clamped_len(a, b);
   const int nblk = blocks_of(L);
   if (a.mode == kSinglePass) {
