@@ -26,8 +26,14 @@ What it computes, and which passage each step follows:
   by the online-softmax rescaling rule) is written out as well
   (lourdhu02.github.io "07 - Inference", sections 5.1 and 5.3).
 
+* fp8 KV cache (oracle/fp8.py): keys and values stored as E4M3 codes with a
+  per-head scale, products in higher precision ("LLM serving: KV cache,
+  batching, paged attention and quantization", learn.mohebi.ai, section 3.7;
+  "07 - Inference", lourdhu02.github.io, section 4.3).
+
 Parity of individual output elements is pinned by the tests in
-tests/test_oracle.py (brute-force SDPA, closed forms, invariants).
+tests/test_oracle.py and tests/test_oracle_fp8.py (brute-force SDPA, closed
+forms, torch's float8 type, invariants).
 """
 
 from .attention import (  # noqa: F401
@@ -44,4 +50,13 @@ from .attention import (  # noqa: F401
     softmax_weights,
     to_f64,
     visible_tokens,
+)
+from .fp8 import (  # noqa: F401
+    cache_write_fp8,
+    e4m3_decode,
+    e4m3_encode,
+    e4m3_table,
+    paged_decode_fp8,
+    paged_decode_fp8_rows,
+    quantize,
 )
