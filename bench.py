@@ -47,6 +47,7 @@ LAUNCH = {
     "llama3-8b-decode": -1,
     "llama3-70b-decode": -1,
     "spec-verify": 0,
+    "llama3-8b-decode-fp8kv": -1,
 }
 
 
@@ -59,9 +60,11 @@ def partition_for(p: wl.Problem) -> int:
 
 def decode_kernel_name(p: wl.Problem, partition: int) -> str:
     rows = p.spec.group * p.q_len
-    kind = "decode_mfma_kernel" if p.dtype == "bf16" and rows >= 8 else "decode_valu_kernel"
+    fp8 = p.spec.kv == "fp8"
+    kind = "decode_mfma_kernel" if fp8 or (p.dtype == "bf16" and rows >= 8) else "decode_valu_kernel"
     mode = "balanced" if partition < 0 else ("partitions" if partition > 0 else "one pass")
-    return f"{kind} ({p.dtype}, head_dim {p.head_dim}, {rows} rows per KV head, {mode})"
+    kv = "fp8 E4M3 KV, bf16 q" if fp8 else p.dtype
+    return f"{kind} ({kv}, head_dim {p.head_dim}, {rows} rows per KV head, {mode})"
 
 
 def kernel_source_hash() -> str:
@@ -94,6 +97,10 @@ class Resident:
         self.new_k = to_dev(p.new_k, torch) if p.new_k is not None else None
         self.new_v = to_dev(p.new_v, torch) if p.new_v is not None else None
         self.slots = torch.from_numpy(p.slot_mapping).cuda() if p.slot_mapping is not None else None
+        self.fp8 = p.spec.kv == "fp8"
+        if self.fp8:
+            self.k_scale = torch.from_numpy(p.k_scale).cuda()
+            self.v_scale = torch.from_numpy(p.v_scale).cuda()
         self.out = torch.empty_like(self.q)
         self.ws = None
         if partition:
@@ -101,10 +108,18 @@ class Resident:
 
     def write(self):
         if self.new_k is not None:
-            self.pa.cache_write(self.new_k, self.new_v, self.k_cache, self.v_cache, self.slots)
+            if self.fp8:
+                self.pa.cache_write_fp8(self.new_k, self.new_v, self.k_cache, self.v_cache, self.slots, self.k_scale,
+                                        self.v_scale)
+            else:
+                self.pa.cache_write(self.new_k, self.new_v, self.k_cache, self.v_cache, self.slots)
 
     def decode(self):
         p = self.p
+        if self.fp8:
+            self.pa.decode_fp8(self.q, self.k_cache, self.v_cache, self.k_scale, self.v_scale, self.tables, self.lens,
+                               float(p.scale), p.q_len, self.partition, out=self.out, workspace=self.ws)
+            return
         self.pa.decode(self.q, self.k_cache, self.v_cache, self.tables, self.lens, float(p.scale), p.q_len,
                        self.partition, out=self.out, workspace=self.ws)
 
@@ -141,8 +156,14 @@ def cpu_baseline(p: wl.Problem, gpu_out, budget_s: float = 10.0):
     from threadpoolctl import threadpool_info
 
     t0 = time.perf_counter()
-    kc, vc = (oracle.cache_write(p.k_cache, p.v_cache, p.new_k, p.new_v, p.slot_mapping)
-              if p.new_k is not None else (p.k_cache, p.v_cache))
+    fp8 = p.spec.kv == "fp8"
+    if p.new_k is None:
+        kc, vc = p.k_cache, p.v_cache
+    elif fp8:
+        kc, vc = oracle.cache_write_fp8(p.k_cache, p.v_cache, p.new_k, p.new_v, p.slot_mapping, p.k_scale, p.v_scale,
+                                        p.dtype)
+    else:
+        kc, vc = oracle.cache_write(p.k_cache, p.v_cache, p.new_k, p.new_v, p.slot_mapping)
     t_write = time.perf_counter() - t0
     n = 0
     worst = 0.0
@@ -150,7 +171,12 @@ def cpu_baseline(p: wl.Problem, gpu_out, budget_s: float = 10.0):
     while n < p.num_seqs or time.perf_counter() - t0 < budget_s:
         b = n % p.num_seqs
         rows = [(b, j, h) for j in range(p.q_len) for h in range(p.num_q_heads)]
-        ref = oracle.paged_decode_rows(p.q, kc, vc, p.block_tables, p.context_lens, p.scale, p.q_len, p.dtype, rows)
+        if fp8:
+            ref = oracle.paged_decode_fp8_rows(p.q, kc, vc, p.k_scale, p.v_scale, p.block_tables, p.context_lens,
+                                               p.scale, p.q_len, p.dtype, rows)
+        else:
+            ref = oracle.paged_decode_rows(p.q, kc, vc, p.block_tables, p.context_lens, p.scale, p.q_len, p.dtype,
+                                           rows)
         if gpu_out is not None and n < p.num_seqs:
             got = np.stack([gpu_out[b * p.q_len + j, h] for (_, j, h) in rows])
             worst = max(worst, float(np.max(np.abs(got - ref))))

@@ -7,7 +7,10 @@
  *   pa_decode       attention of the newest q_len tokens of every sequence over
  *                   its paged KV cache: in one pass, work-balanced across the
  *                   GPU, or as per-partition partials (split context);
- *   pa_reduce       merge the partials of a split pa_decode into the output.
+ *   pa_reduce       merge the partials of a split pa_decode into the output;
+ *   pa_cache_write_fp8, pa_decode_fp8
+ *                   the same over a KV cache of fp8 (E4M3) codes with one
+ *                   scale per KV head.
  *
  * Sources of the definitions (the web pages this library implements):
  *   - per layer, K and V are each stored as [num_blocks, block_size,
@@ -26,7 +29,12 @@
  *     mask ("07 - Inference", lourdhu02.github.io, section 3);
  *   - split context: chunks produce partials (m, l, acc) that a second small
  *     kernel merges with the online-softmax rescaling rule (lourdhu02.github.io,
- *     section 5.3 "Decode attention and FlashDecoding").
+ *     section 5.3 "Decode attention and FlashDecoding");
+ *   - an fp8 KV cache stores keys and values in 8 bits while the products run
+ *     in higher precision, halving the KV bytes read per step
+ *     (learn.mohebi.ai, section 3.7, the table of quantization schemes); E4M3,
+ *     largest magnitude 448, is the fp8 format for inference, with per-tensor,
+ *     per-channel or per-block scales (lourdhu02.github.io, section 4.3).
  *
  * Conventions shared by every entry point:
  *   - Every data pointer is a DEVICE pointer owned by the caller.  The library
@@ -183,6 +191,53 @@ pa_status pa_reduce(void* out, const void* workspace, size_t workspace_bytes, co
                     void* stream);
 
 /* A static, human-readable description of a status code. */
+/*
+ * fp8 KV cache.  The caches hold OCP E4M3 codes (one byte per value: sign,
+ * 4 exponent bits with bias 7, 3 mantissa bits; no infinities; 0x7F/0xFF are
+ * NaN; largest finite magnitude 448) in the same [num_blocks, block_size,
+ * num_kv_heads, head_dim] layout.  Each KV head g has an fp32 scale for K and
+ * one for V: code c of head g stands for decode(c) * scale[g].  Per-tensor
+ * scaling is the case of equal scales.
+ *
+ * pa_cache_write_fp8 - quantize the K and V rows of new tokens into their slots.
+ *
+ *   k, v          [num_tokens, num_kv_heads, head_dim] of dtype (PA_F32 or PA_BF16).
+ *   k_cache,      uint8 [num_blocks, block_size, num_kv_heads, head_dim] codes.
+ *   v_cache
+ *   slot_mapping  int64 [num_tokens] as for pa_cache_write (negative = skip;
+ *                 slots outside the pool are skipped).
+ *   k_scale,      fp32 [num_kv_heads] device arrays, positive and finite.
+ *   v_scale
+ *
+ * Each value x of head g becomes the E4M3 code nearest to the fp32 quotient
+ * x / scale[g] (one correctly rounded fp32 division), ties to the even
+ * mantissa, after clamping the quotient to [-448, 448]; a NaN becomes 0x7F.
+ * Deterministic and bit-exact.
+ */
+pa_status pa_cache_write_fp8(const void* k, const void* v, void* k_cache, void* v_cache,
+                             const int64_t* slot_mapping, const float* k_scale, const float* v_scale,
+                             int32_t num_tokens, int32_t num_blocks, int32_t block_size, int32_t num_kv_heads,
+                             int32_t head_dim, pa_dtype dtype, void* stream);
+
+/*
+ * pa_decode_fp8 - pa_decode over an fp8 KV cache.
+ *
+ * Arguments as pa_decode, with k_cache and v_cache holding E4M3 codes and
+ * k_scale, v_scale the per-head fp32 scales; dtype (the type of q and out)
+ * must be PA_BF16; rows per KV head up to 64.  The keys and values are decoded
+ * to bf16 exactly (every E4M3 value is a bf16 value) and multiplied on the
+ * matrix cores with fp32 accumulation; the K scale is folded into the score
+ * scale and the V scale into the final normalization.  The workspace, the
+ * partition sizes, PA_BALANCED and pa_reduce work as for pa_decode (the
+ * partials are in the output's units, so pa_reduce merges them unchanged).
+ */
+pa_status pa_decode_fp8(void* out, const void* q, const void* k_cache, const void* v_cache, const float* k_scale,
+                        const float* v_scale, const int32_t* block_tables, const int32_t* context_lens, float scale,
+                        int32_t q_len, int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                        int32_t head_dim, int32_t num_blocks, int32_t block_size, int32_t max_blocks_per_seq,
+                        int32_t partition_size, void* workspace, size_t workspace_bytes, pa_dtype dtype,
+                        void* stream);
+
 const char* pa_status_string(pa_status status);
 
 /* Library version as major * 10000 + minor * 100 + patch. */

@@ -11,6 +11,7 @@ on the GPU, the call raises.
     reduce(out, workspace, context_lens, ...)
     decode_workspace_size(...), new_workspace(...)
     paged_attention(...)   # decode, plus reduce when the context is split
+    cache_write_fp8(...), decode_fp8(...)   # the same over an fp8 (E4M3) cache with per-head scales
 """
 
 from __future__ import annotations
@@ -21,13 +22,15 @@ from typing import Optional
 
 __all__ = [
     "PA_F32", "PA_BF16", "PA_BALANCED", "PagedAttentionError", "library_path", "load_library", "status_string", "version",
-    "cache_write", "decode", "reduce", "decode_workspace_size", "paged_attention", "SYMBOLS",
+    "cache_write", "decode", "reduce", "decode_workspace_size", "paged_attention", "cache_write_fp8", "decode_fp8",
+    "SYMBOLS",
 ]
 
 PA_F32, PA_BF16 = 0, 1
 PA_BALANCED = -1  # partition_size selecting the work-balanced decode
 BLOCK_SIZE = 16
-SYMBOLS = ("pa_cache_write", "pa_decode", "pa_decode_workspace_size", "pa_reduce", "pa_status_string", "pa_version")
+SYMBOLS = ("pa_cache_write", "pa_decode", "pa_decode_workspace_size", "pa_reduce", "pa_status_string", "pa_version",
+           "pa_cache_write_fp8", "pa_decode_fp8")
 _STATUS = {0: "PA_OK", 1: "PA_ERR_NULL", 2: "PA_ERR_SHAPE", 3: "PA_ERR_UNSUPPORTED", 4: "PA_ERR_WORKSPACE",
            5: "PA_ERR_HIP"}
 
@@ -64,6 +67,11 @@ def load_library():
     lib.pa_decode_workspace_size.argtypes = [i32] * 8
     lib.pa_reduce.restype = ctypes.c_int
     lib.pa_reduce.argtypes = [vp, vp, sz, vp, i32, i32, i32, i32, i32, i32, i32, ctypes.c_int, vp]
+    lib.pa_cache_write_fp8.restype = ctypes.c_int
+    lib.pa_cache_write_fp8.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, ctypes.c_int, vp]
+    lib.pa_decode_fp8.restype = ctypes.c_int
+    lib.pa_decode_fp8.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, f32, i32, i32, i32, i32, i32, i32, i32, i32, i32,
+                                  vp, sz, ctypes.c_int, vp]
     lib.pa_status_string.restype = ctypes.c_char_p
     lib.pa_status_string.argtypes = [ctypes.c_int]
     lib.pa_version.restype = i32
@@ -235,3 +243,68 @@ def paged_attention(q, k_cache, v_cache, block_tables, context_lens, scale: floa
     if out is None:
         out = torch.empty_like(q)
     return reduce(out, ws, context_lens, q_len, block_tables.shape[1], partition_size, stream)
+
+
+# ---------------------------------------------------------------------------
+# fp8 (E4M3) KV cache
+
+
+def _scales(k_scale, v_scale, n_kv):
+    torch = _torch()
+    pk = _dev(k_scale, "k_scale", torch.float32, 1)
+    pv = _dev(v_scale, "v_scale", torch.float32, 1)
+    if k_scale.shape[0] != n_kv or v_scale.shape[0] != n_kv:
+        raise ValueError(f"k_scale and v_scale must hold one fp32 scale per KV head ({n_kv})")
+    return pk, pv
+
+
+def cache_write_fp8(k, v, k_cache, v_cache, slot_mapping, k_scale, v_scale, stream=None) -> None:
+    """pa_cache_write_fp8: quantize token t's K/V rows (fp32 or bf16) into the uint8
+    E4M3 caches at flat slot slot_mapping[t] with the per-head scales."""
+    torch = _torch()
+    pk = _dev(k, "k", ndim=3)
+    pv = _dev(v, "v", k.dtype, 3)
+    pkc = _dev(k_cache, "k_cache", torch.uint8, 4)
+    pvc = _dev(v_cache, "v_cache", torch.uint8, 4)
+    ps = _dev(slot_mapping, "slot_mapping", torch.int64, 1)
+    T, n_kv, d = k.shape
+    if v.shape != k.shape or k_cache.shape != v_cache.shape or tuple(k_cache.shape[2:]) != (n_kv, d):
+        raise ValueError("k/v must be [T, n_kv, d] and the caches [num_blocks, block_size, n_kv, d]")
+    if slot_mapping.shape[0] != T:
+        raise ValueError("slot_mapping must hold one slot per token")
+    sk, sv = _scales(k_scale, v_scale, n_kv)
+    st = load_library().pa_cache_write_fp8(pk, pv, pkc, pvc, ps, sk, sv, T, k_cache.shape[0], k_cache.shape[1],
+                                           n_kv, d, _dtype_code(k), _stream(stream))
+    _check(st, "pa_cache_write_fp8")
+
+
+def decode_fp8(q, k_cache, v_cache, k_scale, v_scale, block_tables, context_lens, scale: float, q_len: int = 1,
+               partition_size: int = 0, out=None, workspace=None, stream=None):
+    """pa_decode_fp8: decode over uint8 E4M3 caches with per-head scales; q/out bf16.
+    Same partition_size / workspace / return conventions as decode()."""
+    torch = _torch()
+    S = _decode_shapes(q, k_cache, block_tables, context_lens, q_len)
+    n_h, d = q.shape[1], q.shape[2]
+    NB, bs, n_kv = k_cache.shape[0], k_cache.shape[1], k_cache.shape[2]
+    MB = block_tables.shape[1]
+    if v_cache.shape != k_cache.shape:
+        raise ValueError("k_cache and v_cache must have the same shape")
+    args = (_dev(q, "q", torch.bfloat16, 3), _dev(k_cache, "k_cache", torch.uint8, 4),
+            _dev(v_cache, "v_cache", torch.uint8, 4), *_scales(k_scale, v_scale, n_kv),
+            _dev(block_tables, "block_tables", torch.int32, 2), _dev(context_lens, "context_lens", torch.int32, 1))
+    pws, nws = None, 0
+    if partition_size != 0:
+        if workspace is None:
+            workspace = new_workspace(q, k_cache, block_tables, q_len, partition_size)
+        pws, nws = _dev(workspace, "workspace", torch.uint8, 1), workspace.numel()
+    pout = None
+    if partition_size <= 0:
+        if out is None:
+            out = torch.empty_like(q)
+        if out.shape != q.shape:
+            raise ValueError("out must have q's shape")
+        pout = _dev(out, "out", q.dtype, 3)
+    st = load_library().pa_decode_fp8(pout, *args, float(scale), q_len, S, n_h, n_kv, d, NB, bs, MB, partition_size,
+                                      pws, nws, PA_BF16, _stream(stream))
+    _check(st, "pa_decode_fp8")
+    return out if partition_size <= 0 else workspace

@@ -64,18 +64,42 @@ struct MergeTile {
   uint16_t q[R][D + 8];
 };
 
-template <int D, int NT, int NW, int NBUF>
+// fp8 (E4M3) code pair (bytes 0-1, or 2-3 when HIGH) -> bf16 pair, exact:
+// every E4M3 value is a bf16 value
+template <bool HIGH>
+__device__ __forceinline__ uint32_t fp8x2_to_bf16x2(uint32_t codes) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(codes, 1.0f, HIGH));
+}
+
+// KV8: the caches hold fp8 codes with per-head scales (pa_decode_fp8).  The
+// data path differs only in the loads and their conversion to bf16 operands:
+//   K   one 16-byte load per pair of k-steps: lane (j, grp) holds dims
+//       64 kp + 16 grp .. + 15 of token j, so k-step 2 kp + par uses dims
+//       64 kp + 16 grp + 8 par .. + 7 (the query B operand is read from LDS
+//       with the same dims; a dot product does not care about the order);
+//   V   D / 16 bytes per token: lane j holds columns (D / 16) j .. + D/16 - 1 of
+//       tokens 4 grp .. + 3; a byte-level v_perm_b32 gathers column
+//       (D / 16) j + 4 h + e of tokens (0, 1) and (2, 3), converted to the bf16
+//       pairs of the P V B operand.
+// The K scale of the head multiplies the score scale and the V scale the
+// normalized output, exact refactorings of scale * q . (s_k k) and sum p (s_v v).
+template <int D, int NT, int NW, int NBUF, bool KV8>
 struct MfmaAttender {
   static constexpr int kThreads = NW * 64;
   static constexpr int kD = D;
   static constexpr int R = 16 * NT;  // rows, padded to whole tiles
   static constexpr int KS = D / 32;  // score k-steps
   static constexpr int VH = D / 64;  // value column halves
+  static constexpr int KL = KV8 ? KS / 2 : KS;  // K loads (16 bytes) per block
   static_assert(D == 64 || D == 128, "head_dim 64 or 128");
 
   const DecodeParams& a;
   MergeTile<R, D>& sm;
   const int lane, w, j, grp;
+  float out_scale = 1.0f;  // V scale of the current head (fp8 caches)
+
+  // value column of MFMA column j of the P V call (h, e)
+  __device__ static constexpr int col_of(int jj, int h, int e) { return KV8 ? (D / 16) * jj + 4 * h + e : 4 * jj + 64 * h + e; }
 
   __device__ MfmaAttender(const DecodeParams& a_, MergeTile<R, D>& sm_)
       : a(a_),
@@ -92,7 +116,7 @@ struct MfmaAttender {
   __device__ float result(int r, int c, float& M, float& l) const {
     M = sm.m[r];
     l = sm.l[r];
-    return l > 0.0f ? sm.acc[r][c] / l : 0.0f;
+    return l > 0.0f ? sm.acc[r][c] * out_scale / l : 0.0f;
   }
 
   __device__ void run(int b, int g, int L, int lo, int hi) {
@@ -131,21 +155,24 @@ struct MfmaAttender {
         for (int e = 0; e < 4; ++e) acc[t][h][e] = (floatx4_t){0.0f, 0.0f, 0.0f, 0.0f};
     }
 
-    const uint32_t tok_bytes = (uint32_t)a.n_kv * D * 2;
+    constexpr int esz = KV8 ? 1 : 2;
+    const uint32_t tok_bytes = (uint32_t)a.n_kv * D * esz;
     const uint32_t blk_bytes = tok_bytes * kBlockTokens;
-    const uint32_t head_off = (uint32_t)g * D * 2;
+    const uint32_t head_off = (uint32_t)g * D * esz;
     const uint32_t k_off = (uint32_t)j * tok_bytes + head_off + (uint32_t)grp * 16;
-    const uint32_t v_off = (uint32_t)(4 * grp) * tok_bytes + head_off + (uint32_t)j * 8;
+    const uint32_t v_off = (uint32_t)(4 * grp) * tok_bytes + head_off + (uint32_t)j * (KV8 ? D / 16 : 8);
     const char* kbase = static_cast<const char*>(a.k_cache);
     const char* vbase = static_cast<const char*>(a.v_cache);
     const int32_t* __restrict__ table = a.tables + (size_t)b * a.max_blocks;
-    const float scale_log2 = a.scale_log2;
+    const float scale_log2 = KV8 ? a.scale_log2 * a.k_scale[g] : a.scale_log2;
+    if constexpr (KV8) out_scale = a.v_scale[g];
     const int n_mine = hi - lo > w ? (hi - lo - w + NW - 1) / NW : 0;
 
     auto block_ids = [&](int k0, int cnt) { return lane < cnt ? table[lo + w + NW * (k0 + lane)] : 0; };
 
-    // K: KS loads of 16 bytes; V: 4 tokens x VH halves of 8 bytes
-    auto issue = [&](int ids, int cnt, int k0, int kk, uint4(&kb)[KS], uint2(&vb)[4][VH], int& lblk, bool& ok) {
+    // K: KL loads of 16 bytes; V: 4 tokens x VH halves of 8 bytes (bf16), or
+    // 4 tokens x D/16 bytes (fp8, in vb[v][0])
+    auto issue = [&](int ids, int cnt, int k0, int kk, uint4(&kb)[KL], uint2(&vb)[4][VH], int& lblk, bool& ok) {
       const int phys = __builtin_amdgcn_readlane(ids, kk < cnt ? kk : 0);
       ok = kk < cnt && (unsigned)phys < (unsigned)a.num_blocks;
       lblk = lo + w + NW * (k0 + kk);
@@ -157,18 +184,40 @@ struct MfmaAttender {
       const __amdgpu_buffer_rsrc_t vr =
           __builtin_amdgcn_make_buffer_rsrc((void*)(vbase + boff), (short)0, (int)nrec, kBufferWord3);
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks)
-        kb[ks] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(kr, k_off + 64 * ks, 0, 0));
+      for (int kl = 0; kl < KL; ++kl)
+        kb[kl] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(kr, k_off + 64 * kl, 0, 0));
+      if constexpr (KV8) {
 #pragma unroll
-      for (int v = 0; v < 4; ++v)
+        for (int v = 0; v < 4; ++v) {
+          if constexpr (D == 128)
+            vb[v][0] = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(vr, v_off, v * tok_bytes, 0));
+          else
+            vb[v][0] = make_uint2(__builtin_amdgcn_raw_buffer_load_b32(vr, v_off, v * tok_bytes, 0), 0u);
+        }
+      } else {
 #pragma unroll
-        for (int h = 0; h < VH; ++h)
-          vb[v][h] = __builtin_bit_cast(
-              uint2, __builtin_amdgcn_raw_buffer_load_b64(vr, v_off + 128 * h, v * tok_bytes, 0));
+        for (int v = 0; v < 4; ++v)
+#pragma unroll
+          for (int h = 0; h < VH; ++h)
+            vb[v][h] = __builtin_bit_cast(
+                uint2, __builtin_amdgcn_raw_buffer_load_b64(vr, v_off + 128 * h, v * tok_bytes, 0));
+      }
+    };
+
+    // A operand of score k-step ks: 8 dims of K as bf16
+    auto k_operand = [&](const uint4(&kb)[KL], int ks) -> uint4 {
+      if constexpr (KV8) {
+        const uint4 c = kb[ks / 2];
+        const uint32_t lo = (ks & 1) ? c.z : c.x, hi = (ks & 1) ? c.w : c.y;
+        return make_uint4(fp8x2_to_bf16x2<false>(lo), fp8x2_to_bf16x2<true>(lo), fp8x2_to_bf16x2<false>(hi),
+                          fp8x2_to_bf16x2<true>(hi));
+      } else {
+        return kb[ks];
+      }
     };
 
     // scores: s[t][v] = row 16 t + j against token 4 grp + v, log2 units, -inf where masked
-    auto scores = [&](const uint4(&kb)[KS], int lblk, bool ok, floatx4_t(&s)[NT]) {
+    auto scores = [&](const uint4(&kb)[KL], int lblk, bool ok, floatx4_t(&s)[NT]) {
       const int pos0 = lblk * kBlockTokens + 4 * grp;
       // keep the compiler from hoisting the query reads out of the block loop
       // into registers, which is what the LDS copy avoids
@@ -178,8 +227,9 @@ struct MfmaAttender {
         floatx4_t x = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
-          const uint4 qb = *reinterpret_cast<const uint4*>(&sm.q[16 * t + j][32 * ks + 8 * grp]);
-          x = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kb[ks]),
+          const int qd = KV8 ? 64 * (ks / 2) + 16 * grp + 8 * (ks & 1) : 32 * ks + 8 * grp;
+          const uint4 qb = *reinterpret_cast<const uint4*>(&sm.q[16 * t + j][qd]);
+          x = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, k_operand(kb, ks)),
                                                       __builtin_bit_cast(bf16x8_t, qb), x, 0, 0, 0);
         }
 #pragma unroll
@@ -194,10 +244,19 @@ struct MfmaAttender {
       for (int h = 0; h < VH; ++h) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
-          const uint32_t w01 = (e < 2) ? 0 : 1;
-          vt[h][e].x = __builtin_amdgcn_perm(w01 ? vb[1][h].y : vb[1][h].x, w01 ? vb[0][h].y : vb[0][h].x, sel);
-          vt[h][e].y = __builtin_amdgcn_perm(w01 ? vb[3][h].y : vb[3][h].x, w01 ? vb[2][h].y : vb[2][h].x, sel);
+          if constexpr (KV8) {
+            // byte e of dword h of tokens (0, 1) and (2, 3), then fp8 -> bf16
+            const uint32_t sel = 0x0C0C0000u | ((uint32_t)(4 + e) << 8) | (uint32_t)e;
+            const uint32_t d0 = h ? vb[0][0].y : vb[0][0].x, d1 = h ? vb[1][0].y : vb[1][0].x;
+            const uint32_t d2 = h ? vb[2][0].y : vb[2][0].x, d3 = h ? vb[3][0].y : vb[3][0].x;
+            vt[h][e].x = fp8x2_to_bf16x2<false>(__builtin_amdgcn_perm(d1, d0, sel));
+            vt[h][e].y = fp8x2_to_bf16x2<false>(__builtin_amdgcn_perm(d3, d2, sel));
+          } else {
+            const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
+            const uint32_t w01 = (e < 2) ? 0 : 1;
+            vt[h][e].x = __builtin_amdgcn_perm(w01 ? vb[1][h].y : vb[1][h].x, w01 ? vb[0][h].y : vb[0][h].x, sel);
+            vt[h][e].y = __builtin_amdgcn_perm(w01 ? vb[3][h].y : vb[3][h].x, w01 ? vb[2][h].y : vb[2][h].x, sel);
+          }
         }
       }
 #pragma unroll
@@ -235,7 +294,7 @@ struct MfmaAttender {
     for (int k0 = 0; k0 < n_mine; k0 += 64) {
       const int cnt = min(64, n_mine - k0);
       const int ids = block_ids(k0, cnt);
-      uint4 kb[NBUF][KS];
+      uint4 kb[NBUF][KL];
       uint2 vb[NBUF][4][VH];
       int lb[NBUF];
       bool okb[NBUF];
@@ -281,7 +340,7 @@ struct MfmaAttender {
         const int cnt = min(64, n_mine - k0);
         const int ids = block_ids(k0, cnt);
         for (int kk = 0; kk < cnt; ++kk) {
-          uint4 kb1[KS];
+          uint4 kb1[KL];
           uint2 vb1[4][VH];
           int lb1;
           bool ok1;
@@ -299,7 +358,7 @@ struct MfmaAttender {
         const int cnt = min(64, n_mine - k0);
         const int ids = block_ids(k0, cnt);
         for (int kk = 0; kk < cnt; ++kk) {
-          uint4 kb1[KS];
+          uint4 kb1[KL];
           uint2 vb1[4][VH];
           int lb1;
           bool ok1;
@@ -349,7 +408,7 @@ struct MfmaAttender {
             for (int h = 0; h < VH; ++h)
 #pragma unroll
               for (int e = 0; e < 4; ++e) {
-                float& dst = sm.acc[r][4 * j + 64 * h + e];
+                float& dst = sm.acc[r][col_of(j, h, e)];
                 dst = (u > 0 ? dst * f_old : 0.0f) + acc[t][h][e][v] * f_new;
               }
           }
@@ -378,48 +437,53 @@ struct MfmaAttender {
   }
 };
 
-template <int D, int NT, int NW, int NBUF, bool BALANCED>
+template <int D, int NT, int NW, int NBUF, bool BALANCED, bool KV8>
 // Up to three row tiles the kernel is asked for two waves per SIMD: without
 // the bound the allocator keeps values hoisted out of a balanced range's loop
 // over sequences and lands at one wave per SIMD, while with it everything fits
 // without spilling (four tiles would spill, so they keep one wave).
 __global__ __launch_bounds__(NW * 64, NT <= 3 ? 2 : 1) void decode_mfma_kernel(DecodeParams a) {
   __shared__ MergeTile<16 * NT, D> sm;
-  MfmaAttender<D, NT, NW, NBUF> at(a, sm);
+  MfmaAttender<D, NT, NW, NBUF, KV8> at(a, sm);
   if constexpr (BALANCED) drive_balanced(a, at);
   else drive_fixed(a, at);
 }
 
-template <int D, int NT>
+template <int D, int NT, bool KV8>
 hipError_t launch_tiles(const DecodeParams& p, hipStream_t s) {
   constexpr int NB = NT >= 3 ? 2 : 3;  // blocks in flight per wave, fixed schedules
   if (p.mode == kBalanced) {
     // one block in flight per wave, as in the vector-ALU kernel: cheaper
     // pipeline restarts at the sequences a range crosses (70B layer: 221 us
     // against 239 us with three)
-    static const int resident = resident_per_cu(decode_mfma_kernel<D, NT, kWaves, 1, true>, kWaves * 64);
+    static const int resident = resident_per_cu(decode_mfma_kernel<D, NT, kWaves, 1, true, KV8>, kWaves * 64);
     DecodeParams q = p;
     q.num_wgs = balanced_workgroups(resident, p.n_kv);
-    hipLaunchKernelGGL((decode_mfma_kernel<D, NT, kWaves, 1, true>), dim3(q.num_wgs), dim3(kWaves * 64), 0, s, q);
+    hipLaunchKernelGGL((decode_mfma_kernel<D, NT, kWaves, 1, true, KV8>), dim3(q.num_wgs), dim3(kWaves * 64), 0, s,
+                       q);
   } else {
     dim3 grid(p.mode == kPartitions ? p.num_parts : 1, p.n_kv, p.num_seqs);
-    hipLaunchKernelGGL((decode_mfma_kernel<D, NT, kWaves, NB, false>), grid, dim3(kWaves * 64), 0, s, p);
+    hipLaunchKernelGGL((decode_mfma_kernel<D, NT, kWaves, NB, false, KV8>), grid, dim3(kWaves * 64), 0, s, p);
   }
   return hipGetLastError();
 }
 
-template <int D>
+template <int D, bool KV8>
 hipError_t launch_rows(const DecodeParams& p, int rows, hipStream_t s) {
-  if (rows <= 16) return launch_tiles<D, 1>(p, s);
-  if (rows <= 32) return launch_tiles<D, 2>(p, s);
-  if (rows <= 48) return launch_tiles<D, 3>(p, s);
-  return launch_tiles<D, 4>(p, s);
+  if (rows <= 16) return launch_tiles<D, 1, KV8>(p, s);
+  if (rows <= 32) return launch_tiles<D, 2, KV8>(p, s);
+  if (rows <= 48) return launch_tiles<D, 3, KV8>(p, s);
+  return launch_tiles<D, 4, KV8>(p, s);
 }
 
 }  // namespace
 
 hipError_t launch_decode_mfma(const DecodeParams& p, int head_dim, int rows_per_kv, hipStream_t s) {
-  return head_dim == 64 ? launch_rows<64>(p, rows_per_kv, s) : launch_rows<128>(p, rows_per_kv, s);
+  return head_dim == 64 ? launch_rows<64, false>(p, rows_per_kv, s) : launch_rows<128, false>(p, rows_per_kv, s);
+}
+
+hipError_t launch_decode_mfma_fp8(const DecodeParams& p, int head_dim, int rows_per_kv, hipStream_t s) {
+  return head_dim == 64 ? launch_rows<64, true>(p, rows_per_kv, s) : launch_rows<128, true>(p, rows_per_kv, s);
 }
 
 }  // namespace pa

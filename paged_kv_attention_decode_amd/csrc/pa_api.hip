@@ -105,6 +105,34 @@ pa_status pa_cache_write(const void* k, const void* v, void* k_cache, void* v_ca
   return from_hip(pa::launch_cache_write(p, static_cast<hipStream_t>(stream)));
 }
 
+pa_status pa_cache_write_fp8(const void* k, const void* v, void* k_cache, void* v_cache,
+                             const int64_t* slot_mapping, const float* k_scale, const float* v_scale,
+                             int32_t num_tokens, int32_t num_blocks, int32_t block_size, int32_t num_kv_heads,
+                             int32_t head_dim, pa_dtype dtype, void* stream) {
+  if (num_tokens < 0 || num_blocks <= 0 || num_kv_heads <= 0) return PA_ERR_SHAPE;
+  if (dtype != PA_F32 && dtype != PA_BF16) return PA_ERR_UNSUPPORTED;
+  if (block_size != kBlock || (head_dim != 64 && head_dim != 128)) return PA_ERR_UNSUPPORTED;
+  if (num_tokens == 0) return PA_OK;
+  if (!k || !v || !k_cache || !v_cache || !slot_mapping || !k_scale || !v_scale) return PA_ERR_NULL;
+  if (!aligned16(k) || !aligned16(v) || !aligned16(k_cache) || !aligned16(v_cache)) return PA_ERR_SHAPE;
+  const size_t row_codes = (size_t)num_kv_heads * head_dim;
+  if (row_codes / 16 > 0x7fffffff || 2 * (row_codes / 16) * (size_t)num_tokens / 256 > 0x7fffffff) return PA_ERR_SHAPE;
+  pa::CacheWriteFp8Params p;
+  p.k = k;
+  p.v = v;
+  p.k_cache = static_cast<uint8_t*>(k_cache);
+  p.v_cache = static_cast<uint8_t*>(v_cache);
+  p.slots = slot_mapping;
+  p.k_scale = k_scale;
+  p.v_scale = v_scale;
+  p.num_tokens = num_tokens;
+  p.num_blocks = num_blocks;
+  p.head_dim = head_dim;
+  p.row_chunks = (int)(row_codes / 16);
+  p.in_f32 = dtype == PA_F32;
+  return from_hip(pa::launch_cache_write_fp8(p, static_cast<hipStream_t>(stream)));
+}
+
 size_t pa_decode_workspace_size(int32_t num_seqs, int32_t q_len, int32_t num_q_heads, int32_t num_kv_heads,
                                 int32_t head_dim, int32_t max_blocks_per_seq, int32_t block_size,
                                 int32_t partition_size) {
@@ -115,12 +143,17 @@ size_t pa_decode_workspace_size(int32_t num_seqs, int32_t q_len, int32_t num_q_h
   return w.total;
 }
 
-pa_status pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache,
-                    const int32_t* block_tables, const int32_t* context_lens, float scale, int32_t q_len,
-                    int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
-                    int32_t num_blocks, int32_t block_size, int32_t max_blocks_per_seq, int32_t partition_size,
-                    void* workspace, size_t workspace_bytes, pa_dtype dtype, void* stream) {
+namespace {
+
+// pa_decode and pa_decode_fp8: validation, workspace, schedule and launch
+pa_status decode_impl(void* out, const void* q, const void* k_cache, const void* v_cache, const float* k_scale,
+                      const float* v_scale, bool fp8, const int32_t* block_tables, const int32_t* context_lens,
+                      float scale, int32_t q_len, int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                      int32_t head_dim, int32_t num_blocks, int32_t block_size, int32_t max_blocks_per_seq,
+                      int32_t partition_size, void* workspace, size_t workspace_bytes, pa_dtype dtype,
+                      void* stream) {
   if (dtype != PA_F32 && dtype != PA_BF16) return PA_ERR_UNSUPPORTED;
+  if (fp8 && dtype != PA_BF16) return PA_ERR_UNSUPPORTED;
   if (block_size != kBlock || (head_dim != 64 && head_dim != 128)) return PA_ERR_UNSUPPORTED;
   if (num_seqs < 0 || q_len < 1 || q_len > 8 || num_q_heads <= 0 || num_kv_heads <= 0 ||
       num_q_heads % num_kv_heads != 0 || num_blocks <= 0 || max_blocks_per_seq <= 0 ||
@@ -134,6 +167,7 @@ pa_status pa_decode(void* out, const void* q, const void* k_cache, const void* v
   const bool split = partition_size > 0;
   const bool balanced = partition_size == PA_BALANCED;
   if (!q || !k_cache || !v_cache || !block_tables || !context_lens || (!split && !out)) return PA_ERR_NULL;
+  if (fp8 && (!k_scale || !v_scale)) return PA_ERR_NULL;
   if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || (out && !aligned16(out))) return PA_ERR_SHAPE;
 
   pa::DecodeParams p = {};
@@ -141,6 +175,8 @@ pa_status pa_decode(void* out, const void* q, const void* k_cache, const void* v
   p.q = q;
   p.k_cache = k_cache;
   p.v_cache = v_cache;
+  p.k_scale = k_scale;
+  p.v_scale = v_scale;
   p.tables = block_tables;
   p.lens = context_lens;
   p.scale_log2 = (float)((double)scale * 1.4426950408889634);
@@ -177,8 +213,32 @@ pa_status pa_decode(void* out, const void* q, const void* k_cache, const void* v
     }
   }
   hipStream_t s = static_cast<hipStream_t>(stream);
+  if (fp8) return from_hip(pa::launch_decode_mfma_fp8(p, head_dim, rows, s));
   if (dtype == PA_BF16 && rows >= kMfmaMinRows) return from_hip(pa::launch_decode_mfma(p, head_dim, rows, s));
   return from_hip(pa::launch_decode_valu(p, dtype == PA_F32 ? pa::kF32 : pa::kBF16, head_dim, rows, s));
+}
+
+}  // namespace
+
+pa_status pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache,
+                    const int32_t* block_tables, const int32_t* context_lens, float scale, int32_t q_len,
+                    int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                    int32_t num_blocks, int32_t block_size, int32_t max_blocks_per_seq, int32_t partition_size,
+                    void* workspace, size_t workspace_bytes, pa_dtype dtype, void* stream) {
+  return decode_impl(out, q, k_cache, v_cache, nullptr, nullptr, false, block_tables, context_lens, scale, q_len,
+                     num_seqs, num_q_heads, num_kv_heads, head_dim, num_blocks, block_size, max_blocks_per_seq,
+                     partition_size, workspace, workspace_bytes, dtype, stream);
+}
+
+pa_status pa_decode_fp8(void* out, const void* q, const void* k_cache, const void* v_cache, const float* k_scale,
+                        const float* v_scale, const int32_t* block_tables, const int32_t* context_lens, float scale,
+                        int32_t q_len, int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                        int32_t head_dim, int32_t num_blocks, int32_t block_size, int32_t max_blocks_per_seq,
+                        int32_t partition_size, void* workspace, size_t workspace_bytes, pa_dtype dtype,
+                        void* stream) {
+  return decode_impl(out, q, k_cache, v_cache, k_scale, v_scale, true, block_tables, context_lens, scale, q_len,
+                     num_seqs, num_q_heads, num_kv_heads, head_dim, num_blocks, block_size, max_blocks_per_seq,
+                     partition_size, workspace, workspace_bytes, dtype, stream);
 }
 
 pa_status pa_reduce(void* out, const void* workspace, size_t workspace_bytes, const int32_t* context_lens,

@@ -63,6 +63,8 @@ struct DecodeParams {
   float* ws_o;           // partitions: [S*q_len*n_h, P, D]
   int* counters;         // balanced: [S * n_kv] arrival counters, zero between calls
   float* pieces;         // balanced: [2 * num_wgs][rows_per_kv][D + 2] partial (m, l, o) per row
+  const float* k_scale;  // fp8 caches: [n_kv] per-head scales (null otherwise)
+  const float* v_scale;
   float scale_log2;      // softmax scale * log2(e)
   int q_len, group, n_h, n_kv, num_blocks, max_blocks;
   int mode;              // DecodeMode
@@ -90,10 +92,25 @@ struct CacheWriteParams {
   int num_tokens, num_blocks, row_chunks;  // row_chunks = 16-byte chunks per token row (n_kv * D * esize / 16)
 };
 
+struct CacheWriteFp8Params {
+  const void* k;  // [T, n_kv, D] of fp32 or bf16
+  const void* v;
+  uint8_t* k_cache;  // [NB, 16, n_kv, D] E4M3 codes
+  uint8_t* v_cache;
+  const int64_t* slots;
+  const float* k_scale;  // [n_kv]
+  const float* v_scale;
+  int num_tokens, num_blocks, head_dim;
+  int row_chunks;  // 16-code chunks per token row (n_kv * D / 16)
+  int in_f32;      // input dtype: 1 fp32, 0 bf16
+};
+
 // rows_per_kv = group * q_len (already validated)
 hipError_t launch_decode_valu(const DecodeParams& p, ElemType t, int head_dim, int rows_per_kv, hipStream_t s);
 hipError_t launch_decode_mfma(const DecodeParams& p, int head_dim, int rows_per_kv, hipStream_t s);
+hipError_t launch_decode_mfma_fp8(const DecodeParams& p, int head_dim, int rows_per_kv, hipStream_t s);
 hipError_t launch_reduce(const ReduceParams& p, ElemType t, int head_dim, hipStream_t s);
 hipError_t launch_cache_write(const CacheWriteParams& p, hipStream_t s);
+hipError_t launch_cache_write_fp8(const CacheWriteFp8Params& p, hipStream_t s);
 
 }  // namespace pa

@@ -75,6 +75,10 @@ class DeviceProblem:
             self.new_k = to_dev(p.new_k, dt, device)
             self.new_v = to_dev(p.new_v, dt, device)
             self.slots = torch.from_numpy(p.slot_mapping).to(device)
+        self.fp8 = p.spec.kv == "fp8"
+        if self.fp8:
+            self.k_scale = torch.from_numpy(p.k_scale).to(device)
+            self.v_scale = torch.from_numpy(p.v_scale).to(device)
         self.out = torch.empty_like(self.q)
         self.workspace = None
 
@@ -84,15 +88,25 @@ class DeviceProblem:
 
         p = self.p
         if write and self.new_k is not None:
-            pa.cache_write(self.new_k, self.new_v, self.k_cache, self.v_cache, self.slots)
+            if self.fp8:
+                pa.cache_write_fp8(self.new_k, self.new_v, self.k_cache, self.v_cache, self.slots, self.k_scale,
+                                   self.v_scale)
+            else:
+                pa.cache_write(self.new_k, self.new_v, self.k_cache, self.v_cache, self.slots)
+
+        def dec(ps, out=None, workspace=None):
+            if self.fp8:
+                return pa.decode_fp8(self.q, self.k_cache, self.v_cache, self.k_scale, self.v_scale, self.block_tables,
+                                     self.context_lens, float(p.scale), p.q_len, ps, out=out, workspace=workspace)
+            return pa.decode(self.q, self.k_cache, self.v_cache, self.block_tables, self.context_lens, float(p.scale),
+                             p.q_len, ps, out=out, workspace=workspace)
+
         if partition_size <= 0:  # one pass or balanced
             if partition_size < 0 and self.workspace is None:
                 self.workspace = pa.new_workspace(self.q, self.k_cache, self.block_tables, p.q_len, partition_size)
-            pa.decode(self.q, self.k_cache, self.v_cache, self.block_tables, self.context_lens, float(p.scale),
-                      p.q_len, partition_size, out=self.out, workspace=self.workspace)
+            dec(partition_size, out=self.out, workspace=self.workspace)
         else:
-            self.workspace = pa.decode(self.q, self.k_cache, self.v_cache, self.block_tables, self.context_lens,
-                                       float(p.scale), p.q_len, partition_size, workspace=self.workspace)
+            self.workspace = dec(partition_size, workspace=self.workspace)
             pa.reduce(self.out, self.workspace, self.context_lens, p.q_len, p.max_blocks_per_seq, partition_size)
         return self.out
 
@@ -103,7 +117,27 @@ def host_caches_after_write(p: wl.Problem):
 
     if p.new_k is None:
         return p.k_cache, p.v_cache
+    if p.spec.kv == "fp8":
+        return oracle.cache_write_fp8(p.k_cache, p.v_cache, p.new_k, p.new_v, p.slot_mapping, p.k_scale, p.v_scale,
+                                      p.dtype)
     return oracle.cache_write(p.k_cache, p.v_cache, p.new_k, p.new_v, p.slot_mapping)
+
+
+def reference_rows(p: wl.Problem, rows, kc=None, vc=None):
+    """The oracle on the listed (b, j, h) rows over the caches after the write."""
+    import oracle
+
+    if kc is None:
+        kc, vc = host_caches_after_write(p)
+    if p.spec.kv == "fp8":
+        return oracle.paged_decode_fp8_rows(p.q, kc, vc, p.k_scale, p.v_scale, p.block_tables, p.context_lens,
+                                            p.scale, p.q_len, p.dtype, rows)
+    return oracle.paged_decode_rows(p.q, kc, vc, p.block_tables, p.context_lens, p.scale, p.q_len, p.dtype, rows)
+
+
+def reference_full(p: wl.Problem):
+    rows = [(b, j, h) for b in range(p.num_seqs) for j in range(p.q_len) for h in range(p.num_q_heads)]
+    return reference_rows(p, rows).reshape(p.num_seqs * p.q_len, p.num_q_heads, p.head_dim)
 
 
 def sample_rows(p: wl.Problem, n: int, seed: int = 0):

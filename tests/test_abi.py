@@ -15,7 +15,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 def declared_functions():
     text = open(os.path.join(ROOT, "include", "pa.h")).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(pa_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(pa_[a-z0-9_]+)\s*\(", text)))
 
 
 @pytest.fixture(scope="module")
@@ -102,6 +102,33 @@ def test_cache_write_rejects_invalid_arguments(lib):
     assert f(FAKE, FAKE, FAKE, FAKE, FAKE, 4, 16, 16, 2, 80, pa.PA_BF16, None) == 3
     assert f(FAKE, FAKE, FAKE, FAKE, FAKE, -1, 16, 16, 2, 64, pa.PA_BF16, None) == 2
     assert f(None, None, None, None, None, 0, 16, 16, 2, 64, pa.PA_BF16, None) == 0  # nothing to write
+
+
+def test_cache_write_fp8_rejects_invalid_arguments(lib):
+    f = lib.pa_cache_write_fp8
+    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, 4, 16, 16, 2, 64, pa.PA_BF16, None) == 1  # no k_scale
+    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 4, 16, 8, 2, 64, pa.PA_BF16, None) == 3
+    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 4, 16, 16, 2, 96, pa.PA_BF16, None) == 3
+    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, -1, 16, 16, 2, 64, pa.PA_BF16, None) == 2
+    assert f(None, None, None, None, None, None, None, 0, 16, 16, 2, 64, pa.PA_BF16, None) == 0
+
+
+def _decode_fp8(lib, **kw):
+    a = dict(out=FAKE, q=FAKE, kc=FAKE, vc=FAKE, ks=FAKE, vs=FAKE, bt=FAKE, cl=FAKE, scale=0.1, q_len=1, S=2, n_h=4,
+             n_kv=2, d=64, NB=16, bs=16, MB=3, ps=0, ws=None, wsb=0, dt=pa.PA_BF16, stream=None)
+    a.update(kw)
+    return lib.pa_decode_fp8(a["out"], a["q"], a["kc"], a["vc"], a["ks"], a["vs"], a["bt"], a["cl"], a["scale"],
+                             a["q_len"], a["S"], a["n_h"], a["n_kv"], a["d"], a["NB"], a["bs"], a["MB"], a["ps"],
+                             a["ws"], a["wsb"], a["dt"], a["stream"])
+
+
+def test_decode_fp8_rejects_invalid_arguments(lib):
+    assert _decode_fp8(lib, dt=pa.PA_F32) == 3          # q/out must be bf16
+    assert _decode_fp8(lib, ks=None) == 1
+    assert _decode_fp8(lib, vs=None) == 1
+    assert _decode_fp8(lib, n_h=130, n_kv=2) == 3       # 65 rows per KV head
+    assert _decode_fp8(lib, ps=-1, ws=None) == 4
+    assert _decode_fp8(lib, S=0, q=None, out=None) == 0
 
 
 def test_reduce_rejects_invalid_arguments(lib):

@@ -117,6 +117,7 @@ class Spec:
     scale: Optional[float] = None  # None -> fp32(1/sqrt(head_dim))
     pad: str = "valid"  # block-table padding: "valid" random in-range ids | "garbage"
     poison: bool = False  # NaN in cache rows never read (unused blocks, rows >= L)
+    kv: str = "same"  # cache element type: "same" as dtype | "fp8" (E4M3 codes with per-head scales; dtype bf16)
     description: str = ""
 
     @property
@@ -161,6 +162,12 @@ CONFIGS = {
 
 CONFIG_ORDER = ["tiny-f32", "llama3-8b-decode", "llama3-70b-decode", "long-split", "spec-verify"]
 
+# Beyond the five workloads: the Llama-3-8B-shaped layer over an fp8 (E4M3) cache
+CONFIGS["llama3-8b-decode-fp8kv"] = CONFIGS["llama3-8b-decode"].with_(
+    name="llama3-8b-decode-fp8kv", kv="fp8",
+    description="the llama3-8b-decode layer with an fp8 (E4M3) KV cache, per-head scales, 64 new tokens quantized "
+                "by pa_cache_write_fp8")
+
 
 # ----------------------------------------------------------------------------
 # problems
@@ -178,6 +185,8 @@ class Problem:
     new_k: Optional[np.ndarray] = None  # [T, n_kv, d]
     new_v: Optional[np.ndarray] = None
     slot_mapping: Optional[np.ndarray] = None  # int64 [T]
+    k_scale: Optional[np.ndarray] = None  # fp8 caches: float32 [n_kv]
+    v_scale: Optional[np.ndarray] = None
     extra: dict = field(default_factory=dict)
 
     # convenience views of the spec
@@ -240,10 +249,44 @@ def draw_lens(spec: Spec, rng: np.random.Generator) -> np.ndarray:
     return lens.astype(np.int32)
 
 
+FP8_NAN_CODE = np.uint8(0x7F)
+
+
+def fp8_scales(n_kv: int, which: str) -> np.ndarray:
+    """Per-head scales of a synthetic fp8 cache: 1/64 to 1.25/64 (K) and 1/48 to 1.25/48 (V)
+    across the heads, so that N(0,1) data spans most of the +-448 code range and every head
+    has its own scale."""
+    base = 1.0 / 64 if which == "k" else 1.0 / 48
+    return (base * (1.0 + 0.25 * np.arange(n_kv) / max(1, n_kv - 1))).astype(np.float32)
+
+
+def to_fp8_codes(bits_bf16: np.ndarray, scale: np.ndarray) -> np.ndarray:
+    """E4M3 codes of bf16 data divided by the per-head scale (last-but-one axis is the
+    head), through torch's float8_e4m3fn cast after clamping to +-448: a library
+    conversion that prepares synthetic cache contents (the oracle and the kernels
+    each quantize new tokens with their own code)."""
+    import torch
+
+    x = torch.from_numpy(np.ascontiguousarray(bits_bf16).view(np.int16)).view(torch.bfloat16).to(torch.float32)
+    s = torch.from_numpy(scale.astype(np.float32))[:, None]
+    return (x / s).clamp_(-448.0, 448.0).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+
+
 def make_problem(spec: Spec) -> Problem:
     """Draw every input of one workload from spec.seed."""
     if isinstance(spec, str):
         spec = CONFIGS[spec]
+    if spec.kv == "fp8":
+        assert spec.dtype == "bf16", "fp8 caches go with bf16 queries"
+        p = make_problem(spec.with_(kv="same", poison=False))
+        p.spec = spec
+        p.k_scale = fp8_scales(spec.num_kv_heads, "k")
+        p.v_scale = fp8_scales(spec.num_kv_heads, "v")
+        p.k_cache = to_fp8_codes(p.k_cache, p.k_scale)
+        p.v_cache = to_fp8_codes(p.v_cache, p.v_scale)
+        if spec.poison:
+            poison_unread(spec, p.context_lens, p.block_tables, p.k_cache, p.v_cache)
+        return p
     rng = np.random.default_rng(spec.seed)
     S, bs = spec.num_seqs, BLOCK_SIZE
     lens = draw_lens(spec, rng)
@@ -303,7 +346,7 @@ def make_problem(spec: Spec) -> Problem:
 def poison_unread(spec: Spec, lens, tables, k_cache, v_cache) -> None:
     """Write NaN into every cache row that a correct kernel never reads."""
     bs = BLOCK_SIZE
-    nan = BF16_QNAN_BITS if spec.dtype == "bf16" else F32_QNAN
+    nan = FP8_NAN_CODE if spec.kv == "fp8" else (BF16_QNAN_BITS if spec.dtype == "bf16" else F32_QNAN)
     used = np.zeros(k_cache.shape[0], dtype=bool)
     for b in range(len(lens)):
         nb = (int(lens[b]) + bs - 1) // bs
@@ -349,7 +392,8 @@ def algorithmic_bytes(problem: Problem) -> dict:
     'unique' counts physical rows once when sequences share prefix blocks.
     """
     esz = 4 if problem.dtype == "f32" else 2
-    row = problem.num_kv_heads * problem.head_dim * esz  # one token's K (or V) over all kv heads
+    kv_esz = 1 if problem.spec.kv == "fp8" else esz
+    row = problem.num_kv_heads * problem.head_dim * kv_esz  # one token's K (or V) over all kv heads
     logical_tokens = int(problem.context_lens.astype(np.int64).sum())
     shared_tokens = problem.spec.shared_prefix_blocks * BLOCK_SIZE
     unique_tokens = logical_tokens - max(0, problem.num_seqs - 1) * shared_tokens if shared_tokens else logical_tokens
