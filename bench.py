@@ -332,6 +332,7 @@ def main(argv=None):
             "context_tokens": int(p.context_lens.sum()), "num_blocks": p.num_blocks,
             "new_tokens_written": 0 if p.slot_mapping is None else int(len(p.slot_mapping)),
             "partition_size": partition, "seed": spec.seed,
+            "kv_cache": "fp8 E4M3, per-head scales" if p.spec.kv == "fp8" else p.dtype,
         },
         "kv_hbm_gbps_step": round(kv_bytes / (ms_per_step / 1e3) / 1e9, 1),
         "breakdown_us": {"cache_write": round(write_ms * 1e3, 2), "decode": round(decode_ms * 1e3, 2),
