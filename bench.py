@@ -199,6 +199,45 @@ def cpu_baseline(p: wl.Problem, gpu_out, budget_s: float = 10.0):
     }
 
 
+def bench_copy_blocks(args, torch) -> int:
+    """pa_copy_blocks of 2048 distinct random blocks (K and V) within the workload's pool:
+    every step reads and writes 2 x 2048 blocks; bytes moved / time against the HBM peak."""
+    import paged_kv_attention_decode_amd as pa
+
+    spec = wl.CONFIGS[args.config]
+    p = wl.make_problem(spec)
+    kc, vc = to_dev(p.k_cache, torch), to_dev(p.v_cache, torch)
+    n = min(2048, p.num_blocks // 2)
+    ids = np.random.default_rng(spec.seed).permutation(p.num_blocks)
+    mapping = torch.from_numpy(np.stack([ids[:n], ids[n:2 * n]], axis=1).astype(np.int64)).cuda()
+    block_bytes = kc[0].numel() * kc.element_size()
+    for _ in range(max(0, args.warmup)):
+        pa.copy_blocks(kc, vc, kc, vc, mapping)
+    torch.cuda.synchronize()
+    K = args.steps
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
+    t0 = time.perf_counter()
+    for k in range(K):
+        ev[k][0].record()
+        pa.copy_blocks(kc, vc, kc, vc, mapping)
+        ev[k][1].record()
+    torch.cuda.synchronize()
+    ms_per_step = (time.perf_counter() - t0) * 1e3 / K
+    launch_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    moved = 2 * 2 * n * block_bytes  # K and V, read and written
+    achieved = moved / (launch_ms / 1e3) / 1e9
+    print(json.dumps({
+        "metric": "pa_copy_blocks HBM GB/s (read + written) per call", "value": round(achieved, 1), "unit": "GB/s",
+        "n_gpus": 1, "steps": K, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": p.dtype, "data": "synthetic",
+        "config": {"workload": args.config, "op": "copy-blocks", "blocks_copied": n, "block_bytes": block_bytes},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None, "kernel": "copy_blocks_kernel",
+                     "algorithmic_bytes_per_launch": moved, "avg_launch_us": round(launch_ms * 1e3, 2)},
+    }), flush=True)
+    return 0
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -209,6 +248,8 @@ def main(argv=None):
     ap.add_argument("--no-cpu", action="store_true", help="skip the cpu_baseline leg")
     ap.add_argument("--cold", type=int, default=0,
                     help="also time this many decode launches one by one, each after a 1 GiB cache flush")
+    ap.add_argument("--op", default="decode", choices=["decode", "copy-blocks"],
+                    help="decode: the whole path (default); copy-blocks: pa_copy_blocks of 2048 blocks of the pool")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a 1 GiB device copy (for scaling memory counters)")
     args = ap.parse_args(argv)
@@ -224,6 +265,9 @@ def main(argv=None):
         print(json.dumps({"error": "no GPU visible"}))
         return 1
     torch.cuda.set_device(0)
+
+    if args.op == "copy-blocks":
+        return bench_copy_blocks(args, torch)
 
     spec = wl.CONFIGS[args.config]
     p = wl.make_problem(spec)

@@ -10,7 +10,8 @@
  *   pa_reduce       merge the partials of a split pa_decode into the output;
  *   pa_cache_write_fp8, pa_decode_fp8
  *                   the same over a KV cache of fp8 (E4M3) codes with one
- *                   scale per KV head.
+ *                   scale per KV head;
+ *   pa_copy_blocks  copy whole blocks (copy-on-write, swapping).
  *
  * Sources of the definitions (the web pages this library implements):
  *   - per layer, K and V are each stored as [num_blocks, block_size,
@@ -237,6 +238,31 @@ pa_status pa_decode_fp8(void* out, const void* q, const void* k_cache, const voi
                         int32_t head_dim, int32_t num_blocks, int32_t block_size, int32_t max_blocks_per_seq,
                         int32_t partition_size, void* workspace, size_t workspace_bytes, pa_dtype dtype,
                         void* stream);
+
+/*
+ * pa_copy_blocks - copy whole KV blocks, for copy-on-write and swapping.
+ *
+ * Before a sequence writes into a block that other sequences share, it gets a
+ * private copy ("LLM serving: KV cache, batching, paged attention and
+ * quantization", learn.mohebi.ai, section 3.5, sharing and copy-on-write); a
+ * paused sequence's blocks can be swapped out and back ("Chapter 18:
+ * Speculative Decoding and Serving Optimizations", arunshar.com, section
+ * 18.2.2).  For every pair p, block block_mapping[2p] of the source caches is
+ * copied to block block_mapping[2p + 1] of the destination caches, K and V,
+ * as raw bytes (any element type: bf16, fp32 or fp8 codes).
+ *
+ *   src_k, src_v  device caches of src_num_blocks blocks of block_bytes each
+ *                 ([num_blocks, block_size, num_kv_heads, head_dim] of any type).
+ *   dst_k, dst_v  device caches of dst_num_blocks blocks (may be src_k, src_v).
+ *   block_mapping int64 [num_pairs, 2] device array of (source, destination) ids;
+ *                 pairs with an id outside its pool are skipped.  Destinations
+ *                 must be distinct and no destination may be a source of the
+ *                 same call (then the copies do not depend on their order).
+ *   block_bytes   a positive multiple of 16 (bytes of one block of K, or of V).
+ */
+pa_status pa_copy_blocks(const void* src_k, const void* src_v, void* dst_k, void* dst_v,
+                         const int64_t* block_mapping, int32_t num_pairs, int32_t src_num_blocks,
+                         int32_t dst_num_blocks, int64_t block_bytes, void* stream);
 
 const char* pa_status_string(pa_status status);
 

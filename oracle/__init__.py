@@ -31,6 +31,10 @@ What it computes, and which passage each step follows:
   batching, paged attention and quantization", learn.mohebi.ai, section 3.7;
   "07 - Inference", lourdhu02.github.io, section 4.3).
 
+* Block copies for copy-on-write and swapping (oracle/blocks.py): whole
+  blocks as raw bytes (learn.mohebi.ai, section 3.5; arunshar.com, section
+  18.2.2).
+
 Parity of individual output elements is pinned by the tests in
 tests/test_oracle.py and tests/test_oracle_fp8.py (brute-force SDPA, closed
 forms, torch's float8 type, invariants).
@@ -51,6 +55,7 @@ from .attention import (  # noqa: F401
     to_f64,
     visible_tokens,
 )
+from .blocks import copy_blocks  # noqa: F401
 from .fp8 import (  # noqa: F401
     cache_write_fp8,
     e4m3_decode,

@@ -12,6 +12,7 @@ on the GPU, the call raises.
     decode_workspace_size(...), new_workspace(...)
     paged_attention(...)   # decode, plus reduce when the context is split
     cache_write_fp8(...), decode_fp8(...)   # the same over an fp8 (E4M3) cache with per-head scales
+    copy_blocks(...)       # whole-block copies (copy-on-write, swapping)
 """
 
 from __future__ import annotations
@@ -23,14 +24,14 @@ from typing import Optional
 __all__ = [
     "PA_F32", "PA_BF16", "PA_BALANCED", "PagedAttentionError", "library_path", "load_library", "status_string", "version",
     "cache_write", "decode", "reduce", "decode_workspace_size", "paged_attention", "cache_write_fp8", "decode_fp8",
-    "SYMBOLS",
+    "copy_blocks", "SYMBOLS",
 ]
 
 PA_F32, PA_BF16 = 0, 1
 PA_BALANCED = -1  # partition_size selecting the work-balanced decode
 BLOCK_SIZE = 16
 SYMBOLS = ("pa_cache_write", "pa_decode", "pa_decode_workspace_size", "pa_reduce", "pa_status_string", "pa_version",
-           "pa_cache_write_fp8", "pa_decode_fp8")
+           "pa_cache_write_fp8", "pa_decode_fp8", "pa_copy_blocks")
 _STATUS = {0: "PA_OK", 1: "PA_ERR_NULL", 2: "PA_ERR_SHAPE", 3: "PA_ERR_UNSUPPORTED", 4: "PA_ERR_WORKSPACE",
            5: "PA_ERR_HIP"}
 
@@ -72,6 +73,8 @@ def load_library():
     lib.pa_decode_fp8.restype = ctypes.c_int
     lib.pa_decode_fp8.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, f32, i32, i32, i32, i32, i32, i32, i32, i32, i32,
                                   vp, sz, ctypes.c_int, vp]
+    lib.pa_copy_blocks.restype = ctypes.c_int
+    lib.pa_copy_blocks.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, ctypes.c_int64, vp]
     lib.pa_status_string.restype = ctypes.c_char_p
     lib.pa_status_string.argtypes = [ctypes.c_int]
     lib.pa_version.restype = i32
@@ -308,3 +311,27 @@ def decode_fp8(q, k_cache, v_cache, k_scale, v_scale, block_tables, context_lens
                                       pws, nws, PA_BF16, _stream(stream))
     _check(st, "pa_decode_fp8")
     return out if partition_size <= 0 else workspace
+
+
+# ---------------------------------------------------------------------------
+# block copies
+
+
+def copy_blocks(src_k, src_v, dst_k, dst_v, block_mapping, stream=None) -> None:
+    """pa_copy_blocks: for each row (s, d) of block_mapping (int64 [pairs, 2] on the GPU),
+    copy block s of src_k/src_v to block d of dst_k/dst_v as raw bytes.  The caches are
+    [num_blocks, block_size, n_kv, d] of any one element type; src and dst may be the same."""
+    torch = _torch()
+    if src_k.shape != src_v.shape or dst_k.shape != dst_v.shape or src_k.shape[1:] != dst_k.shape[1:]:
+        raise ValueError("K/V pairs must match, and source and destination blocks must have the same shape")
+    if src_k.dtype != dst_k.dtype or src_v.dtype != src_k.dtype or dst_v.dtype != dst_k.dtype:
+        raise TypeError("source and destination caches must have the same element type")
+    pm = _dev(block_mapping, "block_mapping", torch.int64, 2)
+    if block_mapping.shape[1] != 2:
+        raise ValueError("block_mapping must be [pairs, 2]")
+    block_bytes = src_k[0].numel() * src_k.element_size()
+    st = load_library().pa_copy_blocks(_dev(src_k, "src_k", ndim=4), _dev(src_v, "src_v", ndim=4),
+                                       _dev(dst_k, "dst_k", ndim=4), _dev(dst_v, "dst_v", ndim=4), pm,
+                                       block_mapping.shape[0], src_k.shape[0], dst_k.shape[0], block_bytes,
+                                       _stream(stream))
+    _check(st, "pa_copy_blocks")

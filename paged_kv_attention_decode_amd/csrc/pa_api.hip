@@ -133,6 +133,28 @@ pa_status pa_cache_write_fp8(const void* k, const void* v, void* k_cache, void* 
   return from_hip(pa::launch_cache_write_fp8(p, static_cast<hipStream_t>(stream)));
 }
 
+pa_status pa_copy_blocks(const void* src_k, const void* src_v, void* dst_k, void* dst_v,
+                         const int64_t* block_mapping, int32_t num_pairs, int32_t src_num_blocks,
+                         int32_t dst_num_blocks, int64_t block_bytes, void* stream) {
+  if (num_pairs < 0 || src_num_blocks <= 0 || dst_num_blocks <= 0 || block_bytes <= 0 || block_bytes % 16 != 0)
+    return PA_ERR_SHAPE;
+  if (num_pairs == 0) return PA_OK;
+  if (num_pairs > 0x7fffffff / 2) return PA_ERR_UNSUPPORTED;
+  if (!src_k || !src_v || !dst_k || !dst_v || !block_mapping) return PA_ERR_NULL;
+  if (!aligned16(src_k) || !aligned16(src_v) || !aligned16(dst_k) || !aligned16(dst_v)) return PA_ERR_SHAPE;
+  pa::CopyBlocksParams p;
+  p.src_k = src_k;
+  p.src_v = src_v;
+  p.dst_k = dst_k;
+  p.dst_v = dst_v;
+  p.mapping = block_mapping;
+  p.num_pairs = num_pairs;
+  p.src_blocks = src_num_blocks;
+  p.dst_blocks = dst_num_blocks;
+  p.block_chunks = block_bytes / 16;
+  return from_hip(pa::launch_copy_blocks(p, static_cast<hipStream_t>(stream)));
+}
+
 size_t pa_decode_workspace_size(int32_t num_seqs, int32_t q_len, int32_t num_q_heads, int32_t num_kv_heads,
                                 int32_t head_dim, int32_t max_blocks_per_seq, int32_t block_size,
                                 int32_t partition_size) {

@@ -105,6 +105,17 @@ struct CacheWriteFp8Params {
   int in_f32;      // input dtype: 1 fp32, 0 bf16
 };
 
+struct CopyBlocksParams {
+  const void* src_k;
+  const void* src_v;
+  void* dst_k;
+  void* dst_v;
+  const int64_t* mapping;  // [num_pairs, 2] (source, destination)
+  int num_pairs;
+  int64_t src_blocks, dst_blocks;
+  int64_t block_chunks;  // 16-byte chunks per block
+};
+
 // rows_per_kv = group * q_len (already validated)
 hipError_t launch_decode_valu(const DecodeParams& p, ElemType t, int head_dim, int rows_per_kv, hipStream_t s);
 hipError_t launch_decode_mfma(const DecodeParams& p, int head_dim, int rows_per_kv, hipStream_t s);
@@ -112,5 +123,6 @@ hipError_t launch_decode_mfma_fp8(const DecodeParams& p, int head_dim, int rows_
 hipError_t launch_reduce(const ReduceParams& p, ElemType t, int head_dim, hipStream_t s);
 hipError_t launch_cache_write(const CacheWriteParams& p, hipStream_t s);
 hipError_t launch_cache_write_fp8(const CacheWriteFp8Params& p, hipStream_t s);
+hipError_t launch_copy_blocks(const CopyBlocksParams& p, hipStream_t s);
 
 }  // namespace pa

@@ -131,6 +131,14 @@ def test_decode_fp8_rejects_invalid_arguments(lib):
     assert _decode_fp8(lib, S=0, q=None, out=None) == 0
 
 
+def test_copy_blocks_rejects_invalid_arguments(lib):
+    f = lib.pa_copy_blocks
+    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, 3, 16, 16, 8, None) == 2       # block bytes not a multiple of 16
+    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, 3, 0, 16, 4096, None) == 2
+    assert f(FAKE, FAKE, FAKE, FAKE, None, 3, 16, 16, 4096, None) == 1
+    assert f(None, None, None, None, None, 0, 16, 16, 4096, None) == 0    # nothing to copy
+
+
 def test_reduce_rejects_invalid_arguments(lib):
     f = lib.pa_reduce
     assert f(FAKE, FAKE, 1 << 30, FAKE, 2, 1, 4, 64, 3, 16, 0, pa.PA_F32, None) == 2     # partition_size 0
