@@ -199,9 +199,16 @@ def cpu_baseline(p: wl.Problem, gpu_out, budget_s: float = 10.0):
     }
 
 
+PCIE_PEAK_GBPS = 64.0  # host link: PCIe 5.0 x16, one direction
+
+
 def bench_copy_blocks(args, torch) -> int:
-    """pa_copy_blocks of 2048 distinct random blocks (K and V) within the workload's pool:
-    every step reads and writes 2 x 2048 blocks; bytes moved / time against the HBM peak."""
+    """pa_copy_blocks of 2048 distinct random blocks (K and V) of the workload's pool.
+
+    copy-blocks: within the pool (copy-on-write); every call reads and writes
+    2 x 2048 blocks of HBM, rated against the HBM peak.  swap-out / swap-in: the
+    same blocks to / from a pinned host pool of 2048 blocks, rated by the bytes
+    crossing the host link against its one-direction peak."""
     import paged_kv_attention_decode_amd as pa
 
     spec = wl.CONFIGS[args.config]
@@ -209,30 +216,45 @@ def bench_copy_blocks(args, torch) -> int:
     kc, vc = to_dev(p.k_cache, torch), to_dev(p.v_cache, torch)
     n = min(2048, p.num_blocks // 2)
     ids = np.random.default_rng(spec.seed).permutation(p.num_blocks)
-    mapping = torch.from_numpy(np.stack([ids[:n], ids[n:2 * n]], axis=1).astype(np.int64)).cuda()
     block_bytes = kc[0].numel() * kc.element_size()
+    if args.op == "copy-blocks":
+        pairs = np.stack([ids[:n], ids[n:2 * n]], axis=1)
+        src, dst = (kc, vc), (kc, vc)
+        moved, bound, peak = 2 * 2 * n * block_bytes, "hbm", HBM_PEAK_GBPS  # K and V, read and written
+    else:
+        hk = torch.empty((n,) + tuple(kc.shape[1:]), dtype=kc.dtype).pin_memory()
+        hv = torch.empty_like(hk).pin_memory()
+        host = np.random.default_rng(spec.seed + 1).permutation(n)
+        if args.op == "swap-out":
+            pairs = np.stack([ids[:n], host], axis=1)
+            src, dst = (kc, vc), (hk, hv)
+        else:
+            pairs = np.stack([host, ids[:n]], axis=1)
+            src, dst = (hk, hv), (kc, vc)
+        moved, bound, peak = 2 * n * block_bytes, "pcie", PCIE_PEAK_GBPS  # K and V across the link
+    mapping = torch.from_numpy(pairs.astype(np.int64)).cuda()
     for _ in range(max(0, args.warmup)):
-        pa.copy_blocks(kc, vc, kc, vc, mapping)
+        pa.copy_blocks(*src, *dst, mapping)
     torch.cuda.synchronize()
     K = args.steps
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
     t0 = time.perf_counter()
     for k in range(K):
         ev[k][0].record()
-        pa.copy_blocks(kc, vc, kc, vc, mapping)
+        pa.copy_blocks(*src, *dst, mapping)
         ev[k][1].record()
     torch.cuda.synchronize()
     ms_per_step = (time.perf_counter() - t0) * 1e3 / K
     launch_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
-    moved = 2 * 2 * n * block_bytes  # K and V, read and written
     achieved = moved / (launch_ms / 1e3) / 1e9
+    what = "HBM GB/s (read + written)" if bound == "hbm" else "host-link GB/s"
     print(json.dumps({
-        "metric": "pa_copy_blocks HBM GB/s (read + written) per call", "value": round(achieved, 1), "unit": "GB/s",
+        "metric": f"pa_copy_blocks {what} per call", "value": round(achieved, 1), "unit": "GB/s",
         "n_gpus": 1, "steps": K, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": p.dtype, "data": "synthetic",
-        "config": {"workload": args.config, "op": "copy-blocks", "blocks_copied": n, "block_bytes": block_bytes},
-        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None, "kernel": "copy_blocks_kernel",
+        "config": {"workload": args.config, "op": args.op, "blocks_copied": n, "block_bytes": block_bytes},
+        "roofline": {"bound": bound, "achieved": round(achieved, 1), "peak": peak, "unit": "GB/s",
+                     "frac": round(achieved / peak, 4), "traffic": None, "kernel": "copy_blocks_kernel",
                      "algorithmic_bytes_per_launch": moved, "avg_launch_us": round(launch_ms * 1e3, 2)},
     }), flush=True)
     return 0
@@ -248,8 +270,9 @@ def main(argv=None):
     ap.add_argument("--no-cpu", action="store_true", help="skip the cpu_baseline leg")
     ap.add_argument("--cold", type=int, default=0,
                     help="also time this many decode launches one by one, each after a 1 GiB cache flush")
-    ap.add_argument("--op", default="decode", choices=["decode", "copy-blocks"],
-                    help="decode: the whole path (default); copy-blocks: pa_copy_blocks of 2048 blocks of the pool")
+    ap.add_argument("--op", default="decode", choices=["decode", "copy-blocks", "swap-out", "swap-in"],
+                    help="decode: the whole path (default); copy-blocks: pa_copy_blocks of 2048 blocks within "
+                         "the pool; swap-out / swap-in: the same 2048 blocks to / from pinned host memory")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a 1 GiB device copy (for scaling memory counters)")
     args = ap.parse_args(argv)
@@ -266,7 +289,7 @@ def main(argv=None):
         return 1
     torch.cuda.set_device(0)
 
-    if args.op == "copy-blocks":
+    if args.op != "decode":
         return bench_copy_blocks(args, torch)
 
     spec = wl.CONFIGS[args.config]

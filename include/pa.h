@@ -71,7 +71,8 @@ typedef enum {
   PA_ERR_SHAPE = 2,       /* sizes inconsistent or out of range */
   PA_ERR_UNSUPPORTED = 3, /* valid but not implemented (head_dim, block_size, rows per KV head, dtype) */
   PA_ERR_WORKSPACE = 4,   /* workspace missing or smaller than pa_decode_workspace_size() */
-  PA_ERR_HIP = 5          /* the HIP runtime reported an error at launch */
+  PA_ERR_HIP = 5,         /* the HIP runtime reported an error at launch */
+  PA_ERR_MEMORY = 6       /* a buffer is not memory the GPU can access (e.g. pageable host memory) */
 } pa_status;
 
 typedef enum { PA_F32 = 0, PA_BF16 = 1 } pa_dtype;
@@ -251,9 +252,16 @@ pa_status pa_decode_fp8(void* out, const void* q, const void* k_cache, const voi
  * copied to block block_mapping[2p + 1] of the destination caches, K and V,
  * as raw bytes (any element type: bf16, fp32 or fp8 codes).
  *
- *   src_k, src_v  device caches of src_num_blocks blocks of block_bytes each
+ *   src_k, src_v  caches of src_num_blocks blocks of block_bytes each
  *                 ([num_blocks, block_size, num_kv_heads, head_dim] of any type).
- *   dst_k, dst_v  device caches of dst_num_blocks blocks (may be src_k, src_v).
+ *   dst_k, dst_v  caches of dst_num_blocks blocks (may be src_k, src_v).
+ *                 Each of the four may be device memory or pinned host memory
+ *                 (hipHostMalloc), so one call swaps blocks out to host DRAM or
+ *                 back in over the host link.  The library asks the runtime
+ *                 about each pointer (hipPointerGetAttributes) and returns
+ *                 PA_ERR_MEMORY, launching nothing, for memory the GPU cannot
+ *                 access (pageable host memory).  Host buffers must not be
+ *                 touched by the host until the stream has passed the copy.
  *   block_mapping int64 [num_pairs, 2] device array of (source, destination) ids;
  *                 pairs with an id outside its pool are skipped.  Destinations
  *                 must be distinct and no destination may be a source of the

@@ -33,7 +33,7 @@ BLOCK_SIZE = 16
 SYMBOLS = ("pa_cache_write", "pa_decode", "pa_decode_workspace_size", "pa_reduce", "pa_status_string", "pa_version",
            "pa_cache_write_fp8", "pa_decode_fp8", "pa_copy_blocks")
 _STATUS = {0: "PA_OK", 1: "PA_ERR_NULL", 2: "PA_ERR_SHAPE", 3: "PA_ERR_UNSUPPORTED", 4: "PA_ERR_WORKSPACE",
-           5: "PA_ERR_HIP"}
+           5: "PA_ERR_HIP", 6: "PA_ERR_MEMORY"}
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _lib = None
@@ -317,10 +317,21 @@ def decode_fp8(q, k_cache, v_cache, k_scale, v_scale, block_tables, context_lens
 # block copies
 
 
+def _pool(t, name):
+    """A cache for copy_blocks: on the GPU, or in pinned host memory (swap space)."""
+    torch = _torch()
+    if isinstance(t, torch.Tensor) and t.device.type == "cpu" and t.is_pinned():
+        if not t.is_contiguous() or t.dim() != 4:
+            raise ValueError(f"{name} must be a contiguous 4-dimensional cache")
+        return ctypes.c_void_p(t.data_ptr())
+    return _dev(t, name, ndim=4)
+
+
 def copy_blocks(src_k, src_v, dst_k, dst_v, block_mapping, stream=None) -> None:
     """pa_copy_blocks: for each row (s, d) of block_mapping (int64 [pairs, 2] on the GPU),
     copy block s of src_k/src_v to block d of dst_k/dst_v as raw bytes.  The caches are
-    [num_blocks, block_size, n_kv, d] of any one element type; src and dst may be the same."""
+    [num_blocks, block_size, n_kv, d] of any one element type, on the GPU or in pinned
+    host memory (swap out / swap in); src and dst may be the same."""
     torch = _torch()
     if src_k.shape != src_v.shape or dst_k.shape != dst_v.shape or src_k.shape[1:] != dst_k.shape[1:]:
         raise ValueError("K/V pairs must match, and source and destination blocks must have the same shape")
@@ -330,8 +341,8 @@ def copy_blocks(src_k, src_v, dst_k, dst_v, block_mapping, stream=None) -> None:
     if block_mapping.shape[1] != 2:
         raise ValueError("block_mapping must be [pairs, 2]")
     block_bytes = src_k[0].numel() * src_k.element_size()
-    st = load_library().pa_copy_blocks(_dev(src_k, "src_k", ndim=4), _dev(src_v, "src_v", ndim=4),
-                                       _dev(dst_k, "dst_k", ndim=4), _dev(dst_v, "dst_v", ndim=4), pm,
+    st = load_library().pa_copy_blocks(_pool(src_k, "src_k"), _pool(src_v, "src_v"),
+                                       _pool(dst_k, "dst_k"), _pool(dst_v, "dst_v"), pm,
                                        block_mapping.shape[0], src_k.shape[0], dst_k.shape[0], block_bytes,
                                        _stream(stream))
     _check(st, "pa_copy_blocks")

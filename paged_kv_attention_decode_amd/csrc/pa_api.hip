@@ -60,6 +60,29 @@ bool workspace_layout(int32_t S, int32_t q_len, int32_t n_h, int32_t n_kv, int32
 
 pa_status from_hip(hipError_t e) { return e == hipSuccess ? PA_OK : PA_ERR_HIP; }
 
+// The address a kernel uses for p: p itself for device or managed memory, the
+// mapped device address for pinned host memory; false for anything else
+// (pageable or unknown memory), which a kernel must never touch.
+bool gpu_address(const void* p, const void** out) {
+  hipPointerAttribute_t a;
+  if (hipPointerGetAttributes(&a, p) != hipSuccess) {
+    (void)hipGetLastError();  // clear the sticky error the failed query leaves
+    return false;
+  }
+  switch (a.type) {
+    case hipMemoryTypeDevice:
+    case hipMemoryTypeManaged:
+      *out = p;
+      return true;
+    case hipMemoryTypeHost:
+      if (!a.devicePointer) return false;
+      *out = a.devicePointer;
+      return true;
+    default:
+      return false;
+  }
+}
+
 }  // namespace
 
 extern "C" {
@@ -74,6 +97,7 @@ const char* pa_status_string(pa_status s) {
              "<= 64 (bf16), dtype PA_F32 or PA_BF16";
     case PA_ERR_WORKSPACE: return "PA_ERR_WORKSPACE: workspace missing, misaligned or smaller than pa_decode_workspace_size()";
     case PA_ERR_HIP: return "PA_ERR_HIP: the HIP runtime reported an error at launch";
+    case PA_ERR_MEMORY: return "PA_ERR_MEMORY: a buffer is not memory the GPU can access";
   }
   return "unknown pa_status";
 }
@@ -142,12 +166,16 @@ pa_status pa_copy_blocks(const void* src_k, const void* src_v, void* dst_k, void
   if (num_pairs > 0x7fffffff / 2) return PA_ERR_UNSUPPORTED;
   if (!src_k || !src_v || !dst_k || !dst_v || !block_mapping) return PA_ERR_NULL;
   if (!aligned16(src_k) || !aligned16(src_v) || !aligned16(dst_k) || !aligned16(dst_v)) return PA_ERR_SHAPE;
+  const void *sk, *sv, *dk, *dv, *map;
+  if (!gpu_address(src_k, &sk) || !gpu_address(src_v, &sv) || !gpu_address(dst_k, &dk) ||
+      !gpu_address(dst_v, &dv) || !gpu_address(block_mapping, &map))
+    return PA_ERR_MEMORY;
   pa::CopyBlocksParams p;
-  p.src_k = src_k;
-  p.src_v = src_v;
-  p.dst_k = dst_k;
-  p.dst_v = dst_v;
-  p.mapping = block_mapping;
+  p.src_k = sk;
+  p.src_v = sv;
+  p.dst_k = const_cast<void*>(dk);
+  p.dst_v = const_cast<void*>(dv);
+  p.mapping = static_cast<const int64_t*>(map);
   p.num_pairs = num_pairs;
   p.src_blocks = src_num_blocks;
   p.dst_blocks = dst_num_blocks;

@@ -97,3 +97,54 @@ def test_copy_on_write_then_decode():
     r = parity(got, ref, "bf16")
     assert r["ok"], r
     assert np.array_equal(to_host(kd)[7], k[7])  # the shared block is untouched
+
+
+@pytest.mark.parametrize("kind", ["bf16", "fp8"])
+def test_swap_out_to_pinned_host_and_back(kind):
+    """Blocks go out to a pinned host pool and come back into other device
+    blocks, bit-exact against the oracle doing the same two copies."""
+    import paged_kv_attention_decode_amd as pa
+
+    rng = np.random.default_rng(11)
+    n_kv, d = 4, 128
+    gk, gv = pool(rng, 30, n_kv, d, kind), pool(rng, 30, n_kv, d, kind)
+    hk, hv = pool(rng, 12, n_kv, d, kind), pool(rng, 12, n_kv, d, kind)
+    out_map = np.stack([rng.permutation(30)[:9], rng.permutation(12)[:9]], axis=1).astype(np.int64)
+    back_ids = rng.permutation(30)
+    back_map = np.stack([out_map[:, 1], back_ids[:9]], axis=1).astype(np.int64)
+    say(f"swap via pinned host kind={kind}")
+    dk, dv = to_dev(gk, "x"), to_dev(gv, "x")
+    host_k, host_v = to_dev(hk, "x", "cpu").pin_memory(), to_dev(hv, "x", "cpu").pin_memory()
+    assert host_k.is_pinned() and host_v.is_pinned()
+    pa.copy_blocks(dk, dv, host_k, host_v, torch.from_numpy(out_map).cuda())  # swap out
+    torch.cuda.synchronize()
+    ok, ov = oracle.copy_blocks(gk, gv, hk, hv, out_map)
+    assert np.array_equal(to_host(host_k), ok)
+    assert np.array_equal(to_host(host_v), ov)
+    pa.copy_blocks(host_k, host_v, dk, dv, torch.from_numpy(back_map).cuda())  # swap in
+    torch.cuda.synchronize()
+    rk, rv = oracle.copy_blocks(ok, ov, gk, gv, back_map)
+    assert np.array_equal(to_host(dk), rk)
+    assert np.array_equal(to_host(dv), rv)
+
+
+def test_pageable_host_memory_is_refused():
+    """The library launches nothing on memory the GPU cannot reach."""
+    import ctypes
+
+    import paged_kv_attention_decode_amd as pa
+
+    lib = pa.load_library()
+    dev = torch.zeros(4, 16, 2, 64, dtype=torch.bfloat16, device="cuda")
+    pageable = np.zeros((4, 16, 2, 64), np.uint16)
+    mapping = torch.tensor([[0, 1]], dtype=torch.int64, device="cuda")
+    hp = ctypes.c_void_p(pageable.ctypes.data)
+    dp = ctypes.c_void_p(dev.data_ptr())
+    st = lib.pa_copy_blocks(dp, dp, hp, hp, ctypes.c_void_p(mapping.data_ptr()), 1, 4, 4, 4096, None)
+    assert st == 6, pa.status_string(st)
+    st = lib.pa_copy_blocks(hp, hp, dp, dp, ctypes.c_void_p(mapping.data_ptr()), 1, 4, 4, 4096, None)
+    assert st == 6, pa.status_string(st)
+    torch.cuda.synchronize()
+    with pytest.raises(ValueError):
+        pa.copy_blocks(dev, dev, torch.zeros(4, 16, 2, 64, dtype=torch.bfloat16), torch.zeros(4, 16, 2, 64,
+                       dtype=torch.bfloat16), mapping)

@@ -80,3 +80,52 @@ def test_planted_mistake_swapped_pair_is_caught():
     wrong = k2.copy()
     wrong[3] = k[7]  # source and destination swapped
     assert not np.array_equal(ok, wrong)
+
+
+def test_worked_example_four_samples_of_a_thousand_token_prompt():
+    """The parallel-sampling exercise of "LLM serving: KV cache, batching, paged
+    attention and quantization" (learn.mohebi.ai, section 8 "Check yourself",
+    question 4): 4 samples share a 1000-token prompt
+    in ceil(1000/16) = 63 blocks (62 full, one holding 8 tokens) with reference
+    count 4.  Each writes its first new token into the shared last block: the
+    first three writers get a private copy, the last finds the count at 1 and
+    writes in place, for 66 blocks in all.  Played here with reference counts
+    and the oracle's copy and cache write; each sample then sees the 1000
+    shared tokens plus its own token, and nothing else."""
+    rng = np.random.default_rng(12)
+    n_kv, d, prompt, S = 1, 16, 1000, 4
+    NB = 80
+    k = wl.round_to_bf16_bits(rng.standard_normal((NB, 16, n_kv, d)).astype(np.float32))
+    v = wl.round_to_bf16_bits(rng.standard_normal((NB, 16, n_kv, d)).astype(np.float32))
+    n_blocks = -(-prompt // 16)
+    assert n_blocks == 63 and prompt - 62 * 16 == 8
+    free = list(range(n_blocks, NB))
+    refs = {b: S for b in range(n_blocks)}
+    tables = np.tile(np.arange(n_blocks, dtype=np.int32), (S, 1))
+    new_k = wl.round_to_bf16_bits(rng.standard_normal((S, n_kv, d)).astype(np.float32))
+    new_v = wl.round_to_bf16_bits(rng.standard_normal((S, n_kv, d)).astype(np.float32))
+    kk, vv = k, v
+    for s in range(S):
+        last = int(tables[s, -1])
+        if refs[last] > 1:  # shared: copy before writing
+            mine = free.pop(0)
+            kk, vv = oracle.copy_blocks(kk, vv, kk, vv, [(last, mine)])
+            refs[last] -= 1
+            refs[mine] = 1
+            tables[s, -1] = mine
+        kk, vv = oracle.cache_write(kk, vv, new_k[s:s + 1], new_v[s:s + 1],
+                                    np.array([int(tables[s, -1]) * 16 + prompt % 16], np.int64))
+    assert len(refs) == 66 and sum(1 for c in refs.values() if c == S) == 62
+    assert refs[n_blocks - 1] == 1  # the last writer kept the original block
+    lens = np.full(S, prompt + 1, np.int32)
+    q = wl.round_to_bf16_bits(rng.standard_normal((S, 2, d)).astype(np.float32))
+    got = oracle.paged_decode(q, kk, vv, tables, lens, 0.25, 1, "bf16")
+    K0 = oracle.to_f64(k.reshape(-1, n_kv, d)[:prompt, 0], "bf16")
+    V0 = oracle.to_f64(v.reshape(-1, n_kv, d)[:prompt, 0], "bf16")
+    for s in range(S):
+        K = np.concatenate([K0, oracle.to_f64(new_k[s, 0], "bf16")[None]])
+        V = np.concatenate([V0, oracle.to_f64(new_v[s, 0], "bf16")[None]])
+        for h in range(2):
+            sc = 0.25 * (K @ oracle.to_f64(q[s, h], "bf16"))
+            w = np.exp(sc - sc.max())
+            np.testing.assert_allclose(got[s, h], (w / w.sum()) @ V, rtol=0, atol=1e-12)
