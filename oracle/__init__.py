@@ -35,9 +35,16 @@ What it computes, and which passage each step follows:
   blocks as raw bytes (learn.mohebi.ai, section 3.5; arunshar.com, section
   18.2.2).
 
+* Tree-mask verify (oracle/tree.py): the candidates of a draft tree are
+  scored in one pass, each node seeing the context and its own path to the
+  root ("Chapter 18: Speculative Decoding and Serving Optimizations",
+  arunshar.com, section 18.1.2; "07 - Inference", lourdhu02.github.io,
+  section 3.4).
+
 Parity of individual output elements is pinned by the tests in
-tests/test_oracle.py and tests/test_oracle_fp8.py (brute-force SDPA, closed
-forms, torch's float8 type, invariants).
+tests/test_oracle.py, tests/test_oracle_fp8.py, tests/test_oracle_blocks.py
+and tests/test_oracle_tree.py (brute-force SDPA, closed forms, torch's float8
+type, the pages' worked figures, invariants).
 """
 
 from .attention import (  # noqa: F401
@@ -65,3 +72,4 @@ from .fp8 import (  # noqa: F401
     paged_decode_fp8_rows,
     quantize,
 )
+from .tree import paged_tree_decode, paged_tree_decode_rows, path_to_root, visible_positions  # noqa: F401

@@ -118,6 +118,7 @@ class Spec:
     pad: str = "valid"  # block-table padding: "valid" random in-range ids | "garbage"
     poison: bool = False  # NaN in cache rows never read (unused blocks, rows >= L)
     kv: str = "same"  # cache element type: "same" as dtype | "fp8" (E4M3 codes with per-head scales; dtype bf16)
+    tree: str = ""  # q_len > 1: "" causal chain | "binary" complete binary tree (heap numbering) | "random"
     description: str = ""
 
     @property
@@ -162,7 +163,16 @@ CONFIGS = {
 
 CONFIG_ORDER = ["tiny-f32", "llama3-8b-decode", "llama3-70b-decode", "long-split", "spec-verify"]
 
-# Beyond the five workloads: the Llama-3-8B-shaped layer over an fp8 (E4M3) cache
+# Beyond the five workloads: tree verify on the Llama-3-8B-shaped layer (Medusa's
+# 15-node complete binary tree, branching 2 over 4 levels, under a tree mask)
+CONFIGS["tree-verify"] = Spec(
+    name="tree-verify", dtype="bf16", num_seqs=128, num_q_heads=32, num_kv_heads=8, head_dim=128,
+    lens=("uniform", 1024, 4096), max_len=4096, q_len=15, tree="binary", shared_prefix_blocks=32,
+    write_new_tokens=True, seed=5,
+    description="tree verify: a 15-node complete binary tree of candidates per sequence under a tree mask, 32/8 "
+                "heads, d=128, bf16, batch 128, L~U[1024,4096], 32 shared prefix blocks, 1920 new tokens written")
+
+# the Llama-3-8B-shaped layer over an fp8 (E4M3) cache
 CONFIGS["llama3-8b-decode-fp8kv"] = CONFIGS["llama3-8b-decode"].with_(
     name="llama3-8b-decode-fp8kv", kv="fp8",
     description="the llama3-8b-decode layer with an fp8 (E4M3) KV cache, per-head scales, 64 new tokens quantized "
@@ -187,6 +197,7 @@ class Problem:
     slot_mapping: Optional[np.ndarray] = None  # int64 [T]
     k_scale: Optional[np.ndarray] = None  # fp8 caches: float32 [n_kv]
     v_scale: Optional[np.ndarray] = None
+    parents: Optional[np.ndarray] = None  # tree verify: int32 [S, q_len], parents[b, j] in [-1, j)
     extra: dict = field(default_factory=dict)
 
     # convenience views of the spec
@@ -272,6 +283,28 @@ def to_fp8_codes(bits_bf16: np.ndarray, scale: np.ndarray) -> np.ndarray:
     return (x / s).clamp_(-448.0, 448.0).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
 
 
+def tree_parents(spec: Spec) -> Optional[np.ndarray]:
+    """Parent arrays [S, q_len] of a tree-verify workload (None for the causal chain).
+
+    "binary": node j's parent is (j - 1) // 2, the root -1 (heap numbering);
+    "random": node j >= 1 hangs on a uniformly drawn earlier node, node 0 and,
+    with probability 1/8, any later node on the context (a forest)."""
+    if not spec.tree:
+        return None
+    S, T = spec.num_seqs, spec.q_len
+    if spec.tree == "binary":
+        row = np.array([-1] + [(j - 1) // 2 for j in range(1, T)], dtype=np.int32)
+        return np.tile(row, (S, 1))
+    if spec.tree == "random":
+        rng = np.random.default_rng((spec.seed, 7001))
+        par = np.full((S, T), -1, dtype=np.int32)
+        for j in range(1, T):
+            par[:, j] = rng.integers(0, j, size=S)
+            par[rng.random(S) < 0.125, j] = -1
+        return par
+    raise ValueError(f"unknown tree {spec.tree!r}")
+
+
 def make_problem(spec: Spec) -> Problem:
     """Draw every input of one workload from spec.seed."""
     if isinstance(spec, str):
@@ -340,7 +373,7 @@ def make_problem(spec: Spec) -> Problem:
 
     scale = np.float32(1.0 / math.sqrt(d)) if spec.scale is None else np.float32(spec.scale)
     return Problem(spec=spec, context_lens=lens, block_tables=tables, q=q, k_cache=k_cache, v_cache=v_cache,
-                   scale=scale, new_k=new_k, new_v=new_v, slot_mapping=slots)
+                   scale=scale, new_k=new_k, new_v=new_v, slot_mapping=slots, parents=tree_parents(spec))
 
 
 def poison_unread(spec: Spec, lens, tables, k_cache, v_cache) -> None:
