@@ -48,6 +48,7 @@ LAUNCH = {
     "llama3-70b-decode": -1,
     "spec-verify": 0,
     "llama3-8b-decode-fp8kv": -1,
+    "tree-verify": 0,
 }
 
 
@@ -64,7 +65,8 @@ def decode_kernel_name(p: wl.Problem, partition: int) -> str:
     kind = "decode_mfma_kernel" if fp8 or (p.dtype == "bf16" and rows >= 8) else "decode_valu_kernel"
     mode = "balanced" if partition < 0 else ("partitions" if partition > 0 else "one pass")
     kv = "fp8 E4M3 KV, bf16 q" if fp8 else p.dtype
-    return f"{kind} ({kv}, head_dim {p.head_dim}, {rows} rows per KV head, {mode})"
+    mask = f", tree mask over {p.q_len} nodes" if p.parents is not None else ""
+    return f"{kind} ({kv}, head_dim {p.head_dim}, {rows} rows per KV head{mask}, {mode})"
 
 
 def kernel_source_hash() -> str:
@@ -101,6 +103,7 @@ class Resident:
         if self.fp8:
             self.k_scale = torch.from_numpy(p.k_scale).cuda()
             self.v_scale = torch.from_numpy(p.v_scale).cuda()
+        self.parents = torch.from_numpy(p.parents).cuda() if p.parents is not None else None
         self.out = torch.empty_like(self.q)
         self.ws = None
         if partition:
@@ -116,6 +119,10 @@ class Resident:
 
     def decode(self):
         p = self.p
+        if self.parents is not None:
+            self.pa.decode_tree(self.q, self.k_cache, self.v_cache, self.tables, self.lens, self.parents,
+                                float(p.scale), self.partition, out=self.out, workspace=self.ws)
+            return
         if self.fp8:
             self.pa.decode_fp8(self.q, self.k_cache, self.v_cache, self.k_scale, self.v_scale, self.tables, self.lens,
                                float(p.scale), p.q_len, self.partition, out=self.out, workspace=self.ws)
@@ -171,7 +178,10 @@ def cpu_baseline(p: wl.Problem, gpu_out, budget_s: float = 10.0):
     while n < p.num_seqs or time.perf_counter() - t0 < budget_s:
         b = n % p.num_seqs
         rows = [(b, j, h) for j in range(p.q_len) for h in range(p.num_q_heads)]
-        if fp8:
+        if p.parents is not None:
+            ref = oracle.paged_tree_decode_rows(p.q, kc, vc, p.block_tables, p.context_lens, p.parents, p.scale,
+                                                p.dtype, rows)
+        elif fp8:
             ref = oracle.paged_decode_fp8_rows(p.q, kc, vc, p.k_scale, p.v_scale, p.block_tables, p.context_lens,
                                                p.scale, p.q_len, p.dtype, rows)
         else:
@@ -400,6 +410,8 @@ def main(argv=None):
             "new_tokens_written": 0 if p.slot_mapping is None else int(len(p.slot_mapping)),
             "partition_size": partition, "seed": spec.seed,
             "kv_cache": "fp8 E4M3, per-head scales" if p.spec.kv == "fp8" else p.dtype,
+            "mask": "tree (" + p.spec.tree + f", {p.q_len} nodes)" if p.parents is not None
+            else ("causal" if p.q_len > 1 else "none"),
         },
         "kv_hbm_gbps_step": round(kv_bytes / (ms_per_step / 1e3) / 1e9, 1),
         "breakdown_us": {"cache_write": round(write_ms * 1e3, 2), "decode": round(decode_ms * 1e3, 2),

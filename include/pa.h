@@ -1,7 +1,7 @@
 /*
  * pa.h - paged KV-cache decode attention for AMD Instinct MI355X (gfx950).
  *
- * A C ABI over hand-written HIP kernels.  Three operations:
+ * A C ABI over hand-written HIP kernels.  Operations:
  *
  *   pa_cache_write  store the K/V rows of new tokens into their cache slots;
  *   pa_decode       attention of the newest q_len tokens of every sequence over
@@ -11,6 +11,7 @@
  *   pa_cache_write_fp8, pa_decode_fp8
  *                   the same over a KV cache of fp8 (E4M3) codes with one
  *                   scale per KV head;
+ *   pa_decode_tree  verify a tree of draft tokens under a tree mask;
  *   pa_copy_blocks  copy whole blocks (copy-on-write, swapping).
  *
  * Sources of the definitions (the web pages this library implements):
@@ -35,7 +36,13 @@
  *     in higher precision, halving the KV bytes read per step
  *     (learn.mohebi.ai, section 3.7, the table of quantization schemes); E4M3,
  *     largest magnitude 448, is the fp8 format for inference, with per-tensor,
- *     per-channel or per-block scales (lourdhu02.github.io, section 4.3).
+ *     per-channel or per-block scales (lourdhu02.github.io, section 4.3);
+ *   - tree verification: the candidates of a draft tree are checked in one
+ *     pass under a tree attention mask ("Chapter 18: Speculative Decoding
+ *     and Serving Optimizations", arunshar.com, section 18.1.2;
+ *     lourdhu02.github.io, section 3.4);
+ *   - copy-on-write of shared blocks and swapping of paused sequences
+ *     (learn.mohebi.ai, section 3.5; arunshar.com, section 18.2.2).
  *
  * Conventions shared by every entry point:
  *   - Every data pointer is a DEVICE pointer owned by the caller.  The library
@@ -181,7 +188,8 @@ size_t pa_decode_workspace_size(int32_t num_seqs, int32_t q_len, int32_t num_q_h
 /*
  * pa_reduce - merge the per-partition partials of a split pa_decode into out.
  *
- * The arguments must repeat those of the pa_decode call that filled the
+ * The arguments must repeat those of the pa_decode (pa_decode_fp8,
+ * pa_decode_tree with q_len = tree_size, up to 64) call that filled the
  * workspace (same shapes, partition_size, context_lens), on the same stream or
  * after it.  For each query row: M = max over partitions of m_p,
  * w_p = l_p * 2^(m_p - M), out = sum_p w_p * o_p / sum_p w_p, over the
@@ -239,6 +247,42 @@ pa_status pa_decode_fp8(void* out, const void* q, const void* k_cache, const voi
                         int32_t head_dim, int32_t num_blocks, int32_t block_size, int32_t max_blocks_per_seq,
                         int32_t partition_size, void* workspace, size_t workspace_bytes, pa_dtype dtype,
                         void* stream);
+
+/*
+ * pa_decode_tree - verify a tree of draft tokens in one pass (tree attention).
+ *
+ * Speculative decoding with several candidates per position checks them as a
+ * tree in a single forward pass of the target model, e.g. a complete binary
+ * tree of 15 nodes over 4 levels ("Chapter 18: Speculative Decoding and
+ * Serving Optimizations", arunshar.com, section 18.1.2, tree-based
+ * verification for Medusa), under a tree attention mask ("07 - Inference",
+ * lourdhu02.github.io, section 3.4).
+ *
+ *   tree_size     T = 1 .. 64 nodes per sequence; they take the place of the
+ *                 q_len new tokens of pa_decode: node j of sequence b is query
+ *                 row b * T + j, its key and value are already in the cache at
+ *                 position L_b - T + j, and context_lens counts the T nodes.
+ *   tree_parents  int32 [num_seqs, T] device array: the parent node of node j,
+ *                 an earlier node (0 <= parent < j), or -1 for a node that
+ *                 hangs directly on the context (a root; several roots form a
+ *                 forest).  Node j attends to every position before the tree
+ *                 and to the nodes on its own path to the root, itself
+ *                 included; never to its siblings or other branches.  A chain
+ *                 (parent j - 1) gives pa_decode's causal verify.  A parent
+ *                 outside [-1, j) ends the node's path there, as -1 does.
+ *   dtype         PA_BF16 (q, out and the caches); rows per KV head
+ *                 (num_q_heads / num_kv_heads) * T up to 64.  Runs on the
+ *                 matrix cores like bf16 pa_decode with 8 or more rows.
+ *
+ * Every other argument, the workspace, the partition modes, PA_BALANCED and
+ * pa_reduce (called with q_len = T) are those of pa_decode.
+ */
+pa_status pa_decode_tree(void* out, const void* q, const void* k_cache, const void* v_cache,
+                         const int32_t* block_tables, const int32_t* context_lens, const int32_t* tree_parents,
+                         float scale, int32_t tree_size, int32_t num_seqs, int32_t num_q_heads,
+                         int32_t num_kv_heads, int32_t head_dim, int32_t num_blocks, int32_t block_size,
+                         int32_t max_blocks_per_seq, int32_t partition_size, void* workspace,
+                         size_t workspace_bytes, pa_dtype dtype, void* stream);
 
 /*
  * pa_copy_blocks - copy whole KV blocks, for copy-on-write and swapping.

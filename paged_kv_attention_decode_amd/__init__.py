@@ -24,14 +24,14 @@ from typing import Optional
 __all__ = [
     "PA_F32", "PA_BF16", "PA_BALANCED", "PagedAttentionError", "library_path", "load_library", "status_string", "version",
     "cache_write", "decode", "reduce", "decode_workspace_size", "paged_attention", "cache_write_fp8", "decode_fp8",
-    "copy_blocks", "SYMBOLS",
+    "decode_tree", "copy_blocks", "SYMBOLS",
 ]
 
 PA_F32, PA_BF16 = 0, 1
 PA_BALANCED = -1  # partition_size selecting the work-balanced decode
 BLOCK_SIZE = 16
 SYMBOLS = ("pa_cache_write", "pa_decode", "pa_decode_workspace_size", "pa_reduce", "pa_status_string", "pa_version",
-           "pa_cache_write_fp8", "pa_decode_fp8", "pa_copy_blocks")
+           "pa_cache_write_fp8", "pa_decode_fp8", "pa_decode_tree", "pa_copy_blocks")
 _STATUS = {0: "PA_OK", 1: "PA_ERR_NULL", 2: "PA_ERR_SHAPE", 3: "PA_ERR_UNSUPPORTED", 4: "PA_ERR_WORKSPACE",
            5: "PA_ERR_HIP", 6: "PA_ERR_MEMORY"}
 
@@ -73,6 +73,9 @@ def load_library():
     lib.pa_decode_fp8.restype = ctypes.c_int
     lib.pa_decode_fp8.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, f32, i32, i32, i32, i32, i32, i32, i32, i32, i32,
                                   vp, sz, ctypes.c_int, vp]
+    lib.pa_decode_tree.restype = ctypes.c_int
+    lib.pa_decode_tree.argtypes = [vp, vp, vp, vp, vp, vp, vp, f32, i32, i32, i32, i32, i32, i32, i32, i32, i32,
+                                   vp, sz, ctypes.c_int, vp]
     lib.pa_copy_blocks.restype = ctypes.c_int
     lib.pa_copy_blocks.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, ctypes.c_int64, vp]
     lib.pa_status_string.restype = ctypes.c_char_p
@@ -310,6 +313,47 @@ def decode_fp8(q, k_cache, v_cache, k_scale, v_scale, block_tables, context_lens
     st = load_library().pa_decode_fp8(pout, *args, float(scale), q_len, S, n_h, n_kv, d, NB, bs, MB, partition_size,
                                       pws, nws, PA_BF16, _stream(stream))
     _check(st, "pa_decode_fp8")
+    return out if partition_size <= 0 else workspace
+
+
+# ---------------------------------------------------------------------------
+# tree verify
+
+
+def decode_tree(q, k_cache, v_cache, block_tables, context_lens, parents, scale: float, partition_size: int = 0,
+                out=None, workspace=None, stream=None):
+    """pa_decode_tree: T = parents.shape[1] draft-tree nodes per sequence (q is [S*T, n_h, d],
+    bf16), parents int32 [S, T] on the GPU (an earlier node, or -1 for a root).  Same
+    partition_size / workspace / return conventions as decode(), with q_len = T."""
+    torch = _torch()
+    pp = _dev(parents, "parents", torch.int32, 2)
+    T = parents.shape[1]
+    S = _decode_shapes(q, k_cache, block_tables, context_lens, T)
+    if parents.shape[0] != S:
+        raise ValueError("parents must be [num_seqs, tree_size]")
+    n_h, d = q.shape[1], q.shape[2]
+    NB, bs, n_kv = k_cache.shape[0], k_cache.shape[1], k_cache.shape[2]
+    MB = block_tables.shape[1]
+    if v_cache.shape != k_cache.shape:
+        raise ValueError("k_cache and v_cache must have the same shape")
+    args = (_dev(q, "q", torch.bfloat16, 3), _dev(k_cache, "k_cache", torch.bfloat16, 4),
+            _dev(v_cache, "v_cache", torch.bfloat16, 4), _dev(block_tables, "block_tables", torch.int32, 2),
+            _dev(context_lens, "context_lens", torch.int32, 1), pp)
+    pws, nws = None, 0
+    if partition_size != 0:
+        if workspace is None:
+            workspace = new_workspace(q, k_cache, block_tables, T, partition_size)
+        pws, nws = _dev(workspace, "workspace", torch.uint8, 1), workspace.numel()
+    pout = None
+    if partition_size <= 0:
+        if out is None:
+            out = torch.empty_like(q)
+        if out.shape != q.shape:
+            raise ValueError("out must have q's shape")
+        pout = _dev(out, "out", q.dtype, 3)
+    st = load_library().pa_decode_tree(pout, *args, float(scale), T, S, n_h, n_kv, d, NB, bs, MB, partition_size,
+                                       pws, nws, PA_BF16, _stream(stream))
+    _check(st, "pa_decode_tree")
     return out if partition_size <= 0 else workspace
 
 

@@ -30,6 +30,16 @@
 // rounded to bf16 (v_cvt_pk_bf16_f32) for the P V product and the row sums
 // add the same rounded weights, so numerator and denominator agree.  The waves
 // of a workgroup merge one after the other into a single LDS tile.
+//
+// TREE: the q_len new tokens are the nodes of a draft tree checked in one pass
+// ("Chapter 18: Speculative Decoding and Serving Optimizations", arunshar.com,
+// section 18.1.2, tree-based verification for Medusa; "07 - Inference",
+// section 3.4, the tree attention mask).  Node j sits at position
+// L - q_len + j and sees every position before the tree and the nodes on its
+// own path to the root, given by a parent array (parent < node, -1 at a
+// root).  Each row builds that path as a 64-bit node mask once per range; a
+// score then survives when its position is before the tree or its node's bit
+// is set.
 #include "pa_device.h"
 #include "pa_kernels.h"
 #include "pa_schedule.h"
@@ -62,6 +72,8 @@ struct MergeTile {
   // row is padded by 16 bytes so the 16 rows one read touches fall in different
   // banks
   uint16_t q[R][D + 8];
+  // tree verify: bit i of path[r] is set when node i is on row r's path to the root
+  uint64_t path[R];
 };
 
 // fp8 (E4M3) code pair (bytes 0-1, or 2-3 when HIGH) -> bf16 pair, exact:
@@ -83,7 +95,7 @@ __device__ __forceinline__ uint32_t fp8x2_to_bf16x2(uint32_t codes) {
 //       pairs of the P V B operand.
 // The K scale of the head multiplies the score scale and the V scale the
 // normalized output, exact refactorings of scale * q . (s_k k) and sum p (s_v v).
-template <int D, int NT, int NW, int NBUF, bool KV8>
+template <int D, int NT, int NW, int NBUF, bool KV8, bool TREE>
 struct MfmaAttender {
   static constexpr int kThreads = NW * 64;
   static constexpr int kD = D;
@@ -134,12 +146,35 @@ struct MfmaAttender {
             qp + (((size_t)b * a.q_len + r / a.group) * a.n_h + (size_t)g * a.group + r % a.group) * D + 8 * c8);
       *reinterpret_cast<uint4*>(&sm.q[r][8 * c8]) = v;
     }
+    if constexpr (TREE) {
+      // row r's path to the root: walk the parents while they point to an
+      // earlier node (at most q_len - 1 steps)
+      for (int r = threadIdx.x; r < R; r += kThreads) {
+        uint64_t m = 0;
+        if (r < rows) {
+          const int32_t* __restrict__ par = a.parents + (size_t)b * a.q_len;
+          int cur = r / a.group;
+          m = 1ull << cur;
+          for (int it = 0; it < 64; ++it) {
+            const int pp = par[cur];
+            if (pp < 0 || pp >= cur) break;
+            m |= 1ull << pp;
+            cur = pp;
+          }
+        }
+        sm.path[r] = m;
+      }
+    }
     __syncthreads();
-    int vis[NT];  // positions row 16 t + j may see
+    // causal: row 16 t + j sees positions below vis[t]; tree: the context
+    // positions below vis[t] (the tree's start, 0 for padding rows) and the
+    // nodes of its path (sm.path)
+    int vis[NT];
+    const int tree_base = L - a.q_len;  // tree: position of node 0
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
       const int r = 16 * t + j;
-      vis[t] = r < rows ? L - a.q_len + r / a.group + 1 : 0;
+      vis[t] = r < rows ? (TREE ? tree_base : L - a.q_len + r / a.group + 1) : 0;
     }
 
     float m_ref[NT], m_use[NT], lsum[NT];
@@ -232,8 +267,20 @@ struct MfmaAttender {
           x = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, k_operand(kb, ks)),
                                                       __builtin_bit_cast(bf16x8_t, qb), x, 0, 0, 0);
         }
+        if constexpr (TREE) {
+          uint64_t path = 0;
+          if (lblk * kBlockTokens + kBlockTokens > tree_base)  // the block reaches into the tree (wave-uniform)
+            path = sm.path[16 * t + j];
 #pragma unroll
-        for (int v = 0; v < 4; ++v) s[t][v] = (ok && pos0 + v < vis[t]) ? x[v] * scale_log2 : kNegInf;
+          for (int v = 0; v < 4; ++v) {
+            const int rel = pos0 + v - tree_base;  // node index of the position, negative before the tree
+            const bool see = pos0 + v < vis[t] || (rel >= 0 && rel < 64 && ((path >> rel) & 1ull));
+            s[t][v] = (ok && see) ? x[v] * scale_log2 : kNegInf;
+          }
+        } else {
+#pragma unroll
+          for (int v = 0; v < 4; ++v) s[t][v] = (ok && pos0 + v < vis[t]) ? x[v] * scale_log2 : kNegInf;
+        }
       }
     };
 
@@ -437,43 +484,45 @@ struct MfmaAttender {
   }
 };
 
-template <int D, int NT, int NW, int NBUF, bool BALANCED, bool KV8>
+template <int D, int NT, int NW, int NBUF, bool BALANCED, bool KV8, bool TREE>
 // Up to three row tiles the kernel is asked for two waves per SIMD: without
 // the bound the allocator keeps values hoisted out of a balanced range's loop
 // over sequences and lands at one wave per SIMD, while with it everything fits
-// without spilling (four tiles would spill, so they keep one wave).
-__global__ __launch_bounds__(NW * 64, NT <= 3 ? 2 : 1) void decode_mfma_kernel(DecodeParams a) {
+// without spilling.  Four tiles fit two waves too with one block in flight in
+// the fixed schedules; the balanced one would spill, so it keeps one wave.
+__global__ __launch_bounds__(NW * 64, (NT <= 3 || !BALANCED) ? 2 : 1) void decode_mfma_kernel(DecodeParams a) {
   __shared__ MergeTile<16 * NT, D> sm;
-  MfmaAttender<D, NT, NW, NBUF, KV8> at(a, sm);
+  MfmaAttender<D, NT, NW, NBUF, KV8, TREE> at(a, sm);
   if constexpr (BALANCED) drive_balanced(a, at);
   else drive_fixed(a, at);
 }
 
-template <int D, int NT, bool KV8>
+template <int D, int NT, bool KV8, bool TREE>
 hipError_t launch_tiles(const DecodeParams& p, hipStream_t s) {
-  constexpr int NB = NT >= 3 ? 2 : 3;  // blocks in flight per wave, fixed schedules
+  constexpr int NB = NT >= 4 ? 1 : (NT >= 3 ? 2 : 3);  // blocks in flight per wave, fixed schedules
   if (p.mode == kBalanced) {
     // one block in flight per wave, as in the vector-ALU kernel: cheaper
     // pipeline restarts at the sequences a range crosses (70B layer: 221 us
     // against 239 us with three)
-    static const int resident = resident_per_cu(decode_mfma_kernel<D, NT, kWaves, 1, true, KV8>, kWaves * 64);
+    static const int resident =
+        resident_per_cu(decode_mfma_kernel<D, NT, kWaves, 1, true, KV8, TREE>, kWaves * 64);
     DecodeParams q = p;
     q.num_wgs = balanced_workgroups(resident, p.n_kv);
-    hipLaunchKernelGGL((decode_mfma_kernel<D, NT, kWaves, 1, true, KV8>), dim3(q.num_wgs), dim3(kWaves * 64), 0, s,
-                       q);
+    hipLaunchKernelGGL((decode_mfma_kernel<D, NT, kWaves, 1, true, KV8, TREE>), dim3(q.num_wgs), dim3(kWaves * 64),
+                       0, s, q);
   } else {
     dim3 grid(p.mode == kPartitions ? p.num_parts : 1, p.n_kv, p.num_seqs);
-    hipLaunchKernelGGL((decode_mfma_kernel<D, NT, kWaves, NB, false, KV8>), grid, dim3(kWaves * 64), 0, s, p);
+    hipLaunchKernelGGL((decode_mfma_kernel<D, NT, kWaves, NB, false, KV8, TREE>), grid, dim3(kWaves * 64), 0, s, p);
   }
   return hipGetLastError();
 }
 
-template <int D, bool KV8>
+template <int D, bool KV8, bool TREE = false>
 hipError_t launch_rows(const DecodeParams& p, int rows, hipStream_t s) {
-  if (rows <= 16) return launch_tiles<D, 1, KV8>(p, s);
-  if (rows <= 32) return launch_tiles<D, 2, KV8>(p, s);
-  if (rows <= 48) return launch_tiles<D, 3, KV8>(p, s);
-  return launch_tiles<D, 4, KV8>(p, s);
+  if (rows <= 16) return launch_tiles<D, 1, KV8, TREE>(p, s);
+  if (rows <= 32) return launch_tiles<D, 2, KV8, TREE>(p, s);
+  if (rows <= 48) return launch_tiles<D, 3, KV8, TREE>(p, s);
+  return launch_tiles<D, 4, KV8, TREE>(p, s);
 }
 
 }  // namespace
@@ -484,6 +533,11 @@ hipError_t launch_decode_mfma(const DecodeParams& p, int head_dim, int rows_per_
 
 hipError_t launch_decode_mfma_fp8(const DecodeParams& p, int head_dim, int rows_per_kv, hipStream_t s) {
   return head_dim == 64 ? launch_rows<64, true>(p, rows_per_kv, s) : launch_rows<128, true>(p, rows_per_kv, s);
+}
+
+hipError_t launch_decode_mfma_tree(const DecodeParams& p, int head_dim, int rows_per_kv, hipStream_t s) {
+  return head_dim == 64 ? launch_rows<64, false, true>(p, rows_per_kv, s)
+                        : launch_rows<128, false, true>(p, rows_per_kv, s);
 }
 
 }  // namespace pa

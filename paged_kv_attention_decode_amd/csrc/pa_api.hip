@@ -13,6 +13,8 @@ constexpr size_t kAlign = 256;
 constexpr int kMaxRowsF32 = 8;
 constexpr int kMaxRowsBF16 = 64;
 constexpr int kMaxRowsValu = 8;  // the vector-ALU kernel's limit
+constexpr int kMaxQLen = 8;       // new tokens per sequence, causal
+constexpr int kMaxTreeNodes = 64; // tree nodes per sequence (one bit each in a row's path mask)
 // bf16 with at least this many rows per KV head runs on the matrix cores
 #ifndef PA_MFMA_MIN_ROWS
 #define PA_MFMA_MIN_ROWS 8
@@ -195,17 +197,18 @@ size_t pa_decode_workspace_size(int32_t num_seqs, int32_t q_len, int32_t num_q_h
 
 namespace {
 
-// pa_decode and pa_decode_fp8: validation, workspace, schedule and launch
+// pa_decode, pa_decode_fp8 and pa_decode_tree: validation, workspace, schedule and launch
 pa_status decode_impl(void* out, const void* q, const void* k_cache, const void* v_cache, const float* k_scale,
-                      const float* v_scale, bool fp8, const int32_t* block_tables, const int32_t* context_lens,
-                      float scale, int32_t q_len, int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
-                      int32_t head_dim, int32_t num_blocks, int32_t block_size, int32_t max_blocks_per_seq,
-                      int32_t partition_size, void* workspace, size_t workspace_bytes, pa_dtype dtype,
-                      void* stream) {
+                      const float* v_scale, bool fp8, bool tree, const int32_t* parents,
+                      const int32_t* block_tables, const int32_t* context_lens, float scale, int32_t q_len,
+                      int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                      int32_t num_blocks, int32_t block_size, int32_t max_blocks_per_seq, int32_t partition_size,
+                      void* workspace, size_t workspace_bytes, pa_dtype dtype, void* stream) {
   if (dtype != PA_F32 && dtype != PA_BF16) return PA_ERR_UNSUPPORTED;
-  if (fp8 && dtype != PA_BF16) return PA_ERR_UNSUPPORTED;
+  if ((fp8 || tree) && dtype != PA_BF16) return PA_ERR_UNSUPPORTED;
   if (block_size != kBlock || (head_dim != 64 && head_dim != 128)) return PA_ERR_UNSUPPORTED;
-  if (num_seqs < 0 || q_len < 1 || q_len > 8 || num_q_heads <= 0 || num_kv_heads <= 0 ||
+  if (num_seqs < 0 || q_len < 1 || q_len > (tree ? kMaxTreeNodes : kMaxQLen) || num_q_heads <= 0 ||
+      num_kv_heads <= 0 ||
       num_q_heads % num_kv_heads != 0 || num_blocks <= 0 || max_blocks_per_seq <= 0 ||
       (partition_size < 0 && partition_size != PA_BALANCED) || (partition_size > 0 && partition_size % kBlock != 0))
     return PA_ERR_SHAPE;
@@ -218,6 +221,7 @@ pa_status decode_impl(void* out, const void* q, const void* k_cache, const void*
   const bool balanced = partition_size == PA_BALANCED;
   if (!q || !k_cache || !v_cache || !block_tables || !context_lens || (!split && !out)) return PA_ERR_NULL;
   if (fp8 && (!k_scale || !v_scale)) return PA_ERR_NULL;
+  if (tree && !parents) return PA_ERR_NULL;
   if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || (out && !aligned16(out))) return PA_ERR_SHAPE;
 
   pa::DecodeParams p = {};
@@ -227,6 +231,7 @@ pa_status decode_impl(void* out, const void* q, const void* k_cache, const void*
   p.v_cache = v_cache;
   p.k_scale = k_scale;
   p.v_scale = v_scale;
+  p.parents = tree ? parents : nullptr;
   p.tables = block_tables;
   p.lens = context_lens;
   p.scale_log2 = (float)((double)scale * 1.4426950408889634);
@@ -264,6 +269,7 @@ pa_status decode_impl(void* out, const void* q, const void* k_cache, const void*
   }
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (fp8) return from_hip(pa::launch_decode_mfma_fp8(p, head_dim, rows, s));
+  if (tree) return from_hip(pa::launch_decode_mfma_tree(p, head_dim, rows, s));
   if (dtype == PA_BF16 && rows >= kMfmaMinRows) return from_hip(pa::launch_decode_mfma(p, head_dim, rows, s));
   return from_hip(pa::launch_decode_valu(p, dtype == PA_F32 ? pa::kF32 : pa::kBF16, head_dim, rows, s));
 }
@@ -275,9 +281,20 @@ pa_status pa_decode(void* out, const void* q, const void* k_cache, const void* v
                     int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
                     int32_t num_blocks, int32_t block_size, int32_t max_blocks_per_seq, int32_t partition_size,
                     void* workspace, size_t workspace_bytes, pa_dtype dtype, void* stream) {
-  return decode_impl(out, q, k_cache, v_cache, nullptr, nullptr, false, block_tables, context_lens, scale, q_len,
-                     num_seqs, num_q_heads, num_kv_heads, head_dim, num_blocks, block_size, max_blocks_per_seq,
-                     partition_size, workspace, workspace_bytes, dtype, stream);
+  return decode_impl(out, q, k_cache, v_cache, nullptr, nullptr, false, false, nullptr, block_tables, context_lens,
+                     scale, q_len, num_seqs, num_q_heads, num_kv_heads, head_dim, num_blocks, block_size,
+                     max_blocks_per_seq, partition_size, workspace, workspace_bytes, dtype, stream);
+}
+
+pa_status pa_decode_tree(void* out, const void* q, const void* k_cache, const void* v_cache,
+                         const int32_t* block_tables, const int32_t* context_lens, const int32_t* tree_parents,
+                         float scale, int32_t tree_size, int32_t num_seqs, int32_t num_q_heads,
+                         int32_t num_kv_heads, int32_t head_dim, int32_t num_blocks, int32_t block_size,
+                         int32_t max_blocks_per_seq, int32_t partition_size, void* workspace,
+                         size_t workspace_bytes, pa_dtype dtype, void* stream) {
+  return decode_impl(out, q, k_cache, v_cache, nullptr, nullptr, false, true, tree_parents, block_tables,
+                     context_lens, scale, tree_size, num_seqs, num_q_heads, num_kv_heads, head_dim, num_blocks,
+                     block_size, max_blocks_per_seq, partition_size, workspace, workspace_bytes, dtype, stream);
 }
 
 pa_status pa_decode_fp8(void* out, const void* q, const void* k_cache, const void* v_cache, const float* k_scale,
@@ -286,9 +303,9 @@ pa_status pa_decode_fp8(void* out, const void* q, const void* k_cache, const voi
                         int32_t head_dim, int32_t num_blocks, int32_t block_size, int32_t max_blocks_per_seq,
                         int32_t partition_size, void* workspace, size_t workspace_bytes, pa_dtype dtype,
                         void* stream) {
-  return decode_impl(out, q, k_cache, v_cache, k_scale, v_scale, true, block_tables, context_lens, scale, q_len,
-                     num_seqs, num_q_heads, num_kv_heads, head_dim, num_blocks, block_size, max_blocks_per_seq,
-                     partition_size, workspace, workspace_bytes, dtype, stream);
+  return decode_impl(out, q, k_cache, v_cache, k_scale, v_scale, true, false, nullptr, block_tables, context_lens,
+                     scale, q_len, num_seqs, num_q_heads, num_kv_heads, head_dim, num_blocks, block_size,
+                     max_blocks_per_seq, partition_size, workspace, workspace_bytes, dtype, stream);
 }
 
 pa_status pa_reduce(void* out, const void* workspace, size_t workspace_bytes, const int32_t* context_lens,
@@ -297,7 +314,7 @@ pa_status pa_reduce(void* out, const void* workspace, size_t workspace_bytes, co
                     void* stream) {
   if (dtype != PA_F32 && dtype != PA_BF16) return PA_ERR_UNSUPPORTED;
   if (block_size != kBlock || (head_dim != 64 && head_dim != 128)) return PA_ERR_UNSUPPORTED;
-  if (num_seqs < 0 || q_len < 1 || q_len > 8 || num_q_heads <= 0 || max_blocks_per_seq <= 0 ||
+  if (num_seqs < 0 || q_len < 1 || q_len > kMaxTreeNodes || num_q_heads <= 0 || max_blocks_per_seq <= 0 ||
       partition_size <= 0 || partition_size % kBlock != 0)
     return PA_ERR_SHAPE;
   if (num_seqs == 0) return PA_OK;

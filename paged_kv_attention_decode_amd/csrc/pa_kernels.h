@@ -65,6 +65,7 @@ struct DecodeParams {
   float* pieces;         // balanced: [2 * num_wgs][rows_per_kv][D + 2] partial (m, l, o) per row
   const float* k_scale;  // fp8 caches: [n_kv] per-head scales (null otherwise)
   const float* v_scale;
+  const int32_t* parents;  // tree verify: [S, q_len] parent of each node (null: causal among the new tokens)
   float scale_log2;      // softmax scale * log2(e)
   int q_len, group, n_h, n_kv, num_blocks, max_blocks;
   int mode;              // DecodeMode
@@ -120,6 +121,7 @@ struct CopyBlocksParams {
 hipError_t launch_decode_valu(const DecodeParams& p, ElemType t, int head_dim, int rows_per_kv, hipStream_t s);
 hipError_t launch_decode_mfma(const DecodeParams& p, int head_dim, int rows_per_kv, hipStream_t s);
 hipError_t launch_decode_mfma_fp8(const DecodeParams& p, int head_dim, int rows_per_kv, hipStream_t s);
+hipError_t launch_decode_mfma_tree(const DecodeParams& p, int head_dim, int rows_per_kv, hipStream_t s);
 hipError_t launch_reduce(const ReduceParams& p, ElemType t, int head_dim, hipStream_t s);
 hipError_t launch_cache_write(const CacheWriteParams& p, hipStream_t s);
 hipError_t launch_cache_write_fp8(const CacheWriteFp8Params& p, hipStream_t s);

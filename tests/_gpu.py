@@ -79,6 +79,7 @@ class DeviceProblem:
         if self.fp8:
             self.k_scale = torch.from_numpy(p.k_scale).to(device)
             self.v_scale = torch.from_numpy(p.v_scale).to(device)
+        self.parents = None if p.parents is None else torch.from_numpy(p.parents).to(device)
         self.out = torch.empty_like(self.q)
         self.workspace = None
 
@@ -95,6 +96,9 @@ class DeviceProblem:
                 pa.cache_write(self.new_k, self.new_v, self.k_cache, self.v_cache, self.slots)
 
         def dec(ps, out=None, workspace=None):
+            if self.parents is not None:
+                return pa.decode_tree(self.q, self.k_cache, self.v_cache, self.block_tables, self.context_lens,
+                                      self.parents, float(p.scale), ps, out=out, workspace=workspace)
             if self.fp8:
                 return pa.decode_fp8(self.q, self.k_cache, self.v_cache, self.k_scale, self.v_scale, self.block_tables,
                                      self.context_lens, float(p.scale), p.q_len, ps, out=out, workspace=workspace)
@@ -129,6 +133,9 @@ def reference_rows(p: wl.Problem, rows, kc=None, vc=None):
 
     if kc is None:
         kc, vc = host_caches_after_write(p)
+    if p.parents is not None:
+        return oracle.paged_tree_decode_rows(p.q, kc, vc, p.block_tables, p.context_lens, p.parents, p.scale, p.dtype,
+                                             rows)
     if p.spec.kv == "fp8":
         return oracle.paged_decode_fp8_rows(p.q, kc, vc, p.k_scale, p.v_scale, p.block_tables, p.context_lens,
                                             p.scale, p.q_len, p.dtype, rows)

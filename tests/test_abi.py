@@ -131,6 +131,32 @@ def test_decode_fp8_rejects_invalid_arguments(lib):
     assert _decode_fp8(lib, S=0, q=None, out=None) == 0
 
 
+def _decode_tree(lib, **kw):
+    a = dict(out=FAKE, q=FAKE, kc=FAKE, vc=FAKE, bt=FAKE, cl=FAKE, par=FAKE, scale=0.1, T=15, S=2, n_h=4, n_kv=1,
+             d=128, NB=16, bs=16, MB=3, ps=0, ws=None, wsb=0, dt=pa.PA_BF16, stream=None)
+    a.update(kw)
+    return lib.pa_decode_tree(a["out"], a["q"], a["kc"], a["vc"], a["bt"], a["cl"], a["par"], a["scale"], a["T"],
+                              a["S"], a["n_h"], a["n_kv"], a["d"], a["NB"], a["bs"], a["MB"], a["ps"], a["ws"],
+                              a["wsb"], a["dt"], a["stream"])
+
+
+def test_decode_tree_rejects_invalid_arguments(lib):
+    assert _decode_tree(lib, dt=pa.PA_F32) == 3          # bf16 only
+    assert _decode_tree(lib, par=None) == 1              # the tree is required
+    assert _decode_tree(lib, T=65, n_h=1) == 2           # at most 64 nodes
+    assert _decode_tree(lib, T=0) == 2
+    assert _decode_tree(lib, T=17, n_h=4) == 3           # 68 rows per KV head
+    assert _decode_tree(lib, d=96) == 3
+    assert _decode_tree(lib, ps=-1, ws=None) == 4
+    assert _decode_tree(lib, S=0, q=None, out=None) == 0
+
+
+def test_reduce_accepts_tree_sized_q_len_only_up_to_64(lib):
+    f = lib.pa_reduce
+    assert f(FAKE, FAKE, 8, FAKE, 2, 64, 4, 64, 3, 16, 32, pa.PA_BF16, None) == 4      # q_len 64 valid: workspace small
+    assert f(FAKE, FAKE, 1 << 30, FAKE, 2, 65, 4, 64, 3, 16, 32, pa.PA_BF16, None) == 2
+
+
 def test_copy_blocks_rejects_invalid_arguments(lib):
     f = lib.pa_copy_blocks
     assert f(FAKE, FAKE, FAKE, FAKE, FAKE, 3, 16, 16, 8, None) == 2       # block bytes not a multiple of 16
