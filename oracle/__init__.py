@@ -41,9 +41,16 @@ What it computes, and which passage each step follows:
   arunshar.com, section 18.1.2; "07 - Inference", lourdhu02.github.io,
   section 3.4).
 
+* Chunked prefill (oracle/prefill.py): sequences with different numbers of
+  new tokens in one call, each new token seeing the cached prefix and the
+  earlier new tokens ("Chapter 18: Speculative Decoding and Serving
+  Optimizations", arunshar.com, section 18.2.1; "LLM serving: KV cache,
+  batching, paged attention and quantization", learn.mohebi.ai, section 3.6;
+  "07 - Inference", lourdhu02.github.io, section 2.4).
+
 Parity of individual output elements is pinned by the tests in
 tests/test_oracle.py, tests/test_oracle_fp8.py, tests/test_oracle_blocks.py
-and tests/test_oracle_tree.py (brute-force SDPA, closed forms, torch's float8
+tests/test_oracle_tree.py and tests/test_oracle_prefill.py (brute-force SDPA, closed forms, torch's float8
 type, the pages' worked figures, invariants).
 """
 
@@ -73,3 +80,4 @@ from .fp8 import (  # noqa: F401
     quantize,
 )
 from .tree import paged_tree_decode, paged_tree_decode_rows, path_to_root, visible_positions  # noqa: F401
+from .prefill import paged_prefill, paged_prefill_rows, query_counts, query_row, visible_count  # noqa: F401

@@ -119,6 +119,8 @@ class Spec:
     poison: bool = False  # NaN in cache rows never read (unused blocks, rows >= L)
     kv: str = "same"  # cache element type: "same" as dtype | "fp8" (E4M3 codes with per-head scales; dtype bf16)
     tree: str = ""  # q_len > 1: "" causal chain | "binary" complete binary tree (heap numbering) | "random"
+    # prefill: new tokens per sequence, () -> q_len each | ("fixed", (n_0, ...)) | ("chunk", C) -> min(C, L_b)
+    new_tokens: tuple = ()
     description: str = ""
 
     @property
@@ -172,6 +174,15 @@ CONFIGS["tree-verify"] = Spec(
     description="tree verify: a 15-node complete binary tree of candidates per sequence under a tree mask, 32/8 "
                 "heads, d=128, bf16, batch 128, L~U[1024,4096], 32 shared prefix blocks, 1920 new tokens written")
 
+# chunked prefill on the Llama-3-8B-shaped layer: a 2,048-token step budget of four
+# 512-token prompt chunks, each at a different depth of its prompt
+CONFIGS["chunked-prefill"] = Spec(
+    name="chunked-prefill", dtype="bf16", num_seqs=4, num_q_heads=32, num_kv_heads=8, head_dim=128,
+    lens=("chunks", 512, 16), max_len=8192, new_tokens=("chunk", 512), write_new_tokens=True, seed=6,
+    description="chunked prefill: 4 prompt chunks of 512 tokens (a 2,048-token step), chunk k of its prompt "
+                "(k ~ U{0..15}) over a cache of 512 k earlier tokens, causal within the chunk, 32/8 heads, d=128, "
+                "bf16, the chunks' K/V written first")
+
 # the Llama-3-8B-shaped layer over an fp8 (E4M3) cache
 CONFIGS["llama3-8b-decode-fp8kv"] = CONFIGS["llama3-8b-decode"].with_(
     name="llama3-8b-decode-fp8kv", kv="fp8",
@@ -198,6 +209,7 @@ class Problem:
     k_scale: Optional[np.ndarray] = None  # fp8 caches: float32 [n_kv]
     v_scale: Optional[np.ndarray] = None
     parents: Optional[np.ndarray] = None  # tree verify: int32 [S, q_len], parents[b, j] in [-1, j)
+    query_start: Optional[np.ndarray] = None  # prefill: int32 [S + 1], sequence b owns q rows qs[b] .. qs[b+1]-1
     extra: dict = field(default_factory=dict)
 
     # convenience views of the spec
@@ -237,6 +249,13 @@ class Problem:
     def partition_size(self) -> int:
         return self.spec.partition_size
 
+    @property
+    def q_counts(self) -> np.ndarray:
+        """New tokens (query rows per head) of each sequence."""
+        if self.query_start is not None:
+            return (self.query_start[1:] - self.query_start[:-1]).astype(np.int64)
+        return np.full(self.num_seqs, self.q_len, dtype=np.int64)
+
     def as_float32(self, a: np.ndarray) -> np.ndarray:
         return a if self.dtype == "f32" else bf16_bits_to_f32(a)
 
@@ -251,6 +270,9 @@ def draw_lens(spec: Spec, rng: np.random.Generator) -> np.ndarray:
     elif kind == "uniform":
         lo, hi = spec.lens[1], spec.lens[2]
         lens = rng.integers(lo, hi, size=S, endpoint=True)
+    elif kind == "chunks":
+        chunk, max_chunks = spec.lens[1], spec.lens[2]
+        lens = chunk * (rng.integers(0, max_chunks, size=S) + 1)
     elif kind == "lognormal":
         mu, sigma, lo, hi = spec.lens[1:5]
         lens = np.clip(np.rint(rng.lognormal(mu, sigma, size=S)), lo, hi).astype(np.int64)
@@ -305,6 +327,21 @@ def tree_parents(spec: Spec) -> Optional[np.ndarray]:
     raise ValueError(f"unknown tree {spec.tree!r}")
 
 
+def new_token_counts(spec: Spec, lens: np.ndarray) -> np.ndarray:
+    """New tokens of each sequence: q_len each, or the prefill spec's counts."""
+    S = spec.num_seqs
+    if not spec.new_tokens:
+        return np.full(S, spec.q_len, dtype=np.int64)
+    kind = spec.new_tokens[0]
+    if kind == "fixed":
+        counts = np.asarray(spec.new_tokens[1], dtype=np.int64)
+        assert counts.size == S, "fixed new_tokens must list one count per sequence"
+        return counts
+    if kind == "chunk":
+        return np.minimum(np.int64(spec.new_tokens[1]), lens.astype(np.int64))
+    raise ValueError(f"unknown new_tokens {kind!r}")
+
+
 def make_problem(spec: Spec) -> Problem:
     """Draw every input of one workload from spec.seed."""
     if isinstance(spec, str):
@@ -323,11 +360,12 @@ def make_problem(spec: Spec) -> Problem:
     rng = np.random.default_rng(spec.seed)
     S, bs = spec.num_seqs, BLOCK_SIZE
     lens = draw_lens(spec, rng)
-    assert lens.min() >= spec.q_len, "every context must hold its q_len newest tokens"
+    counts = new_token_counts(spec, lens)
+    assert (lens >= counts).all(), "every context must hold its newest tokens"
     nblk = (lens.astype(np.int64) + bs - 1) // bs
     shared = spec.shared_prefix_blocks
     if shared:
-        assert (lens.astype(np.int64) - spec.q_len).min() >= shared * bs, "new tokens must land past the shared prefix"
+        assert (lens.astype(np.int64) - counts).min() >= shared * bs, "new tokens must land past the shared prefix"
     private = nblk - shared
     if spec.num_blocks is None:
         NB = shared + int(math.ceil(1.25 * float(private.sum())))
@@ -353,27 +391,29 @@ def make_problem(spec: Spec) -> Problem:
         cursor += n
 
     n_kv, d = spec.num_kv_heads, spec.head_dim
-    q = fill_normal((S * spec.q_len, spec.num_q_heads, d), spec.dtype, spec.seed, _STREAM_Q)
+    starts = np.concatenate([[0], np.cumsum(counts)]).astype(np.int64)
+    q = fill_normal((int(starts[-1]), spec.num_q_heads, d), spec.dtype, spec.seed, _STREAM_Q)
     k_cache = fill_normal((NB, bs, n_kv, d), spec.dtype, spec.seed, _STREAM_K)
     v_cache = fill_normal((NB, bs, n_kv, d), spec.dtype, spec.seed, _STREAM_V)
 
     new_k = new_v = slots = None
     if spec.write_new_tokens:
-        T = S * spec.q_len
+        T = int(starts[-1])
         new_k = fill_normal((T, n_kv, d), spec.dtype, spec.seed, _STREAM_NEWK)
         new_v = fill_normal((T, n_kv, d), spec.dtype, spec.seed, _STREAM_NEWV)
         slots = np.empty(T, dtype=np.int64)
         for b in range(S):
-            for j in range(spec.q_len):
-                pos = int(lens[b]) - spec.q_len + j
-                slots[b * spec.q_len + j] = int(tables[b, pos // bs]) * bs + pos % bs
+            for j in range(int(counts[b])):
+                pos = int(lens[b]) - int(counts[b]) + j
+                slots[starts[b] + j] = int(tables[b, pos // bs]) * bs + pos % bs
 
     if spec.poison:
         poison_unread(spec, lens, tables, k_cache, v_cache)
 
     scale = np.float32(1.0 / math.sqrt(d)) if spec.scale is None else np.float32(spec.scale)
     return Problem(spec=spec, context_lens=lens, block_tables=tables, q=q, k_cache=k_cache, v_cache=v_cache,
-                   scale=scale, new_k=new_k, new_v=new_v, slot_mapping=slots, parents=tree_parents(spec))
+                   scale=scale, new_k=new_k, new_v=new_v, slot_mapping=slots, parents=tree_parents(spec),
+                   query_start=starts.astype(np.int32) if spec.new_tokens else None)
 
 
 def poison_unread(spec: Spec, lens, tables, k_cache, v_cache) -> None:
@@ -430,14 +470,26 @@ def algorithmic_bytes(problem: Problem) -> dict:
     logical_tokens = int(problem.context_lens.astype(np.int64).sum())
     shared_tokens = problem.spec.shared_prefix_blocks * BLOCK_SIZE
     unique_tokens = logical_tokens - max(0, problem.num_seqs - 1) * shared_tokens if shared_tokens else logical_tokens
-    q_bytes = problem.num_seqs * problem.q_len * problem.num_q_heads * problem.head_dim * esz
+    n_q = int(problem.q_counts.sum())
+    q_bytes = n_q * problem.num_q_heads * problem.head_dim * esz
     return {
         "kv_logical": 2 * logical_tokens * row,
         "kv_unique": 2 * unique_tokens * row,
         "q": q_bytes,
         "out": q_bytes,
-        "tokens": problem.num_seqs * problem.q_len,
+        "tokens": n_q,
     }
+
+
+def attention_flops(problem: Problem) -> int:
+    """Multiply-adds x 2 of the visible (query row, position) pairs: q.k and p.v, 2 d flops each.
+
+    New token i of sequence b sees L_b - n_b + i + 1 positions (at least 0)."""
+    total = 0
+    for L, n in zip(problem.context_lens.astype(np.int64), problem.q_counts):
+        i = np.arange(int(n), dtype=np.int64)
+        total += int(np.maximum(int(L) - int(n) + i + 1, 0).sum())
+    return total * problem.num_q_heads * 4 * problem.head_dim
 
 
 def kv_bytes_per_token(layers: int, kv_heads: int, head_dim: int, bytes_per_value: int) -> int:
