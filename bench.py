@@ -36,7 +36,10 @@ import workloads as wl  # noqa: E402
 HBM_PEAK_GBPS = 8000.0
 DEFAULT_CONFIG = "llama3-8b-decode"
 METRIC = "decode tokens/s and achieved KV HBM GB/s (% of MI355X peak) per pa_decode call"
+PREFILL_METRIC = "prefill tokens/s and attention TFLOP/s (% of MI355X bf16 matrix peak) per pa_prefill call"
 KERNEL_SOURCES = ("decode_valu.hip", "decode_mfma.hip", "pa_schedule.h", "pa_kernels.h", "pa_device.h")
+PREFILL_SOURCES = ("prefill.hip", "pa_prefill.h", "pa_device.h")
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak
 
 # Context split per workload, the fastest measured on MI355X (kernel trace):
 # one pass where every (sequence, KV head) already gives two workgroups per CU,
@@ -60,6 +63,9 @@ def partition_for(p: wl.Problem) -> int:
 
 
 def decode_kernel_name(p: wl.Problem, partition: int) -> str:
+    if p.query_start is not None:
+        return (f"prefill_kernel (bf16, head_dim {p.head_dim}, {p.spec.group} query heads per KV head, "
+                f"up to {int(p.q_counts.max())} new tokens per sequence, 128 query rows per workgroup)")
     rows = p.spec.group * p.q_len
     fp8 = p.spec.kv == "fp8"
     kind = "decode_mfma_kernel" if fp8 or (p.dtype == "bf16" and rows >= 8) else "decode_valu_kernel"
@@ -69,9 +75,9 @@ def decode_kernel_name(p: wl.Problem, partition: int) -> str:
     return f"{kind} ({kv}, head_dim {p.head_dim}, {rows} rows per KV head{mask}, {mode})"
 
 
-def kernel_source_hash() -> str:
+def kernel_source_hash(sources=KERNEL_SOURCES) -> str:
     h = hashlib.sha256()
-    for f in KERNEL_SOURCES:
+    for f in sources:
         with open(os.path.join(ROOT, "paged_kv_attention_decode_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
@@ -104,6 +110,8 @@ class Resident:
             self.k_scale = torch.from_numpy(p.k_scale).cuda()
             self.v_scale = torch.from_numpy(p.v_scale).cuda()
         self.parents = torch.from_numpy(p.parents).cuda() if p.parents is not None else None
+        self.query_start = torch.from_numpy(p.query_start).cuda() if p.query_start is not None else None
+        self.max_q_len = int(p.q_counts.max())
         self.out = torch.empty_like(self.q)
         self.ws = None
         if partition:
@@ -119,6 +127,10 @@ class Resident:
 
     def decode(self):
         p = self.p
+        if self.query_start is not None:
+            self.pa.prefill(self.q, self.k_cache, self.v_cache, self.tables, self.lens, self.query_start,
+                            float(p.scale), self.max_q_len, out=self.out)
+            return
         if self.parents is not None:
             self.pa.decode_tree(self.q, self.k_cache, self.v_cache, self.tables, self.lens, self.parents,
                                 float(p.scale), self.partition, out=self.out, workspace=self.ws)
@@ -141,15 +153,16 @@ class Resident:
         self.reduce()
 
 
-def load_traffic(workload: str, decode_s: float):
-    """HBM traffic of the decode kernel from the committed counter summary, if it
+def load_traffic(workload: str, decode_s: float, sources=KERNEL_SOURCES):
+    """HBM traffic of the attention kernel from the committed counter summary, if it
     was taken on the current kernel sources."""
-    path = os.path.join(ROOT, "profiles", f"decode_traffic_{workload}.json")
+    kind = "prefill" if sources is PREFILL_SOURCES else "decode"
+    path = os.path.join(ROOT, "profiles", f"{kind}_traffic_{workload}.json")
     if not os.path.exists(path):
         return None, None
     with open(path) as f:
         t = json.load(f)
-    if t.get("kernel_source_sha") != kernel_source_hash():
+    if t.get("kernel_source_sha") != kernel_source_hash(sources):
         return None, "kernel changed since the counters were taken"
     per_launch = float(t["fetch_bytes_per_launch"]) + float(t["write_bytes_per_launch"])
     return per_launch / decode_s / 1e9, per_launch
@@ -177,8 +190,11 @@ def cpu_baseline(p: wl.Problem, gpu_out, budget_s: float = 10.0):
     t0 = time.perf_counter()
     while n < p.num_seqs or time.perf_counter() - t0 < budget_s:
         b = n % p.num_seqs
-        rows = [(b, j, h) for j in range(p.q_len) for h in range(p.num_q_heads)]
-        if p.parents is not None:
+        rows = [(b, j, h) for j in range(int(p.q_counts[b])) for h in range(p.num_q_heads)]
+        if p.query_start is not None:
+            ref = oracle.paged_prefill_rows(p.q, kc, vc, p.block_tables, p.context_lens, p.query_start, p.scale,
+                                            p.dtype, rows)
+        elif p.parents is not None:
             ref = oracle.paged_tree_decode_rows(p.q, kc, vc, p.block_tables, p.context_lens, p.parents, p.scale,
                                                 p.dtype, rows)
         elif fp8:
@@ -187,8 +203,9 @@ def cpu_baseline(p: wl.Problem, gpu_out, budget_s: float = 10.0):
         else:
             ref = oracle.paged_decode_rows(p.q, kc, vc, p.block_tables, p.context_lens, p.scale, p.q_len, p.dtype,
                                            rows)
-        if gpu_out is not None and n < p.num_seqs:
-            got = np.stack([gpu_out[b * p.q_len + j, h] for (_, j, h) in rows])
+        if gpu_out is not None and n < p.num_seqs and rows:
+            r0 = int(p.query_start[b]) if p.query_start is not None else b * p.q_len
+            got = np.stack([gpu_out[r0 + j, h] for (_, j, h) in rows])
             worst = max(worst, float(np.max(np.abs(got - ref))))
         n += 1
         if n >= p.num_seqs and time.perf_counter() - t0 >= budget_s:
@@ -197,13 +214,14 @@ def cpu_baseline(p: wl.Problem, gpu_out, budget_s: float = 10.0):
     est = t_write + t_attn * p.num_seqs / n
     threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
     return {
-        "value": p.num_seqs * p.q_len / est,
+        "value": int(p.q_counts.sum()) / est,
         "unit": "tokens/s",
         "cores": int(threads),
         "kind": "oracle",
         "sample": (f"fp64 NumPy oracle on the same workload: cache write of all "
                    f"{len(p.slot_mapping) if p.slot_mapping is not None else 0} new tokens ({t_write:.2f} s), then "
-                   f"attention of {n} sequences x {p.num_q_heads} heads x {p.q_len} query tokens, cycling over the "
+                   f"attention of {n} sequences x {p.num_q_heads} heads x their new tokens "
+                   f"({int(p.q_counts.sum())} in the batch), cycling over the "
                    f"batch of {p.num_seqs} ({t_attn:.2f} s); tokens/s of whole steps"),
         "max_abs_vs_gpu": worst,
     }
@@ -377,21 +395,34 @@ def main(argv=None):
     kv_bytes = ab["kv_unique"] + ab["q"]
     tokens = ab["tokens"]
     decode_s = decode_ms / 1e3
-    achieved = kv_bytes / decode_s / 1e9
-    traffic, traffic_bytes = load_traffic(args.config, decode_s)
-    roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-            "frac": round(achieved / HBM_PEAK_GBPS, 4),
-            "traffic": round(traffic, 1) if isinstance(traffic, float) else None,
-            "kernel": decode_kernel_name(p, partition),
-            "algorithmic_bytes_per_launch": kv_bytes,
-            "avg_launch_us": round(decode_ms * 1e3, 2)}
+    if p.query_start is not None:  # chunked prefill: dense products, rated on the matrix cores
+        flops = wl.attention_flops(p)
+        achieved = flops / decode_s / 1e12
+        traffic, traffic_bytes = load_traffic(args.config, decode_s, PREFILL_SOURCES)
+        roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4),
+                "traffic": round(traffic, 1) if isinstance(traffic, float) else None,
+                "traffic_unit": "GB/s",
+                "kernel": decode_kernel_name(p, partition),
+                "algorithmic_flops_per_launch": flops,
+                "algorithmic_bytes_per_launch": kv_bytes + ab["out"],
+                "avg_launch_us": round(decode_ms * 1e3, 2)}
+    else:
+        achieved = kv_bytes / decode_s / 1e9
+        traffic, traffic_bytes = load_traffic(args.config, decode_s)
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                "traffic": round(traffic, 1) if isinstance(traffic, float) else None,
+                "kernel": decode_kernel_name(p, partition),
+                "algorithmic_bytes_per_launch": kv_bytes,
+                "avg_launch_us": round(decode_ms * 1e3, 2)}
     if isinstance(traffic_bytes, str):
         roof["traffic_note"] = traffic_bytes
     elif traffic_bytes is not None:
         roof["traffic_bytes_per_launch"] = traffic_bytes
 
     res = {
-        "metric": METRIC,
+        "metric": METRIC if p.query_start is None else PREFILL_METRIC,
         "value": round(tokens / (ms_per_step / 1e3), 1),
         "unit": "tokens/s",
         "n_gpus": 1,
@@ -405,13 +436,15 @@ def main(argv=None):
         "data": "synthetic",
         "config": {
             "workload": args.config, "num_seqs": p.num_seqs, "num_q_heads": p.num_q_heads,
-            "num_kv_heads": p.num_kv_heads, "head_dim": p.head_dim, "block_size": 16, "q_len": p.q_len,
+            "num_kv_heads": p.num_kv_heads, "head_dim": p.head_dim, "block_size": 16,
+            "q_len": p.q_len if p.query_start is None else "per sequence",
+            **({"new_tokens_per_seq": [int(x) for x in p.q_counts]} if p.query_start is not None else {}),
             "context_tokens": int(p.context_lens.sum()), "num_blocks": p.num_blocks,
             "new_tokens_written": 0 if p.slot_mapping is None else int(len(p.slot_mapping)),
             "partition_size": partition, "seed": spec.seed,
             "kv_cache": "fp8 E4M3, per-head scales" if p.spec.kv == "fp8" else p.dtype,
             "mask": "tree (" + p.spec.tree + f", {p.q_len} nodes)" if p.parents is not None
-            else ("causal" if p.q_len > 1 else "none"),
+            else ("causal" if int(p.q_counts.max()) > 1 else "none"),
         },
         "kv_hbm_gbps_step": round(kv_bytes / (ms_per_step / 1e3) / 1e9, 1),
         "breakdown_us": {"cache_write": round(write_ms * 1e3, 2), "decode": round(decode_ms * 1e3, 2),

@@ -12,6 +12,7 @@
  *                   the same over a KV cache of fp8 (E4M3) codes with one
  *                   scale per KV head;
  *   pa_decode_tree  verify a tree of draft tokens under a tree mask;
+ *   pa_prefill      chunked prefill: new tokens of varying count per sequence;
  *   pa_copy_blocks  copy whole blocks (copy-on-write, swapping).
  *
  * Sources of the definitions (the web pages this library implements):
@@ -41,6 +42,9 @@
  *     pass under a tree attention mask ("Chapter 18: Speculative Decoding
  *     and Serving Optimizations", arunshar.com, section 18.1.2;
  *     lourdhu02.github.io, section 3.4);
+ *   - chunked prefill: a long prompt processed in chunks over several steps,
+ *     each chunk attending to the cached prefix (arunshar.com, section
+ *     18.2.1; learn.mohebi.ai, section 3.6; lourdhu02.github.io, section 2.4);
  *   - copy-on-write of shared blocks and swapping of paused sequences
  *     (learn.mohebi.ai, section 3.5; arunshar.com, section 18.2.2).
  *
@@ -283,6 +287,48 @@ pa_status pa_decode_tree(void* out, const void* q, const void* k_cache, const vo
                          int32_t num_kv_heads, int32_t head_dim, int32_t num_blocks, int32_t block_size,
                          int32_t max_blocks_per_seq, int32_t partition_size, void* workspace,
                          size_t workspace_bytes, pa_dtype dtype, void* stream);
+
+/*
+ * pa_prefill - attention of the new tokens of sequences with different
+ * numbers of them: chunked prefill, optionally mixed with decode tokens.
+ *
+ * A long prompt is processed in chunks (for example 512 tokens) over several
+ * engine steps, a step filling a token budget with decode tokens and prefill
+ * chunks ("Chapter 18: Speculative Decoding and Serving Optimizations",
+ * arunshar.com, section 18.2.1; "LLM serving: KV cache, batching, paged
+ * attention and quantization", learn.mohebi.ai, section 3.6; "07 -
+ * Inference", lourdhu02.github.io, section 2.4).  Each new token attends to
+ * every cached token before it and to the earlier new tokens of its sequence,
+ * so a prompt run in chunks gives the same result as in one piece.
+ *
+ *   out, q        [num_q_tokens, num_q_heads, head_dim] bf16.  Sequence b owns
+ *                 rows query_start[b] .. query_start[b + 1] - 1, its n_b new
+ *                 tokens in order.
+ *   k_cache,      [num_blocks, block_size, num_kv_heads, head_dim] bf16, with
+ *   v_cache       the new tokens' K/V already written (pa_cache_write).
+ *   block_tables, as for pa_decode; context_lens[b] = L_b counts the n_b new
+ *   context_lens  tokens: new token i sits at position L_b - n_b + i and sees
+ *                 positions 0 .. L_b - n_b + i.  A row with no visible position
+ *                 (L_b < n_b) gets zeros.
+ *   query_start   int32 [num_seqs + 1] device array, nondecreasing, from 0 to
+ *                 num_q_tokens.  A sequence with n_b = 0 is skipped; one whose
+ *                 range is negative, longer than max_q_len or outside
+ *                 [0, num_q_tokens) is skipped too, its rows left untouched.
+ *   max_q_len     an upper bound of every n_b (1 .. 2^20); sizes the grid.
+ *   dtype         PA_BF16.  head_dim 64 or 128, block_size 16.
+ *
+ * Each workgroup owns 128 query rows (new token x query head of one KV head's
+ * group) and walks the sequence's blocks up to the last position those rows
+ * see, staging each block once in LDS for its four waves; the products run on
+ * the matrix cores with fp32 accumulation, the softmax weights rounded to bf16
+ * for P V as in pa_decode.  No workspace; results are bitwise deterministic
+ * and do not depend on the other sequences of the call.
+ */
+pa_status pa_prefill(void* out, const void* q, const void* k_cache, const void* v_cache,
+                     const int32_t* block_tables, const int32_t* context_lens, const int32_t* query_start,
+                     float scale, int32_t num_seqs, int32_t num_q_tokens, int32_t max_q_len, int32_t num_q_heads,
+                     int32_t num_kv_heads, int32_t head_dim, int32_t num_blocks, int32_t block_size,
+                     int32_t max_blocks_per_seq, pa_dtype dtype, void* stream);
 
 /*
  * pa_copy_blocks - copy whole KV blocks, for copy-on-write and swapping.

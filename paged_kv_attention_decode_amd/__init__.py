@@ -24,14 +24,14 @@ from typing import Optional
 __all__ = [
     "PA_F32", "PA_BF16", "PA_BALANCED", "PagedAttentionError", "library_path", "load_library", "status_string", "version",
     "cache_write", "decode", "reduce", "decode_workspace_size", "paged_attention", "cache_write_fp8", "decode_fp8",
-    "decode_tree", "copy_blocks", "SYMBOLS",
+    "decode_tree", "prefill", "copy_blocks", "SYMBOLS",
 ]
 
 PA_F32, PA_BF16 = 0, 1
 PA_BALANCED = -1  # partition_size selecting the work-balanced decode
 BLOCK_SIZE = 16
 SYMBOLS = ("pa_cache_write", "pa_decode", "pa_decode_workspace_size", "pa_reduce", "pa_status_string", "pa_version",
-           "pa_cache_write_fp8", "pa_decode_fp8", "pa_decode_tree", "pa_copy_blocks")
+           "pa_cache_write_fp8", "pa_decode_fp8", "pa_decode_tree", "pa_prefill", "pa_copy_blocks")
 _STATUS = {0: "PA_OK", 1: "PA_ERR_NULL", 2: "PA_ERR_SHAPE", 3: "PA_ERR_UNSUPPORTED", 4: "PA_ERR_WORKSPACE",
            5: "PA_ERR_HIP", 6: "PA_ERR_MEMORY"}
 
@@ -76,6 +76,9 @@ def load_library():
     lib.pa_decode_tree.restype = ctypes.c_int
     lib.pa_decode_tree.argtypes = [vp, vp, vp, vp, vp, vp, vp, f32, i32, i32, i32, i32, i32, i32, i32, i32, i32,
                                    vp, sz, ctypes.c_int, vp]
+    lib.pa_prefill.restype = ctypes.c_int
+    lib.pa_prefill.argtypes = [vp, vp, vp, vp, vp, vp, vp, f32, i32, i32, i32, i32, i32, i32, i32, i32, i32,
+                               ctypes.c_int, vp]
     lib.pa_copy_blocks.restype = ctypes.c_int
     lib.pa_copy_blocks.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, ctypes.c_int64, vp]
     lib.pa_status_string.restype = ctypes.c_char_p
@@ -355,6 +358,39 @@ def decode_tree(q, k_cache, v_cache, block_tables, context_lens, parents, scale:
                                        pws, nws, PA_BF16, _stream(stream))
     _check(st, "pa_decode_tree")
     return out if partition_size <= 0 else workspace
+
+
+# ---------------------------------------------------------------------------
+# chunked prefill
+
+
+def prefill(q, k_cache, v_cache, block_tables, context_lens, query_start, scale: float, max_q_len: int,
+            out=None, stream=None):
+    """pa_prefill: sequence b owns q rows query_start[b] .. query_start[b+1]-1 (int32 [S+1] on the
+    GPU), its new tokens at the last positions of its context; bf16.  max_q_len bounds every
+    sequence's count (a host-side figure: the binding does not read query_start back)."""
+    torch = _torch()
+    if q.dim() != 3 or k_cache.dim() != 4 or v_cache.shape != k_cache.shape:
+        raise ValueError("q must be [tokens, n_h, d] and the caches [num_blocks, block_size, n_kv, d]")
+    S = block_tables.shape[0]
+    if query_start.shape != (S + 1,) or context_lens.shape != (S,):
+        raise ValueError("query_start must be [num_seqs + 1] and context_lens [num_seqs]")
+    n_h, d = q.shape[1], q.shape[2]
+    NB, bs, n_kv = k_cache.shape[0], k_cache.shape[1], k_cache.shape[2]
+    if out is None:
+        out = torch.empty_like(q)
+    if out.shape != q.shape:
+        raise ValueError("out must have q's shape")
+    st = load_library().pa_prefill(_dev(out, "out", torch.bfloat16, 3), _dev(q, "q", torch.bfloat16, 3),
+                                   _dev(k_cache, "k_cache", torch.bfloat16, 4),
+                                   _dev(v_cache, "v_cache", torch.bfloat16, 4),
+                                   _dev(block_tables, "block_tables", torch.int32, 2),
+                                   _dev(context_lens, "context_lens", torch.int32, 1),
+                                   _dev(query_start, "query_start", torch.int32, 1), float(scale), S, q.shape[0],
+                                   int(max_q_len), n_h, n_kv, d, NB, bs, block_tables.shape[1], PA_BF16,
+                                   _stream(stream))
+    _check(st, "pa_prefill")
+    return out
 
 
 # ---------------------------------------------------------------------------

@@ -5,6 +5,7 @@
 #include <hip/hip_runtime.h>
 
 #include "pa_kernels.h"
+#include "pa_prefill.h"
 
 namespace {
 
@@ -15,6 +16,7 @@ constexpr int kMaxRowsBF16 = 64;
 constexpr int kMaxRowsValu = 8;  // the vector-ALU kernel's limit
 constexpr int kMaxQLen = 8;       // new tokens per sequence, causal
 constexpr int kMaxTreeNodes = 64; // tree nodes per sequence (one bit each in a row's path mask)
+constexpr int kMaxPrefillTokens = 1 << 20;  // new tokens of one sequence in one pa_prefill call
 // bf16 with at least this many rows per KV head runs on the matrix cores
 #ifndef PA_MFMA_MIN_ROWS
 #define PA_MFMA_MIN_ROWS 8
@@ -306,6 +308,41 @@ pa_status pa_decode_fp8(void* out, const void* q, const void* k_cache, const voi
   return decode_impl(out, q, k_cache, v_cache, k_scale, v_scale, true, false, nullptr, block_tables, context_lens,
                      scale, q_len, num_seqs, num_q_heads, num_kv_heads, head_dim, num_blocks, block_size,
                      max_blocks_per_seq, partition_size, workspace, workspace_bytes, dtype, stream);
+}
+
+pa_status pa_prefill(void* out, const void* q, const void* k_cache, const void* v_cache,
+                     const int32_t* block_tables, const int32_t* context_lens, const int32_t* query_start,
+                     float scale, int32_t num_seqs, int32_t num_q_tokens, int32_t max_q_len, int32_t num_q_heads,
+                     int32_t num_kv_heads, int32_t head_dim, int32_t num_blocks, int32_t block_size,
+                     int32_t max_blocks_per_seq, pa_dtype dtype, void* stream) {
+  if (dtype != PA_BF16) return PA_ERR_UNSUPPORTED;
+  if (block_size != kBlock || (head_dim != 64 && head_dim != 128)) return PA_ERR_UNSUPPORTED;
+  if (num_seqs < 0 || num_q_tokens < 0 || max_q_len < 0 || num_q_heads <= 0 || num_kv_heads <= 0 ||
+      num_q_heads % num_kv_heads != 0 || num_blocks <= 0 || max_blocks_per_seq <= 0)
+    return PA_ERR_SHAPE;
+  if (num_seqs > 65535 || num_kv_heads > 65535 || max_q_len > kMaxPrefillTokens) return PA_ERR_UNSUPPORTED;
+  if ((long long)max_blocks_per_seq * kBlock > 0x7fffffffLL) return PA_ERR_SHAPE;
+  if (num_seqs == 0 || num_q_tokens == 0 || max_q_len == 0) return PA_OK;
+  if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens || !query_start) return PA_ERR_NULL;
+  if (!aligned16(out) || !aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache)) return PA_ERR_SHAPE;
+  pa::PrefillParams p;
+  p.out = out;
+  p.q = q;
+  p.k_cache = k_cache;
+  p.v_cache = v_cache;
+  p.tables = block_tables;
+  p.lens = context_lens;
+  p.qstart = query_start;
+  p.scale_log2 = (float)((double)scale * 1.4426950408889634);
+  p.group = num_q_heads / num_kv_heads;
+  p.n_h = num_q_heads;
+  p.n_kv = num_kv_heads;
+  p.num_blocks = num_blocks;
+  p.max_blocks = max_blocks_per_seq;
+  p.max_q_len = max_q_len;
+  p.num_q_tokens = num_q_tokens;
+  p.num_seqs = num_seqs;
+  return from_hip(pa::launch_prefill(p, head_dim, static_cast<hipStream_t>(stream)));
 }
 
 pa_status pa_reduce(void* out, const void* workspace, size_t workspace_bytes, const int32_t* context_lens,

@@ -157,6 +157,26 @@ def test_reduce_accepts_tree_sized_q_len_only_up_to_64(lib):
     assert f(FAKE, FAKE, 1 << 30, FAKE, 2, 65, 4, 64, 3, 16, 32, pa.PA_BF16, None) == 2
 
 
+def _prefill(lib, **kw):
+    a = dict(out=FAKE, q=FAKE, kc=FAKE, vc=FAKE, bt=FAKE, cl=FAKE, qs=FAKE, scale=0.1, S=2, T=600, mq=512, n_h=32,
+             n_kv=8, d=128, NB=64, bs=16, MB=40, dt=pa.PA_BF16, stream=None)
+    a.update(kw)
+    return lib.pa_prefill(a["out"], a["q"], a["kc"], a["vc"], a["bt"], a["cl"], a["qs"], a["scale"], a["S"], a["T"],
+                          a["mq"], a["n_h"], a["n_kv"], a["d"], a["NB"], a["bs"], a["MB"], a["dt"], a["stream"])
+
+
+def test_prefill_rejects_invalid_arguments(lib):
+    assert _prefill(lib, dt=pa.PA_F32) == 3            # bf16 only
+    assert _prefill(lib, d=96) == 3
+    assert _prefill(lib, bs=32) == 3
+    assert _prefill(lib, n_h=30) == 2                  # not a multiple of the KV heads
+    assert _prefill(lib, mq=(1 << 20) + 1) == 3
+    assert _prefill(lib, qs=None) == 1
+    assert _prefill(lib, out=None) == 1
+    assert _prefill(lib, S=0, q=None, out=None) == 0   # nothing to do
+    assert _prefill(lib, T=0, q=None, out=None) == 0
+
+
 def test_copy_blocks_rejects_invalid_arguments(lib):
     f = lib.pa_copy_blocks
     assert f(FAKE, FAKE, FAKE, FAKE, FAKE, 3, 16, 16, 8, None) == 2       # block bytes not a multiple of 16
