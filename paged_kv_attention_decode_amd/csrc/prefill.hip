@@ -42,6 +42,9 @@ constexpr int kThreads = kWaves * 64;
 constexpr int kRowsPerWave = kPrefillRowsPerWG / kWaves;  // two 16-row tiles
 static_assert(kRowsPerWave == 32, "two MFMA row tiles per wave");
 constexpr float kOverflowSlack = 64.0f;  // log2 units
+constexpr int kXcds = 8;  // accelerator complex dies of an MI355X
+constexpr int kPrefetch = 2;             // steps (two blocks each) whose global loads are in flight
+constexpr int kBufferWord3 = 0x00020000;  // buffer descriptor word 3 on gfx950: raw 32-bit loads
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2_p __attribute__((ext_vector_type(2)));
@@ -70,11 +73,20 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillParams a) {
   constexpr int LOADS = (NCHUNK + kThreads - 1) / kThreads;
   static_assert(NCHUNK % kThreads == 0, "every thread stages the same number of chunks");
 
-  __shared__ Stage<D> st[2];
+  __shared__ Stage<D> st[2][2];  // [buffer][block of the step]
   __shared__ int s_overflow;
 
-  const int b = blockIdx.z, g = blockIdx.y;
-  const int chunk = (int)gridDim.x - 1 - (int)blockIdx.x;  // the latest rows (most blocks) start first
+  // Workgroups are dealt round-robin to the 8 XCDs, each with its own L2.
+  // Renumber them so that the row chunks of one (sequence, KV head), which
+  // read the same blocks, run on one XCD: the k-th workgroup an XCD receives
+  // takes the k-th item of that XCD's contiguous share of the work.
+  const int n_items = (int)(gridDim.x * gridDim.y * gridDim.z);
+  const int lin = (int)(blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z));
+  const int xcd = lin % kXcds, slot = lin / kXcds;
+  const int per = n_items / kXcds, extra = n_items % kXcds;
+  const int item = xcd * per + min(xcd, extra) + slot;
+  const int b = item / (int)(gridDim.x * gridDim.y), g = (item / (int)gridDim.x) % (int)gridDim.y;
+  const int chunk = (int)gridDim.x - 1 - item % (int)gridDim.x;  // the latest rows (most blocks) first
   const int q0 = a.qstart[b];
   const int n = a.qstart[b + 1] - q0;
   if (q0 < 0 || n <= 0 || n > a.max_q_len || q0 > a.num_q_tokens - n) return;
@@ -95,6 +107,8 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillParams a) {
   const int wr0 = r0 + kRowsPerWave * w;  // the wave's first row
   const bool wave_rows = wr0 < r_end;
   const int wave_end = wave_rows ? min(L, max(0, base + (min(wr0 + kRowsPerWave, r_end) - 1) / a.group + 1)) : 0;
+  // positions below this are seen by every row of the wave (0 when the wave has padding rows)
+  const int wave_min_vis = wr0 + kRowsPerWave <= r_end ? min(L, max(0, base + wr0 / a.group + 1)) : 0;
 
   // the wave's query rows as score B operands: tile tt, row wr0 + 16 tt + j, dims 32 ks + 8 grp .. + 7
   const uint16_t* __restrict__ qp = static_cast<const uint16_t*>(a.q);
@@ -128,37 +142,60 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillParams a) {
   };
   clear();
 
-  // staging: chunk c of a block is K (c < 16 CH) or V, token (c % 16 CH) / CH, 16 bytes (c % CH)
+  // staging: chunk c of a block is K (c < 16 CH) or V, token (c % 16 CH) / CH, 16 bytes (c % CH).
+  // 16 CH is a multiple of 64, so whether a load is of K or of V is the same
+  // across a wave.  A block is read through buffer descriptors whose record
+  // count ends at its last context token (the rest reads as zero); a thread's
+  // byte offset inside the block is fixed.
   const char* kbase = static_cast<const char*>(a.k_cache);
   const char* vbase = static_cast<const char*>(a.v_cache);
-  const size_t tok_stride = (size_t)a.n_kv * D * 2;
-  const size_t head_off = (size_t)g * D * 2;
-  auto fetch = [&](int k, uint4(&r)[LOADS]) {
-    const int phys = table[k];
-    const bool blk_ok = (unsigned)phys < (unsigned)a.num_blocks;
+  const uint32_t tok_stride = (uint32_t)a.n_kv * D * 2;
+  const size_t blk_bytes = (size_t)tok_stride * kBlockTokens;
+  uint32_t voff[LOADS];
 #pragma unroll
-    for (int u = 0; u < LOADS; ++u) {
-      const int c = threadIdx.x + u * kThreads;
-      const int rem = c % (kBlockTokens * CH);
-      const int tok = rem / CH, part = rem % CH;
-      const bool ok = blk_ok && k * kBlockTokens + tok < L;
-      const char* src = (c < kBlockTokens * CH ? kbase : vbase) +
-                        ((size_t)(ok ? phys : 0) * kBlockTokens + tok) * tok_stride + head_off + 16 * part;
-      r[u] = ok ? *reinterpret_cast<const uint4*>(src) : make_uint4(0, 0, 0, 0);
+  for (int u = 0; u < LOADS; ++u) {
+    const int rem = (threadIdx.x + u * kThreads) % (kBlockTokens * CH);
+    voff[u] = (uint32_t)(rem / CH) * tok_stride + (uint32_t)g * D * 2 + 16u * (uint32_t)(rem % CH);
+  }
+  // physical id of logical block blk, -1 when past the range or outside the pool
+  auto phys_of = [&](int blk) -> int {
+    if (blk >= nblk) return -1;
+    const int phys = table[blk];
+    return (unsigned)phys < (unsigned)a.num_blocks ? phys : -1;
+  };
+  // the two blocks of step it (tokens 32 it .. + 31) into registers
+  auto fetch = [&](int it, uint4(&r)[2][LOADS]) {
+#pragma unroll
+    for (int bb = 0; bb < 2; ++bb) {
+      const int blk = 2 * it + bb;
+      const int phys = phys_of(blk);
+      const int valid = phys >= 0 ? min(kBlockTokens, L - blk * kBlockTokens) : 0;
+      const size_t boff = phys >= 0 ? (size_t)phys * blk_bytes : 0;
+      const __amdgpu_buffer_rsrc_t kr =
+          __builtin_amdgcn_make_buffer_rsrc((void*)(kbase + boff), (short)0, valid * (int)tok_stride, kBufferWord3);
+      const __amdgpu_buffer_rsrc_t vr =
+          __builtin_amdgcn_make_buffer_rsrc((void*)(vbase + boff), (short)0, valid * (int)tok_stride, kBufferWord3);
+#pragma unroll
+      for (int u = 0; u < LOADS; ++u) {
+        const bool is_k = w * 64 + u * kThreads < kBlockTokens * CH;  // wave-uniform
+        r[bb][u] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(is_k ? kr : vr, voff[u], 0, 0));
+      }
     }
   };
-  auto put = [&](int buf, const uint4(&r)[LOADS]) {
+  auto put = [&](int buf, const uint4(&r)[2][LOADS]) {
 #pragma unroll
-    for (int u = 0; u < LOADS; ++u) {
-      const int c = threadIdx.x + u * kThreads;
-      const int rem = c % (kBlockTokens * CH);
-      const int tok = rem / CH, part = rem % CH;
-      uint16_t* dst = c < kBlockTokens * CH ? &st[buf].k[tok][8 * part] : &st[buf].v[tok][8 * part];
-      *reinterpret_cast<uint4*>(dst) = r[u];
-    }
+    for (int bb = 0; bb < 2; ++bb)
+#pragma unroll
+      for (int u = 0; u < LOADS; ++u) {
+        const int c = threadIdx.x + u * kThreads;
+        const int rem = c % (kBlockTokens * CH);
+        const int tok = rem / CH, part = rem % CH;
+        uint16_t* dst = c < kBlockTokens * CH ? &st[buf][bb].k[tok][8 * part] : &st[buf][bb].v[tok][8 * part];
+        *reinterpret_cast<uint4*>(dst) = r[bb][u];
+      }
   };
 
-  // per-row reference: the row's maximum over the block (lanes j, j+16, j+32, j+48 share a row)
+  // per-row reference: the row's maximum (lanes j, j+16, j+32, j+48 share a row)
   auto set_reference = [&](const floatx4_t(&s)[2]) {
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt) {
@@ -171,86 +208,135 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillParams a) {
   };
 
   bool overflow = false;  // wave-uniform
-  // mode 0: reference from block 0, weighted sums, overflow check; 1: row maxima only; 2: weighted sums
-  auto compute = [&](int k, int buf, int mode) {
-    if (!wave_rows || k * kBlockTokens >= wave_end) return;  // wave-uniform
-    const bool blk_ok = (unsigned)table[k] < (unsigned)a.num_blocks;
-    const int pos0 = k * kBlockTokens + 4 * grp;
-    floatx4_t s[2];
+  const float c = a.scale_log2;
+  // one step: the 32 tokens of blocks 2 it and 2 it + 1.
+  // mode 0: reference from step 0, weighted sums, overflow check; 1: row maxima only; 2: weighted sums
+  auto compute = [&](int it, int buf, int mode) {
+    if (!wave_rows || it * 2 * kBlockTokens >= wave_end) return;  // wave-uniform
+    floatx4_t x[2][2];  // raw q.k: [block][tile], lane: tokens 4 grp + v of row j
+    bool ok[2], whole[2];
 #pragma unroll
-    for (int tt = 0; tt < 2; ++tt) {
-      floatx4_t x = {0.0f, 0.0f, 0.0f, 0.0f};
+    for (int bb = 0; bb < 2; ++bb) {
+      const int blk = 2 * it + bb;
+      ok[bb] = phys_of(blk) >= 0;
+      whole[bb] = ok[bb] && (blk + 1) * kBlockTokens <= wave_min_vis;  // every row sees all 16 tokens
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        const uint4 kb = *reinterpret_cast<const uint4*>(&st[buf].k[j][32 * ks + 8 * grp]);
-        x = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kb),
-                                                    __builtin_bit_cast(bf16x8_t, qreg[tt][ks]), x, 0, 0, 0);
+      for (int tt = 0; tt < 2; ++tt) {
+        floatx4_t acc_s = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          const uint4 kb = *reinterpret_cast<const uint4*>(&st[buf][bb].k[j][32 * ks + 8 * grp]);
+          acc_s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kb),
+                                                          __builtin_bit_cast(bf16x8_t, qreg[tt][ks]), acc_s, 0, 0, 0);
+        }
+        x[bb][tt] = acc_s;
       }
-#pragma unroll
-      for (int v = 0; v < 4; ++v) s[tt][v] = (blk_ok && pos0 + v < vis[tt]) ? x[v] * a.scale_log2 : kNegInf;
     }
-    if (mode == 1) {
+    // scores in log2 units, -inf where masked (only blocks some row of the wave does not fully see)
+    auto score = [&](int bb, int tt, int v) -> float {
+      const int pos = (2 * it + bb) * kBlockTokens + 4 * grp + v;
+      return (whole[bb] || (ok[bb] && pos < vis[tt])) ? x[bb][tt][v] * c : kNegInf;
+    };
+    if (mode == 1 || (mode == 0 && it == 0)) {
+      floatx4_t sm[2];
 #pragma unroll
       for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
-        for (int v = 0; v < 4; ++v) mx[tt][v] = fmaxf(mx[tt][v], s[tt][v]);
-      return;
+        for (int v = 0; v < 4; ++v) sm[tt][v] = fmaxf(score(0, tt, v), score(1, tt, v));
+      if (mode == 1) {
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+          for (int v = 0; v < 4; ++v) mx[tt][v] = fmaxf(mx[tt][v], sm[tt][v]);
+        return;
+      }
+      set_reference(sm);
     }
-    if (mode == 0) {
-      if (k == 0) set_reference(s);
-      bool big = false;
+    // exponent t = scale q.k - m (one fma where the block is whole), weights 2^t
+    float t[2][2][4];
+    bool big = false;
+    // a row without a reference (nothing seen in step 0) redoes on any weight
+    const float thr[2] = {m_ref[0] == kNegInf ? kNegInf : kOverflowSlack,
+                          m_ref[1] == kNegInf ? kNegInf : kOverflowSlack};
+#pragma unroll
+    for (int bb = 0; bb < 2; ++bb)
 #pragma unroll
       for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
-        for (int v = 0; v < 4; ++v) big |= s[tt][v] > m_ref[tt] + kOverflowSlack;
-      overflow |= __builtin_amdgcn_ballot_w64(big) != 0;
-    }
-    // B operands of P V: column 4 j + 64 h + e of the lane's 4 tokens, bf16 pairs (tokens 0,1), (2,3)
-    uint2 vb[4][VH];
+        for (int v = 0; v < 4; ++v) {
+          if (whole[bb]) {
+            t[bb][tt][v] = __builtin_fmaf(x[bb][tt][v], c, -m_use[tt]);
+          } else {
+            t[bb][tt][v] = score(bb, tt, v) - m_use[tt];
+          }
+          big |= t[bb][tt][v] > thr[tt];
+        }
+    if (mode == 0) overflow |= __builtin_amdgcn_ballot_w64(big) != 0;
+    // B operands of P V (16x16x32): k-slots 0-3 are tokens 4 grp + 0..3 of block 0, slots 4-7 the
+    // same tokens of block 1; column 4 j + 64 h + e; bf16 pairs by v_perm_b32 from the lane's reads
+    // of 4 columns of each of its 8 tokens
+    uint2 vb[2][4][VH];
 #pragma unroll
-    for (int v = 0; v < 4; ++v)
+    for (int bb = 0; bb < 2; ++bb)
 #pragma unroll
-      for (int h = 0; h < VH; ++h) vb[v][h] = *reinterpret_cast<const uint2*>(&st[buf].v[4 * grp + v][4 * j + 64 * h]);
-    uint2 vt[VH][4];
+      for (int v = 0; v < 4; ++v)
 #pragma unroll
-    for (int h = 0; h < VH; ++h)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
-        const bool hi = e >= 2;
-        vt[h][e].x = __builtin_amdgcn_perm(hi ? vb[1][h].y : vb[1][h].x, hi ? vb[0][h].y : vb[0][h].x, sel);
-        vt[h][e].y = __builtin_amdgcn_perm(hi ? vb[3][h].y : vb[3][h].x, hi ? vb[2][h].y : vb[2][h].x, sel);
-      }
+        for (int h = 0; h < VH; ++h)
+          vb[bb][v][h] = *reinterpret_cast<const uint2*>(&st[buf][bb].v[4 * grp + v][4 * j + 64 * h]);
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt) {
-      float p[4];
-#pragma unroll
-      for (int v = 0; v < 4; ++v) p[v] = fast_exp2(s[tt][v] - m_use[tt]);
-      uint2 pa2;
-      pa2.x = pack_bf16(p[0], p[1]);
-      pa2.y = pack_bf16(p[2], p[3]);
-      lsum[tt] += (bf16_lo(pa2.x) + bf16_hi(pa2.x)) + (bf16_lo(pa2.y) + bf16_hi(pa2.y));
+      uint4 pa;
+      pa.x = pack_bf16(fast_exp2(t[0][tt][0]), fast_exp2(t[0][tt][1]));
+      pa.y = pack_bf16(fast_exp2(t[0][tt][2]), fast_exp2(t[0][tt][3]));
+      pa.z = pack_bf16(fast_exp2(t[1][tt][0]), fast_exp2(t[1][tt][1]));
+      pa.w = pack_bf16(fast_exp2(t[1][tt][2]), fast_exp2(t[1][tt][3]));
+      // the row sum adds the same rounded weights the product uses
+      constexpr uint32_t kOnes = 0x3F803F80u;  // bf16 (1, 1)
+      lsum[tt] = dot2_bf16(pa.x, kOnes, dot2_bf16(pa.y, kOnes, dot2_bf16(pa.z, kOnes, dot2_bf16(pa.w, kOnes,
+                                                                                                  lsum[tt]))));
 #pragma unroll
       for (int h = 0; h < VH; ++h)
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
-          acc[tt][h][e] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(
-              __builtin_bit_cast(short4_t, pa2), __builtin_bit_cast(short4_t, vt[h][e]), acc[tt][h][e], 0, 0, 0);
+        for (int e = 0; e < 4; ++e) {
+          const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
+          const bool hi = e >= 2;
+          uint4 vt;
+          vt.x = __builtin_amdgcn_perm(hi ? vb[0][1][h].y : vb[0][1][h].x, hi ? vb[0][0][h].y : vb[0][0][h].x, sel);
+          vt.y = __builtin_amdgcn_perm(hi ? vb[0][3][h].y : vb[0][3][h].x, hi ? vb[0][2][h].y : vb[0][2][h].x, sel);
+          vt.z = __builtin_amdgcn_perm(hi ? vb[1][1][h].y : vb[1][1][h].x, hi ? vb[1][0][h].y : vb[1][0][h].x, sel);
+          vt.w = __builtin_amdgcn_perm(hi ? vb[1][3][h].y : vb[1][3][h].x, hi ? vb[1][2][h].y : vb[1][2][h].x, sel);
+          acc[tt][h][e] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, pa),
+                                                                  __builtin_bit_cast(bf16x8_t, vt), acc[tt][h][e], 0,
+                                                                  0, 0);
+        }
     }
   };
 
-  // one pass over the blocks: block k + 1's loads are in flight while block k is multiplied
+  // one pass over the steps.  Global loads run kPrefetch steps ahead in
+  // registers (slot it % kPrefetch holds step it); LDS holds two steps: the
+  // one being multiplied and the next one.
+  const int nit = (nblk + 1) / 2;
   auto sweep = [&](int mode) {
-    uint4 r[LOADS];
-    fetch(0, r);
-    put(0, r);
+    uint4 r[kPrefetch][2][LOADS];
+#pragma unroll
+    for (int u = 0; u < kPrefetch; ++u)
+      if (u < nit) fetch(u, r[u]);
+    put(0, r[0]);
+    if (kPrefetch < nit) fetch(kPrefetch, r[0]);
     __syncthreads();
-    for (int k = 0; k < nblk; ++k) {
-      const int cur = k & 1;
-      if (k + 1 < nblk) fetch(k + 1, r);
-      compute(k, cur, mode);
-      if (k + 1 < nblk) put(cur ^ 1, r);
-      __syncthreads();  // block k + 1 staged; everyone is done with block k
+    for (int it0 = 0; it0 < nit; it0 += kPrefetch) {
+#pragma unroll
+      for (int u = 0; u < kPrefetch; ++u) {
+        const int it = it0 + u;
+        if (it >= nit) break;
+        compute(it, it & 1, mode);
+        const int nxt = (u + 1) % kPrefetch;  // register slot of step it + 1 (constant once unrolled)
+        if (it + 1 < nit) {
+          put((it + 1) & 1, r[nxt]);
+          if (it + 1 + kPrefetch < nit) fetch(it + 1 + kPrefetch, r[nxt]);
+        }
+        __syncthreads();  // step it + 1 staged; everyone is done with step it
+      }
     }
   };
 
