@@ -163,9 +163,10 @@ pa_status pa_cache_write(const void* k, const void* v, void* k_cache, void* v_ca
  * also does not depend on the other sequences of the batch; in PA_BALANCED
  * mode the cut points follow the whole batch's context lengths, so a
  * sequence's result may differ in the last bits with the batch around it.
- * bf16 with 8 or more rows per KV head runs on the matrix cores, which round
- * the softmax weights to bf16 before the weighted sum of V (the row sums add
- * the same rounded weights); every other case keeps the weights in fp32.
+ * With bf16, the softmax weights are rounded to bf16 before the weighted sum
+ * of V, and the row sums add the same rounded weights: 8 or more rows per KV
+ * head run on the matrix cores, fewer on the vector ALUs (two tokens per
+ * v_dot2_f32_bf16).  fp32 keeps the weights in fp32.
  */
 pa_status pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache,
                     const int32_t* block_tables, const int32_t* context_lens, float scale, int32_t q_len,

@@ -251,19 +251,29 @@ struct MfmaAttender {
       }
     };
 
+    // one tile: its query operands fit in registers for the whole range (16
+    // VGPRs at head_dim 128); more tiles read them from LDS at every block
+    auto q_dim = [&](int ks) { return KV8 ? 64 * (ks / 2) + 16 * grp + 8 * (ks & 1) : 32 * ks + 8 * grp; };
+    uint4 qreg[NT == 1 ? KS : 1];
+    if constexpr (NT == 1) {
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) qreg[ks] = *reinterpret_cast<const uint4*>(&sm.q[j][q_dim(ks)]);
+    }
+
     // scores: s[t][v] = row 16 t + j against token 4 grp + v, log2 units, -inf where masked
     auto scores = [&](const uint4(&kb)[KL], int lblk, bool ok, floatx4_t(&s)[NT]) {
       const int pos0 = lblk * kBlockTokens + 4 * grp;
       // keep the compiler from hoisting the query reads out of the block loop
       // into registers, which is what the LDS copy avoids
-      asm volatile("" ::: "memory");
+      if constexpr (NT > 1) asm volatile("" ::: "memory");
 #pragma unroll
       for (int t = 0; t < NT; ++t) {
         floatx4_t x = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
-          const int qd = KV8 ? 64 * (ks / 2) + 16 * grp + 8 * (ks & 1) : 32 * ks + 8 * grp;
-          const uint4 qb = *reinterpret_cast<const uint4*>(&sm.q[16 * t + j][qd]);
+          uint4 qb;
+          if constexpr (NT == 1) qb = qreg[ks];
+          else qb = *reinterpret_cast<const uint4*>(&sm.q[16 * t + j][q_dim(ks)]);
           x = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, k_operand(kb, ks)),
                                                       __builtin_bit_cast(bf16x8_t, qb), x, 0, 0, 0);
         }

@@ -23,6 +23,10 @@
 //           4q + i, whose weights the score layout holds in lanes 16q + 4i ..
 //           16q + 4i + 3 of the same row, so one DPP row_newbcast per row and
 //           load moves them (other head shapes use a cross-lane permute).
+//           bf16: the weights are rounded to bf16 and the tokens of loads
+//           2m and 2m + 1 go through one v_dot2_f32_bf16 per column and row,
+//           their column pairs formed by v_perm_b32 (the row sums add the
+//           same rounded weights); fp32 multiplies one token at a time.
 //
 // Memory-level parallelism: K/V are read with buffer loads whose descriptor
 // (wave-uniform) points at one physical block, so the per-lane offsets never
@@ -92,6 +96,13 @@ __device__ __forceinline__ void bcast_in_row(float (&pr)[R], const float (&p)[R]
 // x as held by lane src (any lane of the wave)
 __device__ __forceinline__ float lane_from(float x, int src) {
   return __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(src << 2, __builtin_bit_cast(int, x)));
+}
+
+typedef float float2_v __attribute__((ext_vector_type(2)));
+
+// (lo, hi) rounded to bf16 (round to nearest even), as one packed dword
+__device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((float2_v){lo, hi}, bf16x2_t));
 }
 
 template <typename T, int D, int R, int NW>
@@ -245,10 +256,59 @@ struct ValuAttender {
     auto accumulate = [&](const float(&s)[R], const uint4(&vb)[NV]) {
       float p[R];
 #pragma unroll
-      for (int r = 0; r < R; ++r) {
-        p[r] = fast_exp2(s[r] - m_use[r]);
-        lsum[r] += p[r];
+      for (int r = 0; r < R; ++r) p[r] = fast_exp2(s[r] - m_use[r]);
+      if constexpr (kBF16) {
+        // bf16 caches: the weights are rounded to bf16 and P V takes two
+        // tokens per instruction, v_dot2_f32_bf16 of (p_t, p_t') with
+        // (v_t[c], v_t'[c]) for the tokens of value loads 2m and 2m + 1; the
+        // row sum adds the same rounded weights
+        uint32_t pw[R];  // this lane's token's weight, twice, as a bf16 pair
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+          pw[r] = pack_bf16(p[r], p[r]);
+          lsum[r] += bf16_lo(pw[r]);
+        }
+#pragma unroll
+        for (int m = 0; m < NV / 2; ++m) {
+          uint32_t wp[R];  // (weight of load 2m's token, weight of load 2m + 1's token)
+          if constexpr (kRowTokens) {
+            float w0[R], w1[R];
+            float pf[R];
+#pragma unroll
+            for (int r = 0; r < R; ++r) pf[r] = __builtin_bit_cast(float, pw[r]);
+            bcast_in_row<R>(w0, pf, 2 * m);
+            bcast_in_row<R>(w1, pf, 2 * m + 1);
+#pragma unroll
+            for (int r = 0; r < R; ++r)
+              wp[r] = __builtin_amdgcn_perm(__builtin_bit_cast(uint32_t, w1[r]), __builtin_bit_cast(uint32_t, w0[r]),
+                                            0x05040100u);
+          } else {
+            const int src0 = 4 * (tv + TPV * (2 * m)), src1 = 4 * (tv + TPV * (2 * m + 1));
+#pragma unroll
+            for (int r = 0; r < R; ++r) {
+              const float pf = __builtin_bit_cast(float, pw[r]);
+              wp[r] = __builtin_amdgcn_perm(__builtin_bit_cast(uint32_t, lane_from(pf, src1)),
+                                            __builtin_bit_cast(uint32_t, lane_from(pf, src0)), 0x05040100u);
+            }
+          }
+          // column pairs: (v_t[c], v_t'[c]) for the lane's 8 columns
+          const uint4 v0 = vb[2 * m], v1 = vb[2 * m + 1];
+          const uint32_t d0[4] = {v0.x, v0.y, v0.z, v0.w}, d1[4] = {v1.x, v1.y, v1.z, v1.w};
+          uint32_t cp[EPC];
+#pragma unroll
+          for (int d = 0; d < 4; ++d) {
+            cp[2 * d] = __builtin_amdgcn_perm(d1[d], d0[d], 0x05040100u);
+            cp[2 * d + 1] = __builtin_amdgcn_perm(d1[d], d0[d], 0x07060302u);
+          }
+#pragma unroll
+          for (int r = 0; r < R; ++r)
+#pragma unroll
+            for (int e = 0; e < EPC; ++e) acc[r][e] = dot2_bf16(wp[r], cp[e], acc[r][e]);
+        }
+        return;
       }
+#pragma unroll
+      for (int r = 0; r < R; ++r) lsum[r] += p[r];
 #pragma unroll
       for (int i = 0; i < NV; ++i) {
         // weights of the token this lane's value load i holds
