@@ -315,6 +315,35 @@ def test_balanced_with_empty_and_tiny_contexts():
         assert np.all(got[want_zero] == 0)
 
 
+@pytest.mark.parametrize("num_seqs", [4096, 4097], ids=["balanced-max", "one-pass-fallback"])
+def test_balanced_batch_size_limit(num_seqs):
+    """The balanced mode's prefix table holds 4096 sequences; one more falls back to one pass.
+    Either way the result matches the oracle on sampled rows."""
+    spec = wl.Spec(name="wide-batch", dtype="bf16", num_seqs=num_seqs, num_q_heads=4, num_kv_heads=2, head_dim=64,
+                   lens=("uniform", 1, 40), max_len=48, seed=41)
+    p = wl.make_problem(spec)
+    say(f"{num_seqs} sequences, balanced")
+    _, got = run(p, -1)
+    assert np.isfinite(got).all()
+    rows = sample_rows(p, 64)
+    ref = oracle.paged_decode_rows(p.q, p.k_cache, p.v_cache, p.block_tables, p.context_lens, p.scale, p.q_len,
+                                   p.dtype, rows)
+    assert_parity(np.stack([got[b * p.q_len + j, h] for (b, j, h) in rows]), ref, "bf16", f"{num_seqs} sequences")
+
+
+def test_balanced_kv_head_limit_falls_back():
+    """More than 1024 KV heads: the balanced request runs as one pass, still exact to the oracle."""
+    spec = wl.Spec(name="many-heads", dtype="bf16", num_seqs=3, num_q_heads=1025, num_kv_heads=1025, head_dim=64,
+                   lens=("fixed", (5, 20, 33)), max_len=48, seed=43)
+    p = wl.make_problem(spec)
+    say("1025 KV heads, balanced")
+    _, got = run(p, -1)
+    rows = [(b, 0, h) for b in range(3) for h in (0, 1, 511, 1023, 1024)]
+    ref = oracle.paged_decode_rows(p.q, p.k_cache, p.v_cache, p.block_tables, p.context_lens, p.scale, p.q_len,
+                                   p.dtype, rows)
+    assert_parity(np.stack([got[b, h] for (b, _, h) in rows]), ref, "bf16", "1025 KV heads")
+
+
 # ---------------------------------------------------------------------------
 # the full-size workloads, in the launch configuration bench.py times
 
