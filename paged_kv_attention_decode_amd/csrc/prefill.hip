@@ -39,8 +39,9 @@ namespace {
 
 constexpr int kWaves = 4;
 constexpr int kThreads = kWaves * 64;
-constexpr int kRowsPerWave = kPrefillRowsPerWG / kWaves;  // two 16-row tiles
-static_assert(kRowsPerWave == 32, "two MFMA row tiles per wave");
+constexpr int kRowsPerWave = kPrefillRowsPerWG / kWaves;
+constexpr int TW = kRowsPerWave / 16;  // 16-row MFMA tiles per wave
+static_assert(kRowsPerWave % 16 == 0, "whole MFMA row tiles per wave");
 constexpr float kOverflowSlack = 64.0f;  // log2 units
 constexpr int kXcds = 8;  // accelerator complex dies of an MI355X
 constexpr int kPrefetch = 2;             // steps (two blocks each) whose global loads are in flight
@@ -65,7 +66,7 @@ struct Stage {
 };
 
 template <int D>
-__global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillParams a) {
+__global__ __launch_bounds__(kThreads, TW <= 2 ? 2 : 1) void prefill_kernel(PrefillParams a) {
   constexpr int KS = D / 32;                          // score k-steps
   constexpr int VH = D / 64;                          // value column halves
   constexpr int CH = D / 8;                           // 16-byte chunks per token row of the head
@@ -112,10 +113,10 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillParams a) {
 
   // the wave's query rows as score B operands: tile tt, row wr0 + 16 tt + j, dims 32 ks + 8 grp .. + 7
   const uint16_t* __restrict__ qp = static_cast<const uint16_t*>(a.q);
-  uint4 qreg[2][KS];
-  int vis[2];  // row 16 tt + j of the wave sees positions below vis[tt]
+  uint4 qreg[TW][KS];
+  int vis[TW];  // row 16 tt + j of the wave sees positions below vis[tt]
 #pragma unroll
-  for (int tt = 0; tt < 2; ++tt) {
+  for (int tt = 0; tt < TW; ++tt) {
     const int row = wr0 + 16 * tt + j;
     const bool ok = row < r_end;
     const int tok = row / a.group, hh = row % a.group;
@@ -126,12 +127,17 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillParams a) {
       qreg[tt][ks] = ok ? *reinterpret_cast<const uint4*>(src + 32 * ks) : make_uint4(0, 0, 0, 0);
   }
 
-  float m_ref[2] = {kNegInf, kNegInf}, m_use[2] = {0.0f, 0.0f}, lsum[2] = {0.0f, 0.0f};
-  floatx4_t acc[2][VH][4];
-  floatx4_t mx[2];
+  float m_ref[TW], m_use[TW], lsum[TW];
+#pragma unroll
+  for (int tt = 0; tt < TW; ++tt) {
+    m_ref[tt] = kNegInf;
+    m_use[tt] = 0.0f;
+  }
+  floatx4_t acc[TW][VH][4];
+  floatx4_t mx[TW];
   auto clear = [&]() {
 #pragma unroll
-    for (int tt = 0; tt < 2; ++tt) {
+    for (int tt = 0; tt < TW; ++tt) {
       lsum[tt] = 0.0f;
       mx[tt] = (floatx4_t){kNegInf, kNegInf, kNegInf, kNegInf};
 #pragma unroll
@@ -196,9 +202,9 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillParams a) {
   };
 
   // per-row reference: the row's maximum (lanes j, j+16, j+32, j+48 share a row)
-  auto set_reference = [&](const floatx4_t(&s)[2]) {
+  auto set_reference = [&](const floatx4_t(&s)[TW]) {
 #pragma unroll
-    for (int tt = 0; tt < 2; ++tt) {
+    for (int tt = 0; tt < TW; ++tt) {
       float x = fmaxf(fmaxf(s[tt][0], s[tt][1]), fmaxf(s[tt][2], s[tt][3]));
       x = fmaxf(x, shfl_xor(x, 16));
       x = fmaxf(x, shfl_xor(x, 32));
@@ -213,7 +219,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillParams a) {
   // mode 0: reference from step 0, weighted sums, overflow check; 1: row maxima only; 2: weighted sums
   auto compute = [&](int it, int buf, int mode) {
     if (!wave_rows || it * 2 * kBlockTokens >= wave_end) return;  // wave-uniform
-    floatx4_t x[2][2];  // raw q.k: [block][tile], lane: tokens 4 grp + v of row j
+    floatx4_t x[2][TW];  // raw q.k: [block][tile], lane: tokens 4 grp + v of row j
     bool ok[2], whole[2];
 #pragma unroll
     for (int bb = 0; bb < 2; ++bb) {
@@ -221,7 +227,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillParams a) {
       ok[bb] = phys_of(blk) >= 0;
       whole[bb] = ok[bb] && (blk + 1) * kBlockTokens <= wave_min_vis;  // every row sees all 16 tokens
 #pragma unroll
-      for (int tt = 0; tt < 2; ++tt) {
+      for (int tt = 0; tt < TW; ++tt) {
         floatx4_t acc_s = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
@@ -238,14 +244,14 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillParams a) {
       return (whole[bb] || (ok[bb] && pos < vis[tt])) ? x[bb][tt][v] * c : kNegInf;
     };
     if (mode == 1 || (mode == 0 && it == 0)) {
-      floatx4_t sm[2];
+      floatx4_t sm[TW];
 #pragma unroll
-      for (int tt = 0; tt < 2; ++tt)
+      for (int tt = 0; tt < TW; ++tt)
 #pragma unroll
         for (int v = 0; v < 4; ++v) sm[tt][v] = fmaxf(score(0, tt, v), score(1, tt, v));
       if (mode == 1) {
 #pragma unroll
-        for (int tt = 0; tt < 2; ++tt)
+        for (int tt = 0; tt < TW; ++tt)
 #pragma unroll
           for (int v = 0; v < 4; ++v) mx[tt][v] = fmaxf(mx[tt][v], sm[tt][v]);
         return;
@@ -253,15 +259,16 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillParams a) {
       set_reference(sm);
     }
     // exponent t = scale q.k - m (one fma where the block is whole), weights 2^t
-    float t[2][2][4];
+    float t[2][TW][4];
     bool big = false;
     // a row without a reference (nothing seen in step 0) redoes on any weight
-    const float thr[2] = {m_ref[0] == kNegInf ? kNegInf : kOverflowSlack,
-                          m_ref[1] == kNegInf ? kNegInf : kOverflowSlack};
+    float thr[TW];
+#pragma unroll
+    for (int tt = 0; tt < TW; ++tt) thr[tt] = m_ref[tt] == kNegInf ? kNegInf : kOverflowSlack;
 #pragma unroll
     for (int bb = 0; bb < 2; ++bb)
 #pragma unroll
-      for (int tt = 0; tt < 2; ++tt)
+      for (int tt = 0; tt < TW; ++tt)
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
           if (whole[bb]) {
@@ -284,7 +291,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillParams a) {
         for (int h = 0; h < VH; ++h)
           vb[bb][v][h] = *reinterpret_cast<const uint2*>(&st[buf][bb].v[4 * grp + v][4 * j + 64 * h]);
 #pragma unroll
-    for (int tt = 0; tt < 2; ++tt) {
+    for (int tt = 0; tt < TW; ++tt) {
       uint4 pa;
       pa.x = pack_bf16(fast_exp2(t[0][tt][0]), fast_exp2(t[0][tt][1]));
       pa.y = pack_bf16(fast_exp2(t[0][tt][2]), fast_exp2(t[0][tt][3]));
@@ -357,7 +364,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillParams a) {
 
   // row sums over the 4 token groups: lanes j, j+16, j+32, j+48 then hold row j of each tile
 #pragma unroll
-  for (int tt = 0; tt < 2; ++tt) {
+  for (int tt = 0; tt < TW; ++tt) {
     float x = lsum[tt];
     x += shfl_xor(x, 16);
     x += shfl_xor(x, 32);
@@ -366,7 +373,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(PrefillParams a) {
   // output: lane l holds rows 4 (l / 16) + i of each tile, columns 4 (l % 16) + 64 h + e
   uint16_t* __restrict__ op = static_cast<uint16_t*>(a.out);
 #pragma unroll
-  for (int tt = 0; tt < 2; ++tt) {
+  for (int tt = 0; tt < TW; ++tt) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int rr = 4 * grp + i;  // row within the tile
