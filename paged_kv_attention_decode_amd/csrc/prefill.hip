@@ -44,7 +44,8 @@ constexpr int TW = kRowsPerWave / 16;  // 16-row MFMA tiles per wave
 static_assert(kRowsPerWave % 16 == 0, "whole MFMA row tiles per wave");
 constexpr float kOverflowSlack = 64.0f;  // log2 units
 constexpr int kXcds = 8;  // accelerator complex dies of an MI355X
-constexpr int kPrefetch = 2;             // steps (two blocks each) whose global loads are in flight
+constexpr int kStepBlocks = 4;           // blocks staged per step (per barrier), multiplied two at a time
+constexpr int kPrefetch = 1;             // steps whose global loads are in flight
 constexpr int kBufferWord3 = 0x00020000;  // buffer descriptor word 3 on gfx950: raw 32-bit loads
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
@@ -74,7 +75,7 @@ __global__ __launch_bounds__(kThreads, TW <= 2 ? 2 : 1) void prefill_kernel(Pref
   constexpr int LOADS = (NCHUNK + kThreads - 1) / kThreads;
   static_assert(NCHUNK % kThreads == 0, "every thread stages the same number of chunks");
 
-  __shared__ Stage<D> st[2][2];  // [buffer][block of the step]
+  __shared__ Stage<D> st[2][kStepBlocks];  // [buffer][block of the step]
   __shared__ int s_overflow;
 
   // Workgroups are dealt round-robin to the 8 XCDs, each with its own L2.
@@ -169,11 +170,11 @@ __global__ __launch_bounds__(kThreads, TW <= 2 ? 2 : 1) void prefill_kernel(Pref
     const int phys = table[blk];
     return (unsigned)phys < (unsigned)a.num_blocks ? phys : -1;
   };
-  // the two blocks of step it (tokens 32 it .. + 31) into registers
-  auto fetch = [&](int it, uint4(&r)[2][LOADS]) {
+  // the blocks of step it into registers
+  auto fetch = [&](int it, uint4(&r)[kStepBlocks][LOADS]) {
 #pragma unroll
-    for (int bb = 0; bb < 2; ++bb) {
-      const int blk = 2 * it + bb;
+    for (int bb = 0; bb < kStepBlocks; ++bb) {
+      const int blk = kStepBlocks * it + bb;
       const int phys = phys_of(blk);
       const int valid = phys >= 0 ? min(kBlockTokens, L - blk * kBlockTokens) : 0;
       const size_t boff = phys >= 0 ? (size_t)phys * blk_bytes : 0;
@@ -188,9 +189,9 @@ __global__ __launch_bounds__(kThreads, TW <= 2 ? 2 : 1) void prefill_kernel(Pref
       }
     }
   };
-  auto put = [&](int buf, const uint4(&r)[2][LOADS]) {
+  auto put = [&](int buf, const uint4(&r)[kStepBlocks][LOADS]) {
 #pragma unroll
-    for (int bb = 0; bb < 2; ++bb)
+    for (int bb = 0; bb < kStepBlocks; ++bb)
 #pragma unroll
       for (int u = 0; u < LOADS; ++u) {
         const int c = threadIdx.x + u * kThreads;
@@ -215,15 +216,15 @@ __global__ __launch_bounds__(kThreads, TW <= 2 ? 2 : 1) void prefill_kernel(Pref
 
   bool overflow = false;  // wave-uniform
   const float c = a.scale_log2;
-  // one step: the 32 tokens of blocks 2 it and 2 it + 1.
-  // mode 0: reference from step 0, weighted sums, overflow check; 1: row maxima only; 2: weighted sums
-  auto compute = [&](int it, int buf, int mode) {
-    if (!wave_rows || it * 2 * kBlockTokens >= wave_end) return;  // wave-uniform
+  // a pair of blocks: blk0 and blk0 + 1, staged in slots sl and sl + 1 of the buffer.
+  // mode 0: reference from the first pair, weighted sums, overflow check; 1: row maxima only;
+  // 2: weighted sums
+  auto pair = [&](int blk0, int buf, int sl, int mode) {
     floatx4_t x[2][TW];  // raw q.k: [block][tile], lane: tokens 4 grp + v of row j
     bool ok[2], whole[2];
 #pragma unroll
     for (int bb = 0; bb < 2; ++bb) {
-      const int blk = 2 * it + bb;
+      const int blk = blk0 + bb;
       ok[bb] = phys_of(blk) >= 0;
       whole[bb] = ok[bb] && (blk + 1) * kBlockTokens <= wave_min_vis;  // every row sees all 16 tokens
 #pragma unroll
@@ -231,7 +232,7 @@ __global__ __launch_bounds__(kThreads, TW <= 2 ? 2 : 1) void prefill_kernel(Pref
         floatx4_t acc_s = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
-          const uint4 kb = *reinterpret_cast<const uint4*>(&st[buf][bb].k[j][32 * ks + 8 * grp]);
+          const uint4 kb = *reinterpret_cast<const uint4*>(&st[buf][sl + bb].k[j][32 * ks + 8 * grp]);
           acc_s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kb),
                                                           __builtin_bit_cast(bf16x8_t, qreg[tt][ks]), acc_s, 0, 0, 0);
         }
@@ -240,10 +241,10 @@ __global__ __launch_bounds__(kThreads, TW <= 2 ? 2 : 1) void prefill_kernel(Pref
     }
     // scores in log2 units, -inf where masked (only blocks some row of the wave does not fully see)
     auto score = [&](int bb, int tt, int v) -> float {
-      const int pos = (2 * it + bb) * kBlockTokens + 4 * grp + v;
+      const int pos = (blk0 + bb) * kBlockTokens + 4 * grp + v;
       return (whole[bb] || (ok[bb] && pos < vis[tt])) ? x[bb][tt][v] * c : kNegInf;
     };
-    if (mode == 1 || (mode == 0 && it == 0)) {
+    if (mode == 1 || (mode == 0 && blk0 == 0)) {
       floatx4_t sm[TW];
 #pragma unroll
       for (int tt = 0; tt < TW; ++tt)
@@ -289,7 +290,7 @@ __global__ __launch_bounds__(kThreads, TW <= 2 ? 2 : 1) void prefill_kernel(Pref
       for (int v = 0; v < 4; ++v)
 #pragma unroll
         for (int h = 0; h < VH; ++h)
-          vb[bb][v][h] = *reinterpret_cast<const uint2*>(&st[buf][bb].v[4 * grp + v][4 * j + 64 * h]);
+          vb[bb][v][h] = *reinterpret_cast<const uint2*>(&st[buf][sl + bb].v[4 * grp + v][4 * j + 64 * h]);
 #pragma unroll
     for (int tt = 0; tt < TW; ++tt) {
       uint4 pa;
@@ -319,12 +320,22 @@ __global__ __launch_bounds__(kThreads, TW <= 2 ? 2 : 1) void prefill_kernel(Pref
     }
   };
 
+  // one step: its pairs of blocks, those some row of the wave sees
+  auto compute = [&](int it, int buf, int mode) {
+#pragma unroll
+    for (int pp = 0; pp < kStepBlocks / 2; ++pp) {
+      const int blk0 = kStepBlocks * it + 2 * pp;
+      if (!wave_rows || blk0 * kBlockTokens >= wave_end) return;  // wave-uniform
+      pair(blk0, buf, 2 * pp, mode);
+    }
+  };
+
   // one pass over the steps.  Global loads run kPrefetch steps ahead in
   // registers (slot it % kPrefetch holds step it); LDS holds two steps: the
   // one being multiplied and the next one.
-  const int nit = (nblk + 1) / 2;
+  const int nit = (nblk + kStepBlocks - 1) / kStepBlocks;
   auto sweep = [&](int mode) {
-    uint4 r[kPrefetch][2][LOADS];
+    uint4 r[kPrefetch][kStepBlocks][LOADS];
 #pragma unroll
     for (int u = 0; u < kPrefetch; ++u)
       if (u < nit) fetch(u, r[u]);
