@@ -345,7 +345,9 @@ def main(argv=None):
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_per_step = (t1 - t0) * 1e3 / K
-    decode_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    launch_ms = np.array([a.elapsed_time(b) for a, b in ev])
+    decode_ms = float(np.mean(launch_ms))
+    spread_us = {f"p{q}": round(float(np.percentile(launch_ms, q)) * 1e3, 2) for q in (10, 50, 90)}
 
     # breakdown of the other two calls, from a separate untimed pass of whole
     # steps (event-bracketed, so each figure includes one timing event's cost)
@@ -406,7 +408,7 @@ def main(argv=None):
                 "kernel": decode_kernel_name(p, partition),
                 "algorithmic_flops_per_launch": flops,
                 "algorithmic_bytes_per_launch": kv_bytes + ab["out"],
-                "avg_launch_us": round(decode_ms * 1e3, 2)}
+                "avg_launch_us": round(decode_ms * 1e3, 2), "launch_us_percentiles": spread_us}
     else:
         achieved = kv_bytes / decode_s / 1e9
         traffic, traffic_bytes = load_traffic(args.config, decode_s)
@@ -415,7 +417,7 @@ def main(argv=None):
                 "traffic": round(traffic, 1) if isinstance(traffic, float) else None,
                 "kernel": decode_kernel_name(p, partition),
                 "algorithmic_bytes_per_launch": kv_bytes,
-                "avg_launch_us": round(decode_ms * 1e3, 2)}
+                "avg_launch_us": round(decode_ms * 1e3, 2), "launch_us_percentiles": spread_us}
     if isinstance(traffic_bytes, str):
         roof["traffic_note"] = traffic_bytes
     elif traffic_bytes is not None:
