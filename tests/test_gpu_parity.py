@@ -260,6 +260,49 @@ def test_identical_keys_count_probe_fp32(q_len, L):
                 np.testing.assert_allclose(got[b * q_len + j, 0], expect, rtol=2e-6, atol=0)
 
 
+COUNT_SHAPES = [  # (GQA group, q_len, context lengths, partition sizes): the workloads' kernel paths
+    (4, 1, (2304, 2303, 700), (0, -1)),      # 8B decode: vector ALUs
+    (8, 1, (2304, 1000, 33), (0, -1)),       # 70B decode: matrix cores, one tile
+    (8, 5, (2304, 1029, 77), (0, -1)),       # verify: matrix cores, three tiles
+    (4, 1, (131072,), (0, 512)),             # long context: partitions + pa_reduce
+]
+
+
+@pytest.mark.parametrize("G,q_len,lens,parts", COUNT_SHAPES, ids=["8b", "70b", "verify", "long"])
+def test_identical_keys_count_probe_bf16(G, q_len, lens, parts):
+    """bf16 at the workloads' shapes: all keys equal, V[t, c] = 1 where c == t mod d.  Every
+    weight is exactly 1, so each output is count / (p + 1): in one pass the bf16 rounding
+    of one fp32 division, bit for bit; the split and balanced merges of normalized partials
+    stay within one bf16 unit in the last place."""
+    d, n_kv = 128, 2
+    spec = wl.Spec(name="count16", dtype="bf16", num_seqs=len(lens), num_q_heads=G * n_kv, num_kv_heads=n_kv,
+                   head_dim=d, lens=("fixed", lens), max_len=max(lens) + 16, q_len=q_len, seed=9)
+    p = wl.make_problem(spec)
+    p.k_cache[:] = np.uint16(0x3E80)  # 0.25
+    p.v_cache[:] = 0
+    for b, Lb in enumerate(lens):
+        t = np.arange(Lb)
+        blk = p.block_tables[b, t // 16]
+        for g in range(n_kv):
+            p.v_cache[blk, t % 16, g, t % d] = np.uint16(0x3F80)
+    expect = np.zeros((len(lens) * q_len, d), dtype=np.float32)
+    for b, Lb in enumerate(lens):
+        for j in range(q_len):
+            pos = Lb - q_len + j
+            counts = np.array([len(range(c, pos + 1, d)) for c in range(d)], dtype=np.float32)
+            expect[b * q_len + j] = counts / np.float32(pos + 1)
+    expect_bits = wl.round_to_bf16_bits(expect)
+    for ps in parts:
+        say(f"bf16 count probe G={G} q_len={q_len} lens={lens} ps={ps}")
+        d_ = DeviceProblem(p)
+        out = to_host(d_.step(ps, write=False))
+        for h in range(spec.num_q_heads):
+            if ps == 0:
+                assert np.array_equal(out[:, h], expect_bits), (ps, h)
+            else:
+                np.testing.assert_allclose(widen(out[:, h], "bf16"), widen(expect_bits, "bf16"), rtol=2 ** -7, atol=0)
+
+
 @pytest.mark.parametrize("dtype,q_len,n_h", [("f32", 1, 2), ("f32", 2, 2), ("bf16", 1, 2), ("bf16", 2, 2),
                                              ("bf16", 5, 2), ("bf16", 5, 8)])
 def test_scores_rising_far_past_the_first_block(dtype, q_len, n_h):
