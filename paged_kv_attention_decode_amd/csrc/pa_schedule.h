@@ -303,14 +303,27 @@ __device__ void drive_balanced(const DecodeParams& a, Attn& at) {
     __syncthreads();
   };
 
-  while (true) {
-    const long long seg0 = s_prefix[b], seg1 = s_prefix[b + 1];
+  // the sequence holding flat block B1 - 1 (the range's last)
+  int b_last = b;
+  {
+    int l2 = b, h2 = S;  // prefix[l2] <= B1 - 1 < prefix[h2]
+    while (h2 - l2 > 1) {
+      const int mid = (l2 + h2) / 2;
+      if (s_prefix[mid] <= B1 - 1) l2 = mid;
+      else h2 = mid;
+    }
+    b_last = l2;
+  }
+
+  // one sequence's share of the range: written out when whole, published as a piece when cut
+  auto one = [&](int bb) {
+    const long long seg0 = s_prefix[bb], seg1 = s_prefix[bb + 1];
     const int nb = (int)(seg1 - seg0);
     const int blo = (int)((B0 > seg0 ? B0 : seg0) - seg0);
     const int bhi = (int)((B1 < seg1 ? B1 : seg1) - seg0);
-    at.run(b, g, clamped_len(a, b), blo, bhi);
+    at.run(bb, g, clamped_len(a, bb), blo, bhi);
     if (blo == 0 && bhi == nb) {
-      write_final(a, at, b, g);
+      write_final(a, at, bb, g);
     } else {
       // a piece: its partial goes out with device-coherent stores (written
       // through to the point of coherence of all XCDs) and its arrival is
@@ -329,13 +342,42 @@ __device__ void drive_balanced(const DecodeParams& a, Attn& at) {
           coherent_store(mine + (size_t)r * (Attn::kD + 2) + Attn::kD + 1, l);
         }
       }
-      arrive(b, seg0, seg1);
+      arrive(bb, seg0, seg1);
     }
-    if (seg1 >= B1) break;
-    // next sequence with blocks
-    do {
-      ++b;
-    } while (s_prefix[b + 1] == s_prefix[b]);
+  };
+
+  // Order: the cut piece at the range's end first, then the one at its
+  // start, then the whole sequences between.  A cut sequence's two pieces
+  // are then both done early by their workgroups, so the publication round
+  // trips and the last arrival's merge overlap streaming instead of adding to
+  // every workgroup's tail, which ends on plain writes.
+  // (one call site, so the attention body is instantiated once)
+  const bool end_cut = b_last != b && s_prefix[b_last + 1] > B1;
+  int phase = end_cut ? 0 : 1, cur = b;
+  while (true) {
+    int bb;
+    if (phase == 0) {  // the end piece
+      bb = b_last;
+      phase = 1;
+    } else if (phase == 1) {  // the first sequence
+      bb = b;
+      phase = 2;
+    } else if (phase == 2) {  // the sequences between, skipping empty contexts
+      do {
+        ++cur;
+      } while (cur < b_last && s_prefix[cur + 1] == s_prefix[cur]);
+      if (cur >= b_last) {
+        phase = 3;
+        continue;
+      }
+      bb = cur;
+    } else if (phase == 3 && b_last != b && !end_cut) {  // the last sequence, whole or cut at the start
+      bb = b_last;
+      phase = 4;
+    } else {
+      break;
+    }
+    one(bb);
   }
 }
 
