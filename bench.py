@@ -22,6 +22,7 @@ from __future__ import annotations
 import argparse
 import hashlib
 import json
+import re
 import os
 import sys
 import time
@@ -75,11 +76,19 @@ def decode_kernel_name(p: wl.Problem, partition: int) -> str:
     return f"{kind} ({kv}, head_dim {p.head_dim}, {rows} rows per KV head{mask}, {mode})"
 
 
+def code_only(text: str) -> str:
+    """Source text without comments and blank space: what the compiler sees of it, so that
+    editing a comment does not retire counter figures taken on the same kernel."""
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return " ".join(text.split())
+
+
 def kernel_source_hash(sources=KERNEL_SOURCES) -> str:
     h = hashlib.sha256()
     for f in sources:
-        with open(os.path.join(ROOT, "paged_kv_attention_decode_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(ROOT, "paged_kv_attention_decode_amd", "csrc", f), encoding="utf-8") as fh:
+            h.update(code_only(fh.read()).encode())
     return h.hexdigest()[:16]
 
 

@@ -1,6 +1,7 @@
-// Paged decode attention on the matrix cores (bf16), for 9 to 64 query rows per
-// KV head, e.g. the K + 1 tokens of a speculative verify step times the GQA
-// group.  Same computation and contract as the vector-ALU kernel (include/pa.h):
+// Paged decode attention on the matrix cores (bf16 products), for 8 to 64
+// query rows per KV head over bf16 caches, e.g. the K + 1 tokens of a
+// speculative verify step times the GQA group, and for every row count from 1
+// to 64 over fp8 caches (KV8) and for tree verify (TREE).  Same computation and contract as the vector-ALU kernel (include/pa.h):
 // for each sequence b, KV head g and query row r = j * group + hh,
 //   out = sum_t softmax_t(scale * q . k_t) v_t   over the positions row r sees,
 // with the causal mask among the q_len new tokens ("07 - Inference",
