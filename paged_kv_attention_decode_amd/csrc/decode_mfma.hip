@@ -50,18 +50,6 @@ namespace {
 
 constexpr int kWaves = 4;
 constexpr float kOverflowSlack = 64.0f;  // log2 units
-constexpr int kBufferWord3 = 0x00020000;
-
-typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x2_t2 __attribute__((ext_vector_type(2)));
-typedef short short4_t __attribute__((ext_vector_type(4)));
-typedef float floatx4_t __attribute__((ext_vector_type(4)));
-typedef float float2_t __attribute__((ext_vector_type(2)));
-
-__device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
-  return __builtin_bit_cast(uint32_t, __builtin_convertvector((float2_t){lo, hi}, bf16x2_t2));
-}
-
 template <int R, int D>
 struct MergeTile {
   float m[R];      // merged row max (log2 units)

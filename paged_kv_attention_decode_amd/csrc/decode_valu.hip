@@ -57,8 +57,6 @@ namespace {
 
 constexpr int kWaves = 4;
 constexpr float kOverflowSlack = 64.0f;  // log2 units
-// buffer descriptor word 3 for the gfx9 family (raw 32-bit access, no swizzle)
-constexpr int kBufferWord3 = 0x00020000;
 
 template <typename T>
 struct Elem;
@@ -96,13 +94,6 @@ __device__ __forceinline__ void bcast_in_row(float (&pr)[R], const float (&p)[R]
 // x as held by lane src (any lane of the wave)
 __device__ __forceinline__ float lane_from(float x, int src) {
   return __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(src << 2, __builtin_bit_cast(int, x)));
-}
-
-typedef float float2_v __attribute__((ext_vector_type(2)));
-
-// (lo, hi) rounded to bf16 (round to nearest even), as one packed dword
-__device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
-  return __builtin_bit_cast(uint32_t, __builtin_convertvector((float2_v){lo, hi}, bf16x2_t));
 }
 
 template <typename T, int D, int R, int NW>

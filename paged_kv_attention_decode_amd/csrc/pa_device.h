@@ -10,6 +10,18 @@ constexpr int kBlockTokens = 16;
 constexpr float kNegInf = -__builtin_inff();
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));   // MFMA bf16 operands (16x16x32)
+typedef short short4_t __attribute__((ext_vector_type(4)));    // MFMA bf16 operands (16x16x16)
+typedef float floatx4_t __attribute__((ext_vector_type(4)));   // MFMA 16x16 accumulators
+typedef float float2_t __attribute__((ext_vector_type(2)));
+
+// buffer descriptor word 3 on gfx950: raw 32-bit access, no swizzle
+constexpr int kBufferWord3 = 0x00020000;
+
+// (lo, hi) rounded to bf16 (round to nearest even), as one packed dword (v_cvt_pk_bf16_f32)
+__device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((float2_t){lo, hi}, bf16x2_t));
+}
 
 // bf16 halves of a packed dword, widened exactly to fp32
 __device__ __forceinline__ float bf16_lo(uint32_t u) { return __builtin_bit_cast(float, u << 16); }

@@ -46,17 +46,6 @@ constexpr float kOverflowSlack = 64.0f;  // log2 units
 constexpr int kXcds = 8;  // accelerator complex dies of an MI355X
 constexpr int kStepBlocks = 4;           // blocks staged per step (per barrier), multiplied two at a time
 constexpr int kPrefetch = 1;             // steps whose global loads are in flight
-constexpr int kBufferWord3 = 0x00020000;  // buffer descriptor word 3 on gfx950: raw 32-bit loads
-
-typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x2_p __attribute__((ext_vector_type(2)));
-typedef short short4_t __attribute__((ext_vector_type(4)));
-typedef float floatx4_t __attribute__((ext_vector_type(4)));
-typedef float float2_t __attribute__((ext_vector_type(2)));
-
-__device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
-  return __builtin_bit_cast(uint32_t, __builtin_convertvector((float2_t){lo, hi}, bf16x2_p));
-}
 
 // one block of one KV head in LDS; rows padded by 16 bytes so that the 16
 // token rows one K read touches fall in different banks
