@@ -306,7 +306,8 @@ def main(argv=None):
     ap.add_argument("--partition", type=int, default=None, help="override the context split (0 = one pass)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the cpu_baseline leg")
     ap.add_argument("--cold", type=int, default=0,
-                    help="also time this many decode launches one by one, each after a 1 GiB cache flush")
+                    help="also time this many decode launches one by one, each after reading 1 GiB "
+                         "(evicts L2 and MALL)")
     ap.add_argument("--op", default="decode", choices=["decode", "copy-blocks", "swap-out", "swap-in"],
                     help="decode: the whole path (default); copy-blocks: pa_copy_blocks of 2048 blocks within "
                          "the pool; swap-out / swap-in: the same 2048 blocks to / from pinned host memory")
@@ -374,18 +375,22 @@ def main(argv=None):
     write_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in bev]))
     reduce_ms = float(np.mean([e[2].elapsed_time(e[3]) for e in bev])) if partition > 0 else 0.0
 
-    # cold-cache decode launches: a 1 GiB write between launches evicts L2 and MALL
+    # cold-cache decode launches: a 1 GiB read between launches evicts L2 and MALL.  A read,
+    # not a write: the lines a write leaves dirty would be written back during the timed
+    # launch (measured: +45-60 us on every workload), which times the flush, not the decode.
     cold_ms = None
     if args.cold > 0:
-        scratch = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
+        scratch = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
+        scratch.sum()
+        torch.cuda.synchronize()
         times = []
         for _ in range(args.cold):
-            scratch.fill_(1.0)
+            scratch.sum()
             a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             a.record()
             r.decode()
-            b.record()
             r.reduce()
+            b.record()
             torch.cuda.synchronize()
             times.append(a.elapsed_time(b))
         cold_ms = float(np.median(times))
