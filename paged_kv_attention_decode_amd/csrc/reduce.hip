@@ -10,7 +10,9 @@
 //
 // One workgroup of 256 threads per query row: every thread owns 4 columns of
 // one partition slot; the slots stride over the partitions and are summed in
-// a fixed order at the end, so the result is deterministic.
+// a fixed order at the end, so the result is deterministic.  A slot's loads of
+// kBatch partitions are all issued before any is used (one memory round trip
+// per batch, not per partition).
 #include "pa_device.h"
 #include "pa_kernels.h"
 
@@ -18,12 +20,13 @@ namespace pa {
 namespace {
 
 constexpr int kThreads = 256;
+constexpr int kBatch = 8;
 
 template <typename T, int D>
 __global__ __launch_bounds__(kThreads) void reduce_kernel(ReduceParams a) {
   constexpr int TPR = D / 4;             // threads per partial row (4 columns each)
   constexpr int SLOTS = kThreads / TPR;  // partitions in flight per pass
-  __shared__ float s_red[kThreads];
+  __shared__ float s_red[kThreads / 64];
   __shared__ float4 s_acc[SLOTS][TPR];
   __shared__ float s_w[SLOTS];
 
@@ -40,29 +43,46 @@ __global__ __launch_bounds__(kThreads) void reduce_kernel(ReduceParams a) {
   const float* __restrict__ l = a.ws_l + rr * a.num_parts;
   const float4* __restrict__ o = reinterpret_cast<const float4*>(a.ws_o + rr * a.num_parts * D);
 
+  // M: each thread's partitions, then the wave, then the waves (max is exact in any order)
   float M = kNegInf;
   for (int p = tid; p < nparts; p += kThreads) M = fmaxf(M, m[p]);
-  s_red[tid] = M;
+  M = wave_max(M);
+  if ((tid & 63) == 0) s_red[tid >> 6] = M;
   __syncthreads();
-  for (int stride = kThreads / 2; stride > 0; stride >>= 1) {
-    if (tid < stride) s_red[tid] = fmaxf(s_red[tid], s_red[tid + stride]);
-    __syncthreads();
-  }
   M = s_red[0];
+#pragma unroll
+  for (int u = 1; u < kThreads / 64; ++u) M = fmaxf(M, s_red[u]);
 
   const int slot = tid / TPR, cg = tid % TPR;
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
   float wsum = 0.0f;
   if (M != kNegInf) {
-#pragma unroll 4
-    for (int p = slot; p < nparts; p += SLOTS) {
-      const float f = l[p] * fast_exp2(m[p] - M);
-      const float4 x = o[(size_t)p * TPR + cg];
-      acc.x = fmaf(f, x.x, acc.x);
-      acc.y = fmaf(f, x.y, acc.y);
-      acc.z = fmaf(f, x.z, acc.z);
-      acc.w = fmaf(f, x.w, acc.w);
-      wsum += f;
+    for (int p0 = slot; p0 < nparts; p0 += SLOTS * kBatch) {
+      float mm[kBatch], ll[kBatch];
+      float4 x[kBatch];
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) {
+        const int p = p0 + SLOTS * u;
+        mm[u] = kNegInf;
+        ll[u] = 0.0f;
+        x[u] = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (p < nparts) {
+          mm[u] = m[p];
+          ll[u] = l[p];
+          x[u] = o[(size_t)p * TPR + cg];
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) {
+        if (p0 + SLOTS * u < nparts) {
+          const float f = ll[u] * fast_exp2(mm[u] - M);
+          acc.x = fmaf(f, x[u].x, acc.x);
+          acc.y = fmaf(f, x[u].y, acc.y);
+          acc.z = fmaf(f, x[u].z, acc.z);
+          acc.w = fmaf(f, x[u].w, acc.w);
+          wsum += f;
+        }
+      }
     }
   }
   s_acc[slot][cg] = acc;
