@@ -14,6 +14,12 @@ TOL = {
 }
 
 
+# Two GPU results (different schedules of one call) are each within about one bf16 unit of
+# the exact value, so their agreement is held to a tighter gate than the oracle's:
+# |a - b| <= 1e-3 + 1e-2 |b| (decode outputs are of order 0.03) and relative L2 5e-3.
+SCHEDULE_GATE = dict(atol=1e-3, rtol=1e-2, rel_l2=5e-3)
+
+
 def parity(got: np.ndarray, ref: np.ndarray, dtype: str, atol=None, rtol=None, rel_l2=None) -> dict:
     t = dict(TOL[dtype])
     if atol is not None:

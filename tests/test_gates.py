@@ -9,6 +9,10 @@ KV head h mod n_kv instead of h // G), and, where contexts are short enough
 for one token to matter (up to about 2,300 tokens at d = 128), a context one
 token short.  The workloads keep their head shapes and length ranges with
 fewer sequences, so the CPU suite stays fast.
+
+The tighter gate between two schedules of one call (SCHEDULE_GATE) is shown
+to reject a piece of a cut sequence lost or merged twice, and one lost block
+of 16 tokens, and to accept an exact re-partitioning of the same rows.
 """
 
 import numpy as np
@@ -16,7 +20,7 @@ import pytest
 
 import oracle
 import workloads as wl
-from _gpu import parity
+from _gpu import parity, widen
 from oracle import attention as oa
 from oracle import tree as ot
 
@@ -76,3 +80,53 @@ def test_gate_rejects_a_context_one_token_short(name, max_len, monkeypatch):
     wrong = reference(p, rows)
     monkeypatch.undo()
     assert not parity(wrong, ref, p.dtype)["ok"], "a context one token short passes the gate"
+
+
+# The full-size schedule test (tests/test_gpu_parity.py) compares every row of one
+# schedule with another under SCHEDULE_GATE.  What it must catch: a piece of a cut sequence
+# lost or merged twice (a balanced merge or pa_reduce mistake), or one block of 16 tokens
+# lost.  Simulated here with the oracle's own partials and merge on rows of the 8B layer's
+# shape, both sides rounded to bf16 as the GPU outputs are.
+def _rows_through_partials(p, rows, partition_size, edit=None):
+    from oracle import attention as oa
+
+    G = p.spec.group
+    out = []
+    for (b, j, h) in rows:
+        L = int(p.context_lens[b])
+        g = oa.kv_head_of(h, G)
+        K = oa.to_f64(oa.gather_sequence(p.k_cache, p.block_tables[b], L)[:, g], p.dtype)
+        V = oa.to_f64(oa.gather_sequence(p.v_cache, p.block_tables[b], L)[:, g], p.dtype)
+        qv = oa.to_f64(p.q[b * p.q_len + j, h], p.dtype)
+        ms, ls, accs = oa.partition_partials(qv, K, V, float(np.float32(p.scale)),
+                                             oa.visible_tokens(L, p.q_len, j), L, partition_size)
+        if edit is not None:
+            ms, ls, accs = edit(ms, ls, accs)
+        out.append(oa.merge_partials(ms, ls, accs))
+    return widen(wl.round_to_bf16_bits(np.asarray(out, dtype=np.float32)), "bf16")
+
+
+def _drop(k):
+    return lambda ms, ls, accs: (np.delete(ms, k), np.delete(ls, k), np.delete(accs, k, axis=0))
+
+
+def _double(k):
+    return lambda ms, ls, accs: (np.append(ms, ms[k]), np.append(ls, ls[k]), np.vstack([accs, accs[k:k + 1]]))
+
+
+@pytest.mark.parametrize("mistake", ["piece_lost", "piece_doubled", "block_lost"])
+def test_schedule_gate_rejects_a_lost_or_doubled_piece(mistake):
+    from _gpu import SCHEDULE_GATE
+
+    p = shape_of("llama3-8b-decode")
+    rows = rows_of(p, n=16, seed=1)
+    full = _rows_through_partials(p, rows, 512)
+    # another exact partitioning of the same rows passes (both are the exact value, rounded)
+    assert parity(_rows_through_partials(p, rows, 1024), full, p.dtype, **SCHEDULE_GATE)["ok"]
+    if mistake == "piece_lost":
+        bad = _rows_through_partials(p, rows, 512, _drop(1))
+    elif mistake == "piece_doubled":
+        bad = _rows_through_partials(p, rows, 512, _double(1))
+    else:
+        bad = _rows_through_partials(p, rows, 16, _drop(3))
+    assert not parity(bad, full, p.dtype, **SCHEDULE_GATE)["ok"], mistake
