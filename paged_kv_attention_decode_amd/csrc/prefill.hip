@@ -14,17 +14,19 @@
 // rows (new token x head of the GQA group, token-major) of one sequence and
 // KV head, 32 rows per wave, and all four waves walk the same KV blocks.
 // Each block (16 tokens of K and of V for the head) is staged once per
-// workgroup in LDS, double-buffered (the next block's global loads are in
-// flight while the current one is multiplied), and every wave reads it from
-// there:
+// workgroup in LDS, 4 blocks per step, double-buffered (the next step's
+// global loads are in flight while the current one is multiplied), and every
+// wave reads it from there:
 //
 //   scores  S^T = K_blk Q^T per 16-row tile, v_mfma_f32_16x16x32_bf16 with
 //           A = K from LDS (lane l: token l % 16, 8 dims) and B = the wave's
 //           query rows, which stay in registers for the whole sweep; lane l
 //           ends with tokens 4 (l / 16) .. + 3 of row l % 16;
-//   values  O += P V, v_mfma_f32_16x16x16_bf16 with A = P in that same
-//           layout and B = V: a lane reads 4 columns of each of its 4 tokens
-//           from LDS and a v_perm_b32 4 x 4 transpose forms the operands.
+//   values  O += P V over two blocks at a time, v_mfma_f32_16x16x32_bf16
+//           with A = P in that same layout (k-slots: the lane's 4 tokens of
+//           each block) and B = V read with the transposing LDS load
+//           ds_read_b64_tr_b16, which hands lane l the 4 tokens of one value
+//           column directly; call t covers columns 16 t + l % 16.
 //
 // The softmax takes each row's maximum over block 0 (every row sees position
 // 0) as a fixed reference; a score more than 2^64 above it raises a flag, and
@@ -269,17 +271,23 @@ __global__ __launch_bounds__(kThreads, TW <= 2 ? 2 : 1) void prefill_kernel(Pref
           big |= t[bb][tt][v] > thr[tt];
         }
     if (mode == 0) overflow |= __builtin_amdgcn_ballot_w64(big) != 0;
-    // B operands of P V (16x16x32): k-slots 0-3 are tokens 4 grp + 0..3 of block 0, slots 4-7 the
-    // same tokens of block 1; column 4 j + 64 h + e; bf16 pairs by v_perm_b32 from the lane's reads
-    // of 4 columns of each of its 8 tokens
-    uint2 vb[2][4][VH];
+    // B operands of P V (16x16x32): k-slots 0-3 are tokens 4 grp + 0..3 of block 0, slots 4-7
+    // the same tokens of block 1; call (h, e) covers value columns 16 (4 h + e) + n.  Read with
+    // the transposing LDS load (ds_read_b64_tr_b16): within each 16-lane group, output lane
+    // 4 q + k takes element k of the 8 bytes addressed by lane 4 e' + q as its element e'.
+    // Lane s of the group (s = j) addresses token 4 grp + s / 4, columns 16 t + 4 (s % 4) .. + 3,
+    // so lane (j, grp) receives tokens 4 grp + 0..3 of column 16 t + j: its operand half,
+    // with no permutes.
+    short4_t vt4[2][VH][4];
 #pragma unroll
     for (int bb = 0; bb < 2; ++bb)
 #pragma unroll
-      for (int v = 0; v < 4; ++v)
+      for (int h = 0; h < VH; ++h)
 #pragma unroll
-        for (int h = 0; h < VH; ++h)
-          vb[bb][v][h] = *reinterpret_cast<const uint2*>(&st[buf][sl + bb].v[4 * grp + v][4 * j + 64 * h]);
+        for (int e = 0; e < 4; ++e) {
+          const uint16_t* src = &st[buf][sl + bb].v[4 * grp + (j >> 2)][16 * (4 * h + e) + 4 * (j & 3)];
+          vt4[bb][h][e] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) short4_t*)src);
+        }
 #pragma unroll
     for (int tt = 0; tt < TW; ++tt) {
       uint4 pa;
@@ -295,13 +303,8 @@ __global__ __launch_bounds__(kThreads, TW <= 2 ? 2 : 1) void prefill_kernel(Pref
       for (int h = 0; h < VH; ++h)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
-          const bool hi = e >= 2;
-          uint4 vt;
-          vt.x = __builtin_amdgcn_perm(hi ? vb[0][1][h].y : vb[0][1][h].x, hi ? vb[0][0][h].y : vb[0][0][h].x, sel);
-          vt.y = __builtin_amdgcn_perm(hi ? vb[0][3][h].y : vb[0][3][h].x, hi ? vb[0][2][h].y : vb[0][2][h].x, sel);
-          vt.z = __builtin_amdgcn_perm(hi ? vb[1][1][h].y : vb[1][1][h].x, hi ? vb[1][0][h].y : vb[1][0][h].x, sel);
-          vt.w = __builtin_amdgcn_perm(hi ? vb[1][3][h].y : vb[1][3][h].x, hi ? vb[1][2][h].y : vb[1][2][h].x, sel);
+          const uint2 v0 = __builtin_bit_cast(uint2, vt4[0][h][e]), v1 = __builtin_bit_cast(uint2, vt4[1][h][e]);
+          const uint4 vt = make_uint4(v0.x, v0.y, v1.x, v1.y);
           acc[tt][h][e] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, pa),
                                                                   __builtin_bit_cast(bf16x8_t, vt), acc[tt][h][e], 0,
                                                                   0, 0);
@@ -370,7 +373,8 @@ __global__ __launch_bounds__(kThreads, TW <= 2 ? 2 : 1) void prefill_kernel(Pref
     x += shfl_xor(x, 32);
     lsum[tt] = x;
   }
-  // output: lane l holds rows 4 (l / 16) + i of each tile, columns 4 (l % 16) + 64 h + e
+  // output: lane l holds rows 4 (l / 16) + i of each tile, columns 64 h + 16 e + l % 16
+  // (the 16 lanes of a group write 32 contiguous bytes per column group)
   uint16_t* __restrict__ op = static_cast<uint16_t*>(a.out);
 #pragma unroll
   for (int tt = 0; tt < TW; ++tt) {
@@ -382,17 +386,12 @@ __global__ __launch_bounds__(kThreads, TW <= 2 ? 2 : 1) void prefill_kernel(Pref
       const int row = wr0 + 16 * tt + rr;
       if (row >= r_end) continue;
       const int tok = row / a.group, hh = row % a.group;
-      uint16_t* dst = op + (((size_t)q0 + tok) * a.n_h + (size_t)g * a.group + hh) * D + 4 * j;
+      uint16_t* dst = op + (((size_t)q0 + tok) * a.n_h + (size_t)g * a.group + hh) * D + j;
 #pragma unroll
-      for (int h = 0; h < VH; ++h) {
-        float o[4];
+      for (int h = 0; h < VH; ++h)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) o[e] = l > 0.0f ? acc[tt][h][e][i] / l : 0.0f;
-        uint2 packed;
-        packed.x = f32_to_bf16_bits(o[0]) | (f32_to_bf16_bits(o[1]) << 16);
-        packed.y = f32_to_bf16_bits(o[2]) | (f32_to_bf16_bits(o[3]) << 16);
-        *reinterpret_cast<uint2*>(dst + 64 * h) = packed;
-      }
+        for (int e = 0; e < 4; ++e)
+          dst[64 * h + 16 * e] = (uint16_t)f32_to_bf16_bits(l > 0.0f ? acc[tt][h][e][i] / l : 0.0f);
     }
   }
 }
