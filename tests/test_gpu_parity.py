@@ -440,3 +440,29 @@ def test_full_size_schedules_agree_on_every_row(name):
         r = parity(outs[ps], outs[0], p.dtype, **SCHEDULE_GATE)
         say(f"{name}: partition {ps} against one pass: {r}")
         assert r["ok"], (name, ps, r)
+
+
+def test_concurrent_calls_on_two_streams_with_their_own_workspaces():
+    """Two balanced decodes of different batches, launched on two streams at once, each with
+    its own workspace (the contract only forbids sharing one): each equals, bit for bit, the
+    same call made alone."""
+    import torch
+
+    import paged_kv_attention_decode_amd as pa
+
+    probs = [wl.make_problem(INV_SPEC.with_(num_seqs=n, lens=("uniform", 2, 3000), max_len=3008, seed=s))
+             for n, s in ((40, 11), (33, 12))]
+    devs = [DeviceProblem(p) for p in probs]
+    alone = [to_host(d.step(-1).clone()) for d in devs]
+    outs = [torch.empty_like(d.q) for d in devs]
+    wss = [pa.new_workspace(d.q, d.k_cache, d.block_tables, p.q_len, -1) for d, p in zip(devs, probs)]
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    torch.cuda.synchronize()
+    for _ in range(3):
+        for d, p, o, ws, st in zip(devs, probs, outs, wss, streams):
+            with torch.cuda.stream(st):
+                pa.decode(d.q, d.k_cache, d.v_cache, d.block_tables, d.context_lens, float(p.scale), p.q_len, -1,
+                          out=o, workspace=ws)
+        torch.cuda.synchronize()
+        for a, o in zip(alone, outs):
+            assert np.array_equal(a, to_host(o))
