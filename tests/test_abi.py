@@ -80,6 +80,8 @@ def _decode(lib, **kw):
     (dict(bs=32), 3),
     (dict(dt=7), 3),
     (dict(n_h=18, n_kv=2), 3),          # 9 rows per KV head in fp32
+    (dict(n_h=18, n_kv=2, q_len=8, dt=pa.PA_BF16), 3),  # 72 rows per KV head in bf16 (at most 64)
+    (dict(n_h=130, n_kv=2, dt=pa.PA_BF16), 3),          # 65 rows per KV head in bf16
     (dict(ps=512, ws=None), 4),
     (dict(ps=512, ws=FAKE, wsb=16), 4),
     (dict(ps=-1, ws=None), 4),

@@ -118,6 +118,8 @@ SMALL_BF16 = [
     # 8 to 64 rows per KV head: the matrix-core kernel, 1 to 4 row tiles
     dict(G=8, d=128, q_len=2), dict(G=2, d=128, q_len=5), dict(G=8, d=128, q_len=5), dict(G=8, d=64, q_len=5),
     dict(G=5, d=128, q_len=7), dict(G=16, d=128, q_len=4), dict(G=16, d=64, q_len=4), dict(G=12, d=128, q_len=5),
+    # the longest causal verify the ABI takes (q_len 8): 64 rows, and 8 rows of one head
+    dict(G=8, d=128, q_len=8), dict(G=1, d=64, q_len=8),
 ]
 
 
