@@ -66,7 +66,7 @@ def partition_for(p: wl.Problem) -> int:
 def decode_kernel_name(p: wl.Problem, partition: int) -> str:
     if p.query_start is not None:
         return (f"prefill_kernel (bf16, head_dim {p.head_dim}, {p.spec.group} query heads per KV head, "
-                f"up to {int(p.q_counts.max())} new tokens per sequence, 128 query rows per workgroup)")
+                f"up to {int(p.q_counts.max())} new tokens per sequence, 256 query rows per workgroup)")
     rows = p.spec.group * p.q_len
     fp8 = p.spec.kv == "fp8"
     kind = "decode_mfma_kernel" if fp8 or (p.dtype == "bf16" and rows >= 8) else "decode_valu_kernel"

@@ -318,9 +318,9 @@ pa_status pa_decode_tree(void* out, const void* q, const void* k_cache, const vo
  *   max_q_len     an upper bound of every n_b (1 .. 2^20); sizes the grid.
  *   dtype         PA_BF16.  head_dim 64 or 128, block_size 16.
  *
- * Each workgroup owns 128 query rows (new token x query head of one KV head's
+ * Each workgroup owns 256 query rows (new token x query head of one KV head's
  * group) and walks the sequence's blocks up to the last position those rows
- * see, staging each block once in LDS for its four waves; the products run on
+ * see, staging each block once in LDS for its eight waves; the products run on
  * the matrix cores with fp32 accumulation, the softmax weights rounded to bf16
  * for P V as in pa_decode.  No workspace; results are bitwise deterministic
  * and do not depend on the other sequences of the call.

@@ -20,7 +20,7 @@ struct PrefillParams {
 };
 
 // query rows (new token x head of the GQA group) per workgroup
-constexpr int kPrefillRowsPerWG = 128;
+constexpr int kPrefillRowsPerWG = 256;
 
 hipError_t launch_prefill(const PrefillParams& p, int head_dim, hipStream_t s);
 

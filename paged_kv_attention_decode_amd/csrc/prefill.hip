@@ -10,9 +10,10 @@
 // chunks and single decode tokens can share it.
 //
 // With hundreds of query rows per KV head the products are dense, so the
-// layout is the reverse of the decode kernels': a workgroup owns 128 query
+// layout is the reverse of the decode kernels': a workgroup owns 256 query
 // rows (new token x head of the GQA group, token-major) of one sequence and
-// KV head, 32 rows per wave, and all four waves walk the same KV blocks.
+// KV head, 32 rows per wave, and all eight waves (two per SIMD, one
+// workgroup per CU) walk the same KV blocks.
 // Each block (16 tokens of K and of V for the head) is staged once per
 // workgroup in LDS, 4 blocks per step, double-buffered (the next step's
 // global loads are in flight while the current one is multiplied), and every
@@ -39,7 +40,7 @@
 namespace pa {
 namespace {
 
-constexpr int kWaves = 4;
+constexpr int kWaves = 8;
 constexpr int kThreads = kWaves * 64;
 constexpr int kRowsPerWave = kPrefillRowsPerWG / kWaves;
 constexpr int TW = kRowsPerWave / 16;  // 16-row MFMA tiles per wave
@@ -58,13 +59,13 @@ struct Stage {
 };
 
 template <int D>
-__global__ __launch_bounds__(kThreads, TW <= 2 ? 2 : 1) void prefill_kernel(PrefillParams a) {
+__global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillParams a) {
   constexpr int KS = D / 32;                          // score k-steps
   constexpr int VH = D / 64;                          // value column halves
   constexpr int CH = D / 8;                           // 16-byte chunks per token row of the head
   constexpr int NCHUNK = 2 * kBlockTokens * CH;       // K and V chunks of one block
   constexpr int LOADS = (NCHUNK + kThreads - 1) / kThreads;
-  static_assert(NCHUNK % kThreads == 0, "every thread stages the same number of chunks");
+  constexpr bool kRagged = NCHUNK % kThreads != 0;  // d 64: half the threads stage nothing
 
   __shared__ Stage<D> st[2][kStepBlocks];  // [buffer][block of the step]
   __shared__ int s_overflow;
@@ -175,6 +176,7 @@ __global__ __launch_bounds__(kThreads, TW <= 2 ? 2 : 1) void prefill_kernel(Pref
           __builtin_amdgcn_make_buffer_rsrc((void*)(vbase + boff), (short)0, valid * (int)tok_stride, kBufferWord3);
 #pragma unroll
       for (int u = 0; u < LOADS; ++u) {
+        if (kRagged && threadIdx.x + u * kThreads >= NCHUNK) continue;  // wave-uniform
         const bool is_k = w * 64 + u * kThreads < kBlockTokens * CH;  // wave-uniform
         r[bb][u] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(is_k ? kr : vr, voff[u], 0, 0));
       }
@@ -186,6 +188,7 @@ __global__ __launch_bounds__(kThreads, TW <= 2 ? 2 : 1) void prefill_kernel(Pref
 #pragma unroll
       for (int u = 0; u < LOADS; ++u) {
         const int c = threadIdx.x + u * kThreads;
+        if (kRagged && c >= NCHUNK) continue;
         const int rem = c % (kBlockTokens * CH);
         const int tok = rem / CH, part = rem % CH;
         uint16_t* dst = c < kBlockTokens * CH ? &st[buf][bb].k[tok][8 * part] : &st[buf][bb].v[tok][8 * part];

@@ -4,7 +4,7 @@ Gate: the bf16 tolerance |gpu - ref| <= 2e-2 + 1e-2 |ref| and relative L2
 <= 5e-3 against oracle.paged_prefill on the same seeded inputs (the new
 tokens' K/V written by pa_cache_write first), over mixes of prefill chunks,
 single decode tokens and empty entries, GQA groups 1-8, head_dim 64/128,
-chunks that span several 128-row workgroups with ragged tails; exact
+chunks that span several 256-row workgroups with ragged tails; exact
 properties: a prompt fed in chunks gives the rows of a single prefill bit for
 bit, physical block ids do not matter, NaN in rows never read does not leak,
 malformed query_start entries leave their rows untouched.
@@ -86,7 +86,8 @@ def check(p, what):
 CASES = [
     dict(counts=(40, 1, 200, 0, 33), lens=(40, 300, 520, 7, 33), G=4, d=128),  # from scratch, decode, deep chunk
     dict(counts=(64, 64, 1, 1), lens=(64, 700, 65, 9), G=8, d=128),
-    dict(counts=(129, 17), lens=(400, 17), G=1, d=128),                       # rows cross workgroups
+    dict(counts=(129, 17), lens=(400, 17), G=1, d=128),                       # waves without rows
+    dict(counts=(300, 17), lens=(420, 17), G=1, d=128),                       # rows cross workgroups
     dict(counts=(96, 5, 50), lens=(96, 250, 170), G=4, d=64),
     dict(counts=(31, 100), lens=(47, 333), G=3, d=128),                       # a group that does not divide 32
     dict(counts=(16, 16, 16), lens=(16, 32, 48), G=2, d=64),                  # block-aligned
