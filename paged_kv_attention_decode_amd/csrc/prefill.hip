@@ -15,7 +15,7 @@
 // KV head, 32 rows per wave, and all eight waves (two per SIMD, one
 // workgroup per CU) walk the same KV blocks.
 // Each block (16 tokens of K and of V for the head) is staged once per
-// workgroup in LDS, 4 blocks per step, double-buffered (the next step's
+// workgroup in LDS, 8 blocks per step, double-buffered (the next step's
 // global loads are in flight while the current one is multiplied), and every
 // wave reads it from there:
 //
@@ -47,7 +47,7 @@ constexpr int TW = kRowsPerWave / 16;  // 16-row MFMA tiles per wave
 static_assert(kRowsPerWave % 16 == 0, "whole MFMA row tiles per wave");
 constexpr float kOverflowSlack = 64.0f;  // log2 units
 constexpr int kXcds = 8;  // accelerator complex dies of an MI355X
-constexpr int kStepBlocks = 4;           // blocks staged per step (per barrier), multiplied two at a time
+constexpr int kStepBlocks = 8;           // blocks staged per step (per barrier), multiplied two at a time
 constexpr int kPrefetch = 1;             // steps whose global loads are in flight
 
 // one block of one KV head in LDS; rows padded by 16 bytes so that the 16
