@@ -156,18 +156,21 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillParams a) {
     const int rem = (threadIdx.x + u * kThreads) % (kBlockTokens * CH);
     voff[u] = (uint32_t)(rem / CH) * tok_stride + (uint32_t)g * D * 2 + 16u * (uint32_t)(rem % CH);
   }
-  // physical id of logical block blk, -1 when past the range or outside the pool
+  // physical id of logical block blk, -1 when past the range or outside the
+  // pool (no branch: the table read is clamped into the range, nblk >= 1)
   auto phys_of = [&](int blk) -> int {
-    if (blk >= nblk) return -1;
-    const int phys = table[blk];
-    return (unsigned)phys < (unsigned)a.num_blocks ? phys : -1;
+    const int phys = table[min(blk, nblk - 1)];
+    return blk < nblk && (unsigned)phys < (unsigned)a.num_blocks ? phys : -1;
   };
-  // the blocks of step it into registers
-  auto fetch = [&](int it, uint4(&r)[kStepBlocks][LOADS]) {
+  // the blocks of step it into registers; returns bit bb set where block bb of
+  // the step is valid, so that the multiply needs no block-table reads
+  auto fetch = [&](int it, uint4(&r)[kStepBlocks][LOADS]) -> uint32_t {
+    uint32_t okm = 0;
 #pragma unroll
     for (int bb = 0; bb < kStepBlocks; ++bb) {
       const int blk = kStepBlocks * it + bb;
       const int phys = phys_of(blk);
+      okm |= (phys >= 0 ? 1u : 0u) << bb;
       const int valid = phys >= 0 ? min(kBlockTokens, L - blk * kBlockTokens) : 0;
       const size_t boff = phys >= 0 ? (size_t)phys * blk_bytes : 0;
       const __amdgpu_buffer_rsrc_t kr =
@@ -181,6 +184,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillParams a) {
         r[bb][u] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(is_k ? kr : vr, voff[u], 0, 0));
       }
     }
+    return okm;
   };
   auto put = [&](int buf, const uint4(&r)[kStepBlocks][LOADS]) {
 #pragma unroll
@@ -210,16 +214,17 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillParams a) {
 
   bool overflow = false;  // wave-uniform
   const float c = a.scale_log2;
-  // a pair of blocks: blk0 and blk0 + 1, staged in slots sl and sl + 1 of the buffer.
+  // a pair of blocks: blk0 and blk0 + 1, staged in slots sl and sl + 1 of the buffer, valid
+  // where bits 0 and 1 of okb are set.
   // mode 0: reference from the first pair, weighted sums, overflow check; 1: row maxima only;
   // 2: weighted sums
-  auto pair = [&](int blk0, int buf, int sl, int mode) {
+  auto pair = [&](int blk0, int buf, int sl, int mode, uint32_t okb) {
     floatx4_t x[2][TW];  // raw q.k: [block][tile], lane: tokens 4 grp + v of row j
     bool ok[2], whole[2];
 #pragma unroll
     for (int bb = 0; bb < 2; ++bb) {
       const int blk = blk0 + bb;
-      ok[bb] = phys_of(blk) >= 0;
+      ok[bb] = (okb >> bb) & 1u;
       whole[bb] = ok[bb] && (blk + 1) * kBlockTokens <= wave_min_vis;  // every row sees all 16 tokens
 #pragma unroll
       for (int tt = 0; tt < TW; ++tt) {
@@ -233,11 +238,13 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillParams a) {
         x[bb][tt] = acc_s;
       }
     }
-    // scores in log2 units, -inf where masked (only blocks some row of the wave does not fully see)
-    auto score = [&](int bb, int tt, int v) -> float {
+    // whether row j of tile tt sees token 4 grp + v of block bb
+    auto sees = [&](int bb, int tt, int v) -> bool {
       const int pos = (blk0 + bb) * kBlockTokens + 4 * grp + v;
-      return (whole[bb] || (ok[bb] && pos < vis[tt])) ? x[bb][tt][v] * c : kNegInf;
+      return whole[bb] || (ok[bb] && pos < vis[tt]);
     };
+    // scores in log2 units, -inf where masked
+    auto score = [&](int bb, int tt, int v) -> float { return sees(bb, tt, v) ? x[bb][tt][v] * c : kNegInf; };
     if (mode == 1 || (mode == 0 && blk0 == 0)) {
       floatx4_t sm[TW];
 #pragma unroll
@@ -253,7 +260,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillParams a) {
       }
       set_reference(sm);
     }
-    // exponent t = scale q.k - m (one fma where the block is whole), weights 2^t
+    // exponent t = scale q.k - m (one fma; -inf where masked, selected without a branch), weights 2^t
     float t[2][TW][4];
     bool big = false;
     // a row without a reference (nothing seen in step 0) redoes on any weight
@@ -266,11 +273,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillParams a) {
       for (int tt = 0; tt < TW; ++tt)
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
-          if (whole[bb]) {
-            t[bb][tt][v] = __builtin_fmaf(x[bb][tt][v], c, -m_use[tt]);
-          } else {
-            t[bb][tt][v] = score(bb, tt, v) - m_use[tt];
-          }
+          t[bb][tt][v] = sees(bb, tt, v) ? __builtin_fmaf(x[bb][tt][v], c, -m_use[tt]) : kNegInf;
           big |= t[bb][tt][v] > thr[tt];
         }
     if (mode == 0) overflow |= __builtin_amdgcn_ballot_w64(big) != 0;
@@ -315,38 +318,43 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillParams a) {
     }
   };
 
-  // one step: its pairs of blocks, those some row of the wave sees
-  auto compute = [&](int it, int buf, int mode) {
+  // one step: its pairs of blocks, those some row of the wave sees; bit bb of okm is set
+  // where block bb of the step is valid
+  auto compute = [&](int it, int buf, int mode, uint32_t okm) {
 #pragma unroll
     for (int pp = 0; pp < kStepBlocks / 2; ++pp) {
       const int blk0 = kStepBlocks * it + 2 * pp;
       if (!wave_rows || blk0 * kBlockTokens >= wave_end) return;  // wave-uniform
-      pair(blk0, buf, 2 * pp, mode);
+      pair(blk0, buf, 2 * pp, mode, okm >> (2 * pp));
     }
   };
 
   // one pass over the steps.  Global loads run kPrefetch steps ahead in
   // registers (slot it % kPrefetch holds step it); LDS holds two steps: the
-  // one being multiplied and the next one.
+  // one being multiplied and the next one.  okm[k] holds the valid-block bits
+  // of step it + k.
   const int nit = (nblk + kStepBlocks - 1) / kStepBlocks;
   auto sweep = [&](int mode) {
     uint4 r[kPrefetch][kStepBlocks][LOADS];
+    uint32_t okm[kPrefetch + 1];
 #pragma unroll
-    for (int u = 0; u < kPrefetch; ++u)
-      if (u < nit) fetch(u, r[u]);
+    for (int u = 0; u < kPrefetch; ++u) okm[u] = u < nit ? fetch(u, r[u]) : 0u;
     put(0, r[0]);
-    if (kPrefetch < nit) fetch(kPrefetch, r[0]);
+    okm[kPrefetch] = kPrefetch < nit ? fetch(kPrefetch, r[0]) : 0u;
     __syncthreads();
     for (int it0 = 0; it0 < nit; it0 += kPrefetch) {
 #pragma unroll
       for (int u = 0; u < kPrefetch; ++u) {
         const int it = it0 + u;
         if (it >= nit) break;
-        compute(it, it & 1, mode);
+        compute(it, it & 1, mode, okm[0]);
+#pragma unroll
+        for (int k = 0; k < kPrefetch; ++k) okm[k] = okm[k + 1];
+        okm[kPrefetch] = 0u;
         const int nxt = (u + 1) % kPrefetch;  // register slot of step it + 1 (constant once unrolled)
         if (it + 1 < nit) {
           put((it + 1) & 1, r[nxt]);
-          if (it + 1 + kPrefetch < nit) fetch(it + 1 + kPrefetch, r[nxt]);
+          if (it + 1 + kPrefetch < nit) okm[kPrefetch] = fetch(it + 1 + kPrefetch, r[nxt]);
         }
         __syncthreads();  // step it + 1 staged; everyone is done with step it
       }
