@@ -267,15 +267,28 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillParams a) {
     float thr[TW];
 #pragma unroll
     for (int tt = 0; tt < TW; ++tt) thr[tt] = m_ref[tt] == kNegInf ? kNegInf : kOverflowSlack;
+    if (whole[0] && whole[1]) {  // wave-uniform: every row sees both blocks whole
 #pragma unroll
-    for (int bb = 0; bb < 2; ++bb)
+      for (int bb = 0; bb < 2; ++bb)
 #pragma unroll
-      for (int tt = 0; tt < TW; ++tt)
+        for (int tt = 0; tt < TW; ++tt)
 #pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          t[bb][tt][v] = sees(bb, tt, v) ? __builtin_fmaf(x[bb][tt][v], c, -m_use[tt]) : kNegInf;
-          big |= t[bb][tt][v] > thr[tt];
-        }
+          for (int v = 0; v < 4; ++v) t[bb][tt][v] = __builtin_fmaf(x[bb][tt][v], c, -m_use[tt]);
+    } else {
+#pragma unroll
+      for (int bb = 0; bb < 2; ++bb)
+#pragma unroll
+        for (int tt = 0; tt < TW; ++tt)
+#pragma unroll
+          for (int v = 0; v < 4; ++v)
+            t[bb][tt][v] = sees(bb, tt, v) ? __builtin_fmaf(x[bb][tt][v], c, -m_use[tt]) : kNegInf;
+    }
+#pragma unroll
+    for (int tt = 0; tt < TW; ++tt) {
+      const float hi = fmaxf(fmaxf(fmaxf(t[0][tt][0], t[0][tt][1]), fmaxf(t[0][tt][2], t[0][tt][3])),
+                             fmaxf(fmaxf(t[1][tt][0], t[1][tt][1]), fmaxf(t[1][tt][2], t[1][tt][3])));
+      big |= hi > thr[tt];
+    }
     if (mode == 0) overflow |= __builtin_amdgcn_ballot_w64(big) != 0;
     // B operands of P V (16x16x32): k-slots 0-3 are tokens 4 grp + 0..3 of block 0, slots 4-7
     // the same tokens of block 1; call (h, e) covers value columns 16 (4 h + e) + n.  Read with
