@@ -159,12 +159,16 @@ struct MfmaAttender {
     // positions below vis[t] (the tree's start, 0 for padding rows) and the
     // nodes of its path (sm.path)
     int vis[NT];
+    bool real[NT];  // row 16 t + j is a query row, not padding of the tile
     const int tree_base = L - a.q_len;  // tree: position of node 0
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
       const int r = 16 * t + j;
+      real[t] = r < rows;
       vis[t] = r < rows ? (TREE ? tree_base : L - a.q_len + r / a.group + 1) : 0;
     }
+    // every query row sees all positions below this (tree: the context before node 0)
+    const int vis_all = TREE ? tree_base : L - a.q_len + 1;
 
     float m_ref[NT], m_use[NT], lsum[NT];
     floatx4_t acc[NT][VH][4];
@@ -255,8 +259,8 @@ struct MfmaAttender {
       // keep the compiler from hoisting the query reads out of the block loop
       // into registers, which is what the LDS copy avoids
       if constexpr (NT > 1) asm volatile("" ::: "memory");
-#pragma unroll
-      for (int t = 0; t < NT; ++t) {
+      // raw q.k of tile t
+      auto tile = [&](int t) -> floatx4_t {
         floatx4_t x = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
@@ -266,17 +270,37 @@ struct MfmaAttender {
           x = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, k_operand(kb, ks)),
                                                       __builtin_bit_cast(bf16x8_t, qb), x, 0, 0, 0);
         }
-        if constexpr (TREE) {
-          uint64_t path = 0;
-          if (lblk * kBlockTokens + kBlockTokens > tree_base)  // the block reaches into the tree (wave-uniform)
-            path = sm.path[16 * t + j];
+        return x;
+      };
+      if constexpr (TREE) {
+        floatx4_t x[NT];
 #pragma unroll
-          for (int v = 0; v < 4; ++v) {
-            const int rel = pos0 + v - tree_base;  // node index of the position, negative before the tree
-            const bool see = pos0 + v < vis[t] || (rel >= 0 && rel < 64 && ((path >> rel) & 1ull));
-            s[t][v] = (ok && see) ? x[v] * scale_log2 : kNegInf;
-          }
+        for (int t = 0; t < NT; ++t) x[t] = tile(t);
+        // One wave-uniform branch per block: where every query row sees the
+        // whole block only the padding rows are masked; otherwise each score
+        // is checked against its row's context bound and tree path.
+        if (ok && lblk * kBlockTokens + kBlockTokens <= vis_all) {
+#pragma unroll
+          for (int t = 0; t < NT; ++t)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) s[t][v] = real[t] ? x[t][v] * scale_log2 : kNegInf;
         } else {
+#pragma unroll
+          for (int t = 0; t < NT; ++t) {
+            const uint64_t path = sm.path[16 * t + j];
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+              const int rel = pos0 + v - tree_base;  // node index of the position, negative before the tree
+              const bool see = pos0 + v < vis[t] || (rel >= 0 && rel < 64 && ((path >> rel) & 1ull));
+              s[t][v] = (ok && see) ? x[t][v] * scale_log2 : kNegInf;
+            }
+          }
+        }
+      } else {
+        // causal: one select per score (measured no slower than a branch here)
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+          const floatx4_t x = tile(t);
 #pragma unroll
           for (int v = 0; v < 4; ++v) s[t][v] = (ok && pos0 + v < vis[t]) ? x[v] * scale_log2 : kNegInf;
         }
