@@ -212,7 +212,11 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillParams a) {
     }
   };
 
-  bool overflow = false;  // wave-uniform
+  // per lane and tile, the largest exponent of the first sweep, checked against
+  // the overflow threshold once the sweep is done (the reference is fixed by then)
+  float tmax[TW];
+#pragma unroll
+  for (int tt = 0; tt < TW; ++tt) tmax[tt] = kNegInf;
   const float c = a.scale_log2;
   // a pair of blocks: blk0 and blk0 + 1, staged in slots sl and sl + 1 of the buffer, valid
   // where bits 0 and 1 of okb are set.
@@ -262,11 +266,6 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillParams a) {
     }
     // exponent t = scale q.k - m (one fma; -inf where masked, selected without a branch), weights 2^t
     float t[2][TW][4];
-    bool big = false;
-    // a row without a reference (nothing seen in step 0) redoes on any weight
-    float thr[TW];
-#pragma unroll
-    for (int tt = 0; tt < TW; ++tt) thr[tt] = m_ref[tt] == kNegInf ? kNegInf : kOverflowSlack;
     if (whole[0] && whole[1]) {  // wave-uniform: every row sees both blocks whole
 #pragma unroll
       for (int bb = 0; bb < 2; ++bb)
@@ -287,9 +286,8 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillParams a) {
     for (int tt = 0; tt < TW; ++tt) {
       const float hi = fmaxf(fmaxf(fmaxf(t[0][tt][0], t[0][tt][1]), fmaxf(t[0][tt][2], t[0][tt][3])),
                              fmaxf(fmaxf(t[1][tt][0], t[1][tt][1]), fmaxf(t[1][tt][2], t[1][tt][3])));
-      big |= hi > thr[tt];
+      tmax[tt] = fmaxf(tmax[tt], hi);
     }
-    if (mode == 0) overflow |= __builtin_amdgcn_ballot_w64(big) != 0;
     // B operands of P V (16x16x32): k-slots 0-3 are tokens 4 grp + 0..3 of block 0, slots 4-7
     // the same tokens of block 1; call (h, e) covers value columns 16 (4 h + e) + n.  Read with
     // the transposing LDS load (ds_read_b64_tr_b16): within each 16-lane group, output lane
@@ -377,7 +375,11 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillParams a) {
   if (threadIdx.x == 0) s_overflow = 0;
   if (nblk > 0) {
     sweep(0);  // its first barrier also publishes s_overflow = 0
-    if (overflow && lane == 0) s_overflow = 1;
+    // a row without a reference (nothing seen in step 0) redoes on any weight
+    bool big = false;
+#pragma unroll
+    for (int tt = 0; tt < TW; ++tt) big |= tmax[tt] > (m_ref[tt] == kNegInf ? kNegInf : kOverflowSlack);
+    if (__builtin_amdgcn_ballot_w64(big) != 0 && lane == 0) s_overflow = 1;
     __syncthreads();
     if (s_overflow) {  // exact redo: true row maxima, then the weighted sums
       clear();
