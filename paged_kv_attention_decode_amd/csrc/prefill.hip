@@ -220,7 +220,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillParams a) {
   const float c = a.scale_log2;
   // a pair of blocks: blk0 and blk0 + 1, staged in slots sl and sl + 1 of the buffer, valid
   // where bits 0 and 1 of okb are set.
-  // mode 0: reference from the first pair, weighted sums, overflow check; 1: row maxima only;
+  // mode 0: reference from the first pair, weighted sums, largest exponents; 1: row maxima only;
   // 2: weighted sums
   auto pair = [&](int blk0, int buf, int sl, int mode, uint32_t okb) {
     floatx4_t x[2][TW];  // raw q.k: [block][tile], lane: tokens 4 grp + v of row j
