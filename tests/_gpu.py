@@ -14,13 +14,27 @@ TOL = {
 }
 
 
-# Two GPU results (different schedules of one call) are each within about one bf16 unit of
-# the exact value, so their agreement is held to a tighter gate than the oracle's:
-# |a - b| <= 1e-3 + 1e-2 |b| (decode outputs are of order 0.03) and relative L2 5e-3.
-SCHEDULE_GATE = dict(atol=1e-3, rtol=1e-2, rel_l2=5e-3)
+# Every output row (one query token and head, head_dim values) on its own: relative L2
+# against the oracle's row.  The whole-output gates above can hide one wrong row among
+# thousands; a lost or doubled piece of a cut sequence, or one lost block of 16 tokens,
+# moves its rows by 2e-2 to 1 in this measure, while bf16 rounding of the weights and of
+# the output stays near 2e-3 (tests/test_gates.py shows both).  Rows whose reference is
+# zero (nothing visible) are held to an absolute norm of the same size.
+ROW_REL_L2 = 1e-2
 
 
-def parity(got: np.ndarray, ref: np.ndarray, dtype: str, atol=None, rtol=None, rel_l2=None) -> dict:
+def row_rel_l2(got: np.ndarray, ref: np.ndarray) -> np.ndarray:
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    num = np.linalg.norm(got - ref, axis=-1)
+    den = np.linalg.norm(ref, axis=-1)
+    return np.where(den > 0, num / np.where(den > 0, den, 1.0), num)
+
+
+def parity(got: np.ndarray, ref: np.ndarray, dtype: str, atol=None, rtol=None, rel_l2=None,
+           rows: bool = False) -> dict:
+    """The stated elementwise tolerance plus relative L2 over the whole output; with
+    rows=True also ROW_REL_L2 on every row (last axis) for bf16 outputs."""
     t = dict(TOL[dtype])
     if atol is not None:
         t["atol"] = atol
@@ -37,8 +51,47 @@ def parity(got: np.ndarray, ref: np.ndarray, dtype: str, atol=None, rtol=None, r
     denom = float(np.linalg.norm(ref))
     rl2 = float(np.linalg.norm(got - ref) / denom) if denom > 0 else float(np.linalg.norm(got))
     ok = finite and excess <= 0.0 and rl2 <= t["rel_l2"]
-    return dict(ok=ok, finite=finite, max_abs=float(err.max()) if err.size else 0.0, excess=excess, rel_l2=rl2,
-                tol=t)
+    r = dict(ok=ok, finite=finite, max_abs=float(err.max()) if err.size else 0.0, excess=excess, rel_l2=rl2, tol=t)
+    if rows:
+        worst = float(row_rel_l2(got, ref).max()) if err.size else 0.0
+        r["row_rel_l2"] = worst
+        r["ok"] = r["ok"] and worst <= ROW_REL_L2
+    return r
+
+
+class OracleJob:
+    """The oracle's full output for a named workload, computed by tests/_oracle_full.py in a
+    child process (its worker pool never shares state with the process driving the GPU)
+    while the caller runs the GPU side; result() waits for it."""
+
+    def __init__(self, name: str, workers: int = 0):
+        import os
+        import subprocess
+        import sys
+        import tempfile
+
+        if workers <= 0:
+            try:
+                workers = min(16, len(os.sched_getaffinity(0)))
+            except AttributeError:  # pragma: no cover
+                workers = min(16, os.cpu_count() or 1)
+        fd, self.path = tempfile.mkstemp(suffix=".npy")
+        os.close(fd)
+        here = os.path.dirname(os.path.abspath(__file__))
+        self.proc = subprocess.Popen([sys.executable, os.path.join(here, "_oracle_full.py"), name, self.path,
+                                      str(workers)])
+
+    def result(self, timeout: float = 600.0) -> np.ndarray:
+        import os
+
+        try:
+            rc = self.proc.wait(timeout=timeout)
+            assert rc == 0, f"the oracle's child process failed ({rc})"
+            return np.load(self.path)
+        finally:
+            if self.proc.poll() is None:
+                self.proc.kill()
+            os.unlink(self.path)
 
 
 def to_dev(a: np.ndarray, dtype: str, device="cuda"):
@@ -169,3 +222,35 @@ def sample_rows(p: wl.Problem, n: int, seed: int = 0):
         b = sorted(bs)[int(rng.integers(0, len(bs)))]
         rows.add((b, int(rng.integers(0, p.q_len)), int(rng.integers(0, p.num_q_heads))))
     return sorted(rows)
+
+
+def check_full_size_every_row(name: str, say=print) -> dict:
+    """A full-size workload on the GPU in the schedule bench.py times and in the other
+    schedules (one pass, 512-token partitions + pa_reduce, balanced), every output row
+    against the oracle (parity with rows=True), and the cache write's rows bit for bit."""
+    import bench
+
+    job = OracleJob(name)  # the oracle runs beside the GPU work
+    p = wl.make_problem(name)
+    d = DeviceProblem(p)
+    schedules = [bench.partition_for(p)] + [ps for ps in (0, 512, -1) if ps != bench.partition_for(p)]
+    outs = {}
+    for ps in schedules:
+        say(f"{name}: partition {ps}")
+        d.workspace = None  # a fresh workspace per schedule (a split one must not serve a balanced call)
+        outs[ps] = widen(to_host(d.step(ps).clone()), p.dtype)
+        assert np.isfinite(outs[ps]).all(), (name, ps)
+    if p.new_k is not None:  # the cache write, on the rows it touched
+        kc, _ = host_caches_after_write(p)
+        flat = to_host(d.k_cache).reshape(-1, p.num_kv_heads, p.head_dim)
+        want = kc.reshape(-1, p.num_kv_heads, p.head_dim)
+        assert np.array_equal(flat[p.slot_mapping], want[p.slot_mapping]), name
+    say(f"{name}: waiting for the oracle")
+    ref = job.result()
+    results = {}
+    for ps in schedules:
+        r = parity(outs[ps], ref, p.dtype, rows=True)
+        say(f"{name}: partition {ps} against the oracle on every row: {r}")
+        assert r["ok"], (name, ps, r)
+        results[ps] = r
+    return results

@@ -10,9 +10,10 @@ for one token to matter (up to about 2,300 tokens at d = 128), a context one
 token short.  The workloads keep their head shapes and length ranges with
 fewer sequences, so the CPU suite stays fast.
 
-The tighter gate between two schedules of one call (SCHEDULE_GATE) is shown
-to reject a piece of a cut sequence lost or merged twice, and one lost block
-of 16 tokens, and to accept an exact re-partitioning of the same rows.
+The per-row gate of the full-size tests (parity(..., rows=True): relative L2
+of every output row against the oracle's) is shown to reject a piece of a cut
+sequence lost or merged twice, and one lost block of 16 tokens, in a single
+row among many, and to accept an exact re-partitioning of the same rows.
 """
 
 import numpy as np
@@ -82,11 +83,11 @@ def test_gate_rejects_a_context_one_token_short(name, max_len, monkeypatch):
     assert not parity(wrong, ref, p.dtype)["ok"], "a context one token short passes the gate"
 
 
-# The full-size schedule test (tests/test_gpu_parity.py) compares every row of one
-# schedule with another under SCHEDULE_GATE.  What it must catch: a piece of a cut sequence
-# lost or merged twice (a balanced merge or pa_reduce mistake), or one block of 16 tokens
-# lost.  Simulated here with the oracle's own partials and merge on rows of the 8B layer's
-# shape, both sides rounded to bf16 as the GPU outputs are.
+# The full-size tests (tests/_gpu.py check_full_size_every_row) compare every row of every
+# schedule with the oracle.  What they must catch: a piece of a cut sequence lost or merged
+# twice (a balanced merge or pa_reduce mistake), or one block of 16 tokens lost, even in one
+# row of thousands.  Simulated here with the oracle's own partials and merge on rows of the
+# 8B layer's shape, rounded to bf16 as the GPU outputs are.
 def _rows_through_partials(p, rows, partition_size, edit=None):
     from oracle import attention as oa
 
@@ -115,18 +116,26 @@ def _double(k):
 
 
 @pytest.mark.parametrize("mistake", ["piece_lost", "piece_doubled", "block_lost"])
-def test_schedule_gate_rejects_a_lost_or_doubled_piece(mistake):
-    from _gpu import SCHEDULE_GATE
-
+def test_row_gate_rejects_one_row_with_a_lost_or_doubled_piece(mistake):
     p = shape_of("llama3-8b-decode")
     rows = rows_of(p, n=16, seed=1)
-    full = _rows_through_partials(p, rows, 512)
-    # another exact partitioning of the same rows passes (both are the exact value, rounded)
-    assert parity(_rows_through_partials(p, rows, 1024), full, p.dtype, **SCHEDULE_GATE)["ok"]
+    ref = reference(p, rows)
+    exact = _rows_through_partials(p, rows, 512)
+    # an exact partitioning of the same rows, rounded to bf16, passes
+    assert parity(exact, ref, p.dtype, rows=True)["ok"]
+    assert parity(_rows_through_partials(p, rows, 1024), ref, p.dtype, rows=True)["ok"]
+    # the mistake in every row is caught by every gate; in one row only by the per-row gate
     if mistake == "piece_lost":
         bad = _rows_through_partials(p, rows, 512, _drop(1))
     elif mistake == "piece_doubled":
         bad = _rows_through_partials(p, rows, 512, _double(1))
     else:
         bad = _rows_through_partials(p, rows, 16, _drop(3))
-    assert not parity(bad, full, p.dtype, **SCHEDULE_GATE)["ok"], mistake
+    assert not parity(bad, ref, p.dtype, rows=True)["ok"], mistake
+    for i in range(len(rows)):
+        one = exact.copy()
+        one[i] = bad[i]
+        # embedded among 2,048 exact rows (the 8B layer's output), as in the full-size tests
+        big_ref = np.concatenate([ref, np.repeat(ref, 128, axis=0)])
+        big = np.concatenate([one, np.repeat(exact, 128, axis=0)])
+        assert not parity(big, big_ref, p.dtype, rows=True)["ok"], (mistake, i)

@@ -14,7 +14,7 @@ import pytest
 
 import oracle
 import workloads as wl
-from _gpu import SCHEDULE_GATE, DeviceProblem, host_caches_after_write, parity, reference_full, reference_rows, sample_rows, to_host, widen
+from _gpu import check_full_size_every_row, DeviceProblem, host_caches_after_write, parity, reference_full, reference_rows, sample_rows, to_host, widen
 
 pytestmark = pytest.mark.gpu
 
@@ -160,39 +160,7 @@ def test_fp8_one_token_returns_scaled_v():
             np.testing.assert_allclose(got[b, h], want, rtol=2 ** -8, atol=0)
 
 
-def test_fp8_full_size_sampled_rows():
-    import bench
-
-    spec = wl.CONFIGS["llama3-8b-decode-fp8kv"]
-    say("fp8 8B layer: generating")
-    p = wl.make_problem(spec)
-    ps = bench.partition_for(p)
-    d = DeviceProblem(p)
-    out = widen(to_host(d.step(ps)), p.dtype)
-    assert np.isfinite(out).all()
-    kc_dev = d.k_cache.cpu().numpy().reshape(-1, p.num_kv_heads, p.head_dim)
-    kc, vc = host_caches_after_write(p)
-    assert np.array_equal(kc_dev[p.slot_mapping], kc.reshape(-1, p.num_kv_heads, p.head_dim)[p.slot_mapping])
-    rows = sample_rows(p, 48)
-    say(f"fp8 8B layer: oracle on {len(rows)} rows")
-    ref = reference_rows(p, rows, kc, vc)
-    got = np.stack([out[b * p.q_len + j, h] for (b, j, h) in rows])
-    r = assert_parity(got, ref, "llama3-8b-decode-fp8kv")
-    say(f"fp8 8B layer: {r}")
-
-
-def test_fp8_full_size_schedules_agree_on_every_row():
-    """Every output row of the full llama3-8b-decode-fp8kv workload: one pass, 512-token partitions +
-    pa_reduce and balanced agree under the gate for two GPU results (SCHEDULE_GATE)."""
-    p = wl.make_problem("llama3-8b-decode-fp8kv")
-    d = DeviceProblem(p)
-    outs = {}
-    for ps in (0, 512, -1):
-        say(f"llama3-8b-decode-fp8kv: partition {ps}")
-        d.workspace = None  # a fresh workspace per schedule (a split one must not serve a balanced call)
-        outs[ps] = widen(to_host(d.step(ps).clone()), p.dtype)
-        assert np.isfinite(outs[ps]).all()
-    for ps in (512, -1):
-        r = parity(outs[ps], outs[0], p.dtype, **SCHEDULE_GATE)
-        say(f"llama3-8b-decode-fp8kv: partition {ps} against one pass: {r}")
-        assert r["ok"], (ps, r)
+def test_fp8_full_size_every_row():
+    """Every output row of the full llama3-8b-decode-fp8kv workload, in the schedule bench.py times and in the
+    others, against the oracle (stated tolerance, relative L2, and relative L2 per row)."""
+    check_full_size_every_row("llama3-8b-decode-fp8kv", say)

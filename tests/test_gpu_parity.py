@@ -16,7 +16,7 @@ import pytest
 
 import oracle
 import workloads as wl
-from _gpu import SCHEDULE_GATE, DeviceProblem, host_caches_after_write, parity, sample_rows, to_dev, to_host, widen
+from _gpu import DeviceProblem, check_full_size_every_row, host_caches_after_write, parity, sample_rows, to_dev, to_host, widen
 
 pytestmark = pytest.mark.gpu
 
@@ -396,52 +396,12 @@ FULL = ["llama3-8b-decode", "llama3-70b-decode", "long-split", "spec-verify"]
 
 
 @pytest.mark.parametrize("name", FULL)
-def test_full_size_sampled_rows(name):
-    import bench
-
-    spec = wl.CONFIGS[name]
-    say(f"{name}: generating")
-    p = wl.make_problem(spec)
-    ps = bench.partition_for(p)
-    say(f"{name}: GPU path, partition {ps}")
-    d = DeviceProblem(p)
-    out = widen(to_host(d.step(ps)), p.dtype)
-    assert np.isfinite(out).all()
-    # the cache write, checked on the rows it touched
-    if p.new_k is not None:
-        kc = to_host(d.k_cache)
-        flat = kc.reshape(-1, p.num_kv_heads, p.head_dim)
-        assert np.array_equal(flat[p.slot_mapping], p.new_k)
-    rows = sample_rows(p, 48)
-    say(f"{name}: oracle on {len(rows)} rows")
-    kc, vc = host_caches_after_write(p)
-    ref = oracle.paged_decode_rows(p.q, kc, vc, p.block_tables, p.context_lens, p.scale, p.q_len, p.dtype, rows)
-    got = np.stack([out[b * p.q_len + j, h] for (b, j, h) in rows])
-    r = assert_parity(got, ref, p.dtype, name)
-    say(f"{name}: {r}")
-
-
-# every row at full size: the schedules compute one function.  The sampled test above pins
-# each workload's own schedule to the oracle; this one covers the rows it does not sample,
-# where a schedule-specific mistake (a lost or doubled piece of a cut sequence, a partition
-# dropped by pa_reduce) would show as a disagreement between schedules, under the tighter
-# gate SCHEDULE_GATE (tests/_gpu.py; tests/test_gates.py shows it rejects a lost piece).
-
-
-@pytest.mark.parametrize("name", ["llama3-8b-decode", "llama3-70b-decode", "spec-verify"])
-def test_full_size_schedules_agree_on_every_row(name):
-    p = wl.make_problem(wl.CONFIGS[name])
-    d = DeviceProblem(p)
-    outs = {}
-    for ps in (0, 512, -1):  # one pass, 512-token partitions + pa_reduce, balanced
-        say(f"{name}: partition {ps}")
-        d.workspace = None  # a fresh workspace per schedule (a split one must not serve a balanced call)
-        outs[ps] = widen(to_host(d.step(ps).clone()), p.dtype)
-        assert np.isfinite(outs[ps]).all()
-    for ps in (512, -1):
-        r = parity(outs[ps], outs[0], p.dtype, **SCHEDULE_GATE)
-        say(f"{name}: partition {ps} against one pass: {r}")
-        assert r["ok"], (name, ps, r)
+def test_full_size_every_row(name):
+    """Every output row of the full workload, in the schedule bench.py times and in the
+    others, against the oracle: the stated tolerance, relative L2 over the output, and
+    relative L2 per row (which a lost or doubled piece of a cut sequence, or one lost
+    block, fails; tests/test_gates.py)."""
+    check_full_size_every_row(name, say)
 
 
 def test_concurrent_calls_on_two_streams_with_their_own_workspaces():

@@ -16,7 +16,7 @@ import pytest
 
 import oracle
 import workloads as wl
-from _gpu import SCHEDULE_GATE, DeviceProblem, host_caches_after_write, parity, reference_full, reference_rows, sample_rows, to_dev
+from _gpu import check_full_size_every_row, DeviceProblem, host_caches_after_write, parity, reference_full, reference_rows, sample_rows, to_dev
 from _gpu import to_host, widen
 
 pytestmark = pytest.mark.gpu
@@ -165,37 +165,7 @@ def test_tree_poisoned_unread_rows():
         assert np.array_equal(a, b)
 
 
-def test_tree_verify_full_size_sampled_rows():
-    import bench
-
-    spec = wl.CONFIGS["tree-verify"]
-    say("tree-verify: generating")
-    p = wl.make_problem(spec)
-    ps = bench.partition_for(p)
-    d = DeviceProblem(p)
-    out = widen(to_host(d.step(ps)), p.dtype)
-    assert np.isfinite(out).all()
-    kc, vc = host_caches_after_write(p)
-    rows = sample_rows(p, 64)
-    say(f"tree-verify: oracle on {len(rows)} rows (partition {ps})")
-    ref = reference_rows(p, rows, kc, vc)
-    got = np.stack([out[b * p.q_len + j, h] for (b, j, h) in rows])
-    r = assert_parity(got, ref, "tree-verify")
-    say(f"tree-verify: {r}")
-
-
-def test_tree_full_size_schedules_agree_on_every_row():
-    """Every output row of the full tree-verify workload: one pass, 512-token partitions +
-    pa_reduce and balanced agree under the gate for two GPU results (SCHEDULE_GATE)."""
-    p = wl.make_problem("tree-verify")
-    d = DeviceProblem(p)
-    outs = {}
-    for ps in (0, 512, -1):
-        say(f"tree-verify: partition {ps}")
-        d.workspace = None  # a fresh workspace per schedule (a split one must not serve a balanced call)
-        outs[ps] = widen(to_host(d.step(ps).clone()), p.dtype)
-        assert np.isfinite(outs[ps]).all()
-    for ps in (512, -1):
-        r = parity(outs[ps], outs[0], p.dtype, **SCHEDULE_GATE)
-        say(f"tree-verify: partition {ps} against one pass: {r}")
-        assert r["ok"], (ps, r)
+def test_tree_verify_full_size_every_row():
+    """Every output row of the full tree-verify workload, in the schedule bench.py times and in the
+    others, against the oracle (stated tolerance, relative L2, and relative L2 per row)."""
+    check_full_size_every_row("tree-verify", say)
