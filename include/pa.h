@@ -83,7 +83,8 @@ typedef enum {
   PA_ERR_UNSUPPORTED = 3, /* valid but not implemented (head_dim, block_size, rows per KV head, dtype) */
   PA_ERR_WORKSPACE = 4,   /* workspace missing or smaller than pa_decode_workspace_size() */
   PA_ERR_HIP = 5,         /* the HIP runtime reported an error at launch */
-  PA_ERR_MEMORY = 6       /* a buffer is not memory the GPU can access (e.g. pageable host memory) */
+  PA_ERR_MEMORY = 6,      /* a buffer is not memory the GPU can access (e.g. pageable host memory) */
+  PA_ERR_SCRATCH = 7      /* pa_decode_balanced_noalloc: the call needs more than its fixed scratch */
 } pa_status;
 
 typedef enum { PA_F32 = 0, PA_BF16 = 1 } pa_dtype;
@@ -174,6 +175,34 @@ pa_status pa_decode(void* out, const void* q, const void* k_cache, const void* v
                     int32_t num_blocks, int32_t block_size, int32_t max_blocks_per_seq,
                     int32_t partition_size, void* workspace, size_t workspace_bytes, pa_dtype dtype,
                     void* stream);
+
+/*
+ * pa_decode_balanced_noalloc - pa_decode with partition_size PA_BALANCED and no
+ * workspace argument, for callers that cannot allocate memory (code under HIP
+ * graph capture, serving loops that must not call hipMalloc, harnesses that
+ * forbid it).
+ *
+ * Arguments, layouts and results are those of pa_decode; the call computes
+ * bit for bit what pa_decode computes with PA_BALANCED.  The balanced mode's
+ * counters and partial results live in a fixed 32 MiB array of device memory
+ * inside the library (one per GPU, held until the process ends), so the call
+ * allocates nothing: no hipMalloc, no hipFree, no allocating library routine.
+ * The first call on a device looks the array up and clears it with a kernel
+ * on the given stream.  Every call on a GPU shares that GPU's array: calls that
+ * overlap in time on one GPU (other streams, other threads) race and must not
+ * be made.
+ *
+ * Returns PA_ERR_SCRATCH, launching nothing, when the call would need more
+ * than 32 MiB, i.e. when pa_decode_workspace_size(..., PA_BALANCED) exceeds
+ * 33554432 bytes (with head_dim 128, up to 31 rows per KV head fit, fewer when
+ * num_seqs * num_kv_heads is above about 130,000); PA_ERR_HIP when the array
+ * cannot be looked up; the errors of pa_decode otherwise.
+ */
+pa_status pa_decode_balanced_noalloc(void* out, const void* q, const void* k_cache, const void* v_cache,
+                                     const int32_t* block_tables, const int32_t* context_lens, float scale,
+                                     int32_t q_len, int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                                     int32_t head_dim, int32_t num_blocks, int32_t block_size,
+                                     int32_t max_blocks_per_seq, pa_dtype dtype, void* stream);
 
 /*
  * pa_decode_workspace_size - bytes of workspace pa_decode needs for partition_size.

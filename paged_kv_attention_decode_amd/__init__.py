@@ -24,16 +24,17 @@ from typing import Optional
 __all__ = [
     "PA_F32", "PA_BF16", "PA_BALANCED", "PagedAttentionError", "library_path", "load_library", "status_string", "version",
     "cache_write", "decode", "reduce", "decode_workspace_size", "paged_attention", "cache_write_fp8", "decode_fp8",
-    "decode_tree", "prefill", "copy_blocks", "SYMBOLS",
+    "decode_tree", "prefill", "copy_blocks", "decode_balanced_noalloc", "SYMBOLS",
 ]
 
 PA_F32, PA_BF16 = 0, 1
 PA_BALANCED = -1  # partition_size selecting the work-balanced decode
 BLOCK_SIZE = 16
 SYMBOLS = ("pa_cache_write", "pa_decode", "pa_decode_workspace_size", "pa_reduce", "pa_status_string", "pa_version",
-           "pa_cache_write_fp8", "pa_decode_fp8", "pa_decode_tree", "pa_prefill", "pa_copy_blocks")
+           "pa_cache_write_fp8", "pa_decode_fp8", "pa_decode_tree", "pa_prefill", "pa_copy_blocks",
+           "pa_decode_balanced_noalloc")
 _STATUS = {0: "PA_OK", 1: "PA_ERR_NULL", 2: "PA_ERR_SHAPE", 3: "PA_ERR_UNSUPPORTED", 4: "PA_ERR_WORKSPACE",
-           5: "PA_ERR_HIP", 6: "PA_ERR_MEMORY"}
+           5: "PA_ERR_HIP", 6: "PA_ERR_MEMORY", 7: "PA_ERR_SCRATCH"}
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _lib = None
@@ -66,6 +67,9 @@ def load_library():
                               ctypes.c_int, vp]
     lib.pa_decode_workspace_size.restype = sz
     lib.pa_decode_workspace_size.argtypes = [i32] * 8
+    lib.pa_decode_balanced_noalloc.restype = ctypes.c_int
+    lib.pa_decode_balanced_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, f32, i32, i32, i32, i32, i32, i32, i32, i32,
+                                               ctypes.c_int, vp]
     lib.pa_reduce.restype = ctypes.c_int
     lib.pa_reduce.argtypes = [vp, vp, sz, vp, i32, i32, i32, i32, i32, i32, i32, ctypes.c_int, vp]
     lib.pa_cache_write_fp8.restype = ctypes.c_int
@@ -226,6 +230,30 @@ def decode(q, k_cache, v_cache, block_tables, context_lens, scale: float, q_len:
                                   partition_size, pws, nws, _dtype_code(q), _stream(stream))
     _check(st, "pa_decode")
     return out if partition_size <= 0 else workspace
+
+
+def decode_balanced_noalloc(q, k_cache, v_cache, block_tables, context_lens, scale: float, q_len: int = 1,
+                            out=None, stream=None):
+    """pa_decode_balanced_noalloc: the balanced decode on the library's fixed scratch
+    (the C call allocates nothing; out is allocated here when not given)."""
+    torch = _torch()
+    S = _decode_shapes(q, k_cache, block_tables, context_lens, q_len)
+    n_h, d = q.shape[1], q.shape[2]
+    NB, bs, n_kv = k_cache.shape[0], k_cache.shape[1], k_cache.shape[2]
+    MB = block_tables.shape[1]
+    if v_cache.shape != k_cache.shape:
+        raise ValueError("k_cache and v_cache must have the same shape")
+    if out is None:
+        out = torch.empty_like(q)
+    if out.shape != q.shape:
+        raise ValueError("out must have q's shape")
+    st = load_library().pa_decode_balanced_noalloc(
+        _dev(out, "out", q.dtype, 3), _dev(q, "q", ndim=3), _dev(k_cache, "k_cache", q.dtype, 4),
+        _dev(v_cache, "v_cache", q.dtype, 4), _dev(block_tables, "block_tables", torch.int32, 2),
+        _dev(context_lens, "context_lens", torch.int32, 1), float(scale), q_len, S, n_h, n_kv, d, NB, bs, MB,
+        _dtype_code(q), _stream(stream))
+    _check(st, "pa_decode_balanced_noalloc")
+    return out
 
 
 def reduce(out, workspace, context_lens, q_len: int, max_blocks_per_seq: int, partition_size: int, stream=None):

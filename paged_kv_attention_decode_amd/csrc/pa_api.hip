@@ -4,6 +4,8 @@
 
 #include <hip/hip_runtime.h>
 
+#include <mutex>
+
 #include "pa_kernels.h"
 #include "pa_prefill.h"
 
@@ -102,6 +104,9 @@ const char* pa_status_string(pa_status s) {
     case PA_ERR_WORKSPACE: return "PA_ERR_WORKSPACE: workspace missing, misaligned or smaller than pa_decode_workspace_size()";
     case PA_ERR_HIP: return "PA_ERR_HIP: the HIP runtime reported an error at launch";
     case PA_ERR_MEMORY: return "PA_ERR_MEMORY: a buffer is not memory the GPU can access";
+    case PA_ERR_SCRATCH:
+      return "PA_ERR_SCRATCH: pa_decode_balanced_noalloc needs more than its fixed 32 MiB scratch for these sizes "
+             "(use pa_decode with a workspace)";
   }
   return "unknown pa_status";
 }
@@ -276,7 +281,63 @@ pa_status decode_impl(void* out, const void* q, const void* k_cache, const void*
   return from_hip(pa::launch_decode_valu(p, dtype == PA_F32 ? pa::kF32 : pa::kBF16, head_dim, rows, s));
 }
 
+// ---- pa_decode_balanced_noalloc: the balanced decode with a fixed scratch.
+// The balanced mode's counters and pieces live in this array instead of a
+// caller's workspace.  Host code never passes the array's name to a kernel
+// (in host code it is only a stand-in for the device symbol): the device
+// address comes from hipGetSymbolAddress, once per device, and is kept here.
+constexpr size_t kNoAllocScratchBytes = size_t(32) << 20;
+static __device__ __align__(256) char scratch[kNoAllocScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+char* g_scratch_ptr[kMaxDevices] = {};
+
+__global__ void zero_words(uint4* p, size_t n) {
+  for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x)
+    p[i] = make_uint4(0u, 0u, 0u, 0u);
+}
+
+// this device's copy of the array; the first call on a device clears it (a
+// kernel on the caller's stream, ahead of the decode)
+pa_status scratch_of_current_device(char** out, hipStream_t s) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return PA_ERR_HIP;
+  if (dev < 0 || dev >= kMaxDevices) return PA_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return PA_ERR_HIP;
+    hipLaunchKernelGGL(zero_words, dim3(256), dim3(256), 0, s, static_cast<uint4*>(ptr),
+                       kNoAllocScratchBytes / sizeof(uint4));
+    if (hipGetLastError() != hipSuccess) return PA_ERR_HIP;
+    g_scratch_ptr[dev] = static_cast<char*>(ptr);
+  }
+  *out = g_scratch_ptr[dev];
+  return PA_OK;
+}
+
 }  // namespace
+
+pa_status pa_decode_balanced_noalloc(void* out, const void* q, const void* k_cache, const void* v_cache,
+                                     const int32_t* block_tables, const int32_t* context_lens, float scale,
+                                     int32_t q_len, int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                                     int32_t head_dim, int32_t num_blocks, int32_t block_size,
+                                     int32_t max_blocks_per_seq, pa_dtype dtype, void* stream) {
+  WsLayout w;
+  if (num_seqs > 0 && workspace_layout(num_seqs, q_len, num_q_heads, num_kv_heads, head_dim, max_blocks_per_seq,
+                                       block_size, PA_BALANCED, &w) &&
+      w.total > kNoAllocScratchBytes)
+    return PA_ERR_SCRATCH;  // more than the fixed scratch holds
+  char* ws = nullptr;
+  if (num_seqs > 0) {
+    const pa_status st = scratch_of_current_device(&ws, static_cast<hipStream_t>(stream));
+    if (st != PA_OK) return st;
+  }
+  return decode_impl(out, q, k_cache, v_cache, nullptr, nullptr, false, false, nullptr, block_tables, context_lens,
+                     scale, q_len, num_seqs, num_q_heads, num_kv_heads, head_dim, num_blocks, block_size,
+                     max_blocks_per_seq, PA_BALANCED, ws, kNoAllocScratchBytes, dtype, stream);
+}
 
 pa_status pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache,
                     const int32_t* block_tables, const int32_t* context_lens, float scale, int32_t q_len,
