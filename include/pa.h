@@ -345,6 +345,9 @@ pa_status pa_decode_tree(void* out, const void* q, const void* k_cache, const vo
  *                 range is negative, longer than max_q_len or outside
  *                 [0, num_q_tokens) is skipped too, its rows left untouched.
  *   max_q_len     an upper bound of every n_b (1 .. 2^20); sizes the grid.
+ *                 PA_ERR_UNSUPPORTED when max_q_len * (num_q_heads /
+ *                 num_kv_heads) or the number of workgroups, ceil(that / 256)
+ *                 * num_kv_heads * num_seqs, exceeds 2^31 - 1.
  *   dtype         PA_BF16.  head_dim 64 or 128, block_size 16.
  *
  * Each workgroup owns 256 query rows (new token x query head of one KV head's

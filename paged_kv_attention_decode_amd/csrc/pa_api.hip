@@ -383,6 +383,12 @@ pa_status pa_prefill(void* out, const void* q, const void* k_cache, const void* 
     return PA_ERR_SHAPE;
   if (num_seqs > 65535 || num_kv_heads > 65535 || max_q_len > kMaxPrefillTokens) return PA_ERR_UNSUPPORTED;
   if ((long long)max_blocks_per_seq * kBlock > 0x7fffffffLL) return PA_ERR_SHAPE;
+  {
+    // the kernel indexes query rows and its workgroups with 32-bit ints
+    const long long rows = (long long)max_q_len * (num_q_heads / num_kv_heads);
+    const long long chunks = (rows + pa::kPrefillRowsPerWG - 1) / pa::kPrefillRowsPerWG;
+    if (rows > 0x7fffffffLL || chunks * num_kv_heads * num_seqs > 0x7fffffffLL) return PA_ERR_UNSUPPORTED;
+  }
   if (num_seqs == 0 || num_q_tokens == 0 || max_q_len == 0) return PA_OK;
   if (!out || !q || !k_cache || !v_cache || !block_tables || !context_lens || !query_start) return PA_ERR_NULL;
   if (!aligned16(out) || !aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache)) return PA_ERR_SHAPE;

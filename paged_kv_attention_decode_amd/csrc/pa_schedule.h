@@ -295,7 +295,14 @@ __device__ void drive_balanced(const DecodeParams& a, Attn& at) {
       int* cnt = a.counters + (size_t)bb * n_kv + g;
       const int old = __hip_atomic_fetch_add(cnt, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       const int is_last = old == npieces - 1;
-      if (is_last) __hip_atomic_store(cnt, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (is_last) {
+        __hip_atomic_store(cnt, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        // the merge's loads come after every other piece's arrival: an
+        // agent-scope acquire (an invalidate of this CU's caches, cheap, and
+        // a compiler barrier), which the workgroup barrier below extends to
+        // the other threads
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+      }
       s_last = is_last;
     }
     __syncthreads();

@@ -173,6 +173,11 @@ def test_prefill_rejects_invalid_arguments(lib):
     assert _prefill(lib, bs=32) == 3
     assert _prefill(lib, n_h=30) == 2                  # not a multiple of the KV heads
     assert _prefill(lib, mq=(1 << 20) + 1) == 3
+    # workgroups past 2^31 - 1: 2^20 tokens x 8 heads per KV head = 32768 chunks of 256 rows, x 8 x 8192
+    assert _prefill(lib, mq=1 << 20, n_h=64, n_kv=8, S=8192, T=1 << 20) == 3
+    assert _prefill(lib, mq=1 << 20, n_h=64, n_kv=8, S=8191, T=1 << 20, qs=None) == 1  # one fewer fits
+    # query rows of one (sequence, KV head) past 2^31 - 1: 2^20 tokens x 2048 heads per KV head
+    assert _prefill(lib, mq=1 << 20, n_h=2048, n_kv=1, S=1, T=1 << 20) == 3
     assert _prefill(lib, qs=None) == 1
     assert _prefill(lib, out=None) == 1
     assert _prefill(lib, S=0, q=None, out=None) == 0   # nothing to do

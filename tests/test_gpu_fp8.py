@@ -160,6 +160,31 @@ def test_fp8_one_token_returns_scaled_v():
             np.testing.assert_allclose(got[b, h], want, rtol=2 ** -8, atol=0)
 
 
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("G,q_len", [(4, 1), (8, 5)])
+def test_fp8_scores_rising_far_past_the_first_block(G, q_len, d):
+    """Key codes grow along the context in one dimension (to 7 after the
+    per-head scale; queries 256 there), so weights relative to a wave's first
+    block exceed 2^64 even within one 512-token partition and the fp8 kernel
+    must take its exact two-pass path, in every schedule."""
+    spec = small(G=G, d=d, q_len=q_len, n_kv=2, S=3, lens=("fixed", (1000, 700, 40)), seed=53).with_(
+        write_new_tokens=False, max_len=1024)
+    p = wl.make_problem(spec)
+    p.q[:] = 0
+    p.q[:, :, 0] = wl.round_to_bf16_bits(np.array([256.0], dtype=np.float32))[0]
+    vals = np.zeros(p.k_cache.shape, dtype=np.float32)
+    for b, L in enumerate(p.context_lens):
+        for t in range(int(L)):
+            vals[p.block_tables[b, t // 16], t % 16, :, 0] = 7.0 * t / 1000.0
+    p.k_cache[:] = wl.to_fp8_codes(wl.round_to_bf16_bits(vals), p.k_scale)
+    ref = reference_full(p)
+    for ps in (0, 512, -1):
+        say(f"fp8 ramp G={G} q_len={q_len} d={d} ps={ps}")
+        _, got = run(p, ps)
+        assert np.isfinite(got).all()
+        assert_parity(got, ref, f"fp8 ramp ps={ps}")
+
+
 def test_fp8_full_size_every_row():
     """Every output row of the full llama3-8b-decode-fp8kv workload, in the schedule bench.py times and in the
     others, against the oracle (stated tolerance, relative L2, and relative L2 per row)."""

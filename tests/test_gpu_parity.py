@@ -305,14 +305,16 @@ def test_identical_keys_count_probe_bf16(G, q_len, lens, parts):
                 np.testing.assert_allclose(widen(out[:, h], "bf16"), widen(expect_bits, "bf16"), rtol=2 ** -7, atol=0)
 
 
+@pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("dtype,q_len,n_h", [("f32", 1, 2), ("f32", 2, 2), ("bf16", 1, 2), ("bf16", 2, 2),
                                              ("bf16", 5, 2), ("bf16", 5, 8)])
-def test_scores_rising_far_past_the_first_block(dtype, q_len, n_h):
-    """Scores grow by ~0.1 per position, so weights relative to a wave's first
-    block exceed 2^64 and the kernel must take its exact two-pass path."""
-    d = 64
+def test_scores_rising_far_past_the_first_block(dtype, q_len, n_h, d):
+    """Scores grow by ~0.1 per position (scale 1/8 at both head sizes), so
+    weights relative to a wave's first block exceed 2^64 and every kernel
+    variant (vector ALU and matrix core, d 64 and 128) must take its exact
+    two-pass path, in each schedule."""
     spec = wl.Spec(name="ramp", dtype=dtype, num_seqs=3, num_q_heads=n_h, num_kv_heads=1, head_dim=d,
-                   lens=("fixed", (1000, 700, 40)), max_len=1024, q_len=q_len, seed=31)
+                   lens=("fixed", (1000, 700, 40)), max_len=1024, q_len=q_len, seed=31, scale=0.125)
     p = wl.make_problem(spec)
     p.q[:] = 0
     p.k_cache[:] = 0
@@ -325,7 +327,7 @@ def test_scores_rising_far_past_the_first_block(dtype, q_len, n_h):
                 wl.round_to_bf16_bits(np.array([val]))[0] if dtype == "bf16" else val)
     ref = full_reference(p)
     for ps in (0, 512, -1):
-        say(f"ramp {dtype} q_len={q_len} heads={n_h} ps={ps}")
+        say(f"ramp {dtype} d={d} q_len={q_len} heads={n_h} ps={ps}")
         _, got = run(p, ps)
         assert_parity(got, ref, dtype, f"ramp ps={ps}")
 

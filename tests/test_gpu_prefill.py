@@ -179,18 +179,19 @@ def test_chunked_prefill_full_size_sampled_rows():
     assert r["ok"], r
 
 
-def test_prefill_scores_rising_far_past_the_first_block():
-    """Keys grow along the context (0.3 per position in one dimension, queries 4
-    there), so a row's late weights exceed its reference from step 0 by about
-    2^150, past the fp32 range: only the exact two-sweep path, which the
-    overflow flag must trigger, gives finite results.  The new tokens continue
-    the ramp through pa_cache_write."""
-    p = wl.make_problem(spec((40, 1, 300), (700, 500, 300), G=2, d=64, n_kv=1, seed=33))
+@pytest.mark.parametrize("d", [64, 128])
+def test_prefill_scores_rising_far_past_the_first_block(d):
+    """Keys grow along the context (0.3 per position in one dimension, queries
+    4 sqrt(d / 64) there), so a row's late weights exceed its reference from
+    step 0 by about 2^150, past the fp32 range: only the exact two-sweep path,
+    which the overflow flag must trigger, gives finite results.  The new tokens
+    continue the ramp through pa_cache_write."""
+    p = wl.make_problem(spec((40, 1, 300), (700, 500, 300), G=2, d=d, n_kv=1, seed=33))
     bits = lambda x: wl.round_to_bf16_bits(np.array([x], dtype=np.float32))[0]
     p.q[:] = 0
     p.k_cache[:] = 0
     p.new_k[:] = 0
-    p.q[:, :, 0] = bits(4.0)
+    p.q[:, :, 0] = bits(4.0 * np.sqrt(d / 64.0))
     for b in range(len(p.context_lens)):
         L, n = int(p.context_lens[b]), int(p.q_counts[b])
         base = L - n
@@ -198,5 +199,5 @@ def test_prefill_scores_rising_far_past_the_first_block():
             p.k_cache[p.block_tables[b, t // 16], t % 16, 0, 0] = bits(0.3 * t)
         for i in range(n):
             p.new_k[int(p.query_start[b]) + i, 0, 0] = bits(0.3 * (base + i))
-    say("prefill ramp")
-    check(p, "ramp")
+    say(f"prefill ramp d={d}")
+    check(p, f"ramp d={d}")

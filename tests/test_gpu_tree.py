@@ -165,6 +165,31 @@ def test_tree_poisoned_unread_rows():
         assert np.array_equal(a, b)
 
 
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("G,T,tree", [(4, 15, "binary"), (1, 9, "random"), (3, 13, "random")])
+def test_tree_scores_rising_far_past_the_first_block(G, T, tree, d):
+    """Keys grow by 0.2 per position in one dimension (queries 4 there, scale
+    1/8), so weights relative to a wave's first block exceed 2^64 and the tree
+    kernel must take its exact two-pass path, in every schedule; the tree's
+    own nodes sit on the ramp too."""
+    spec = small(G=G, d=d, T=T, tree=tree, n_kv=1, S=3, lens=("fixed", (1000, 700, 40)), seed=59).with_(
+        write_new_tokens=False, max_len=1024, scale=0.125)
+    p = wl.make_problem(spec)
+    bits = lambda x: wl.round_to_bf16_bits(np.array([x], dtype=np.float32))[0]
+    p.q[:] = 0
+    p.k_cache[:] = 0
+    p.q[:, :, 0] = bits(4.0)
+    for b, L in enumerate(p.context_lens):
+        for t in range(int(L)):
+            p.k_cache[p.block_tables[b, t // 16], t % 16, 0, 0] = bits(0.2 * t)
+    ref = reference_full(p)
+    for ps in (0, 512, -1):
+        say(f"tree ramp G={G} T={T} {tree} d={d} ps={ps}")
+        _, got = run(p, ps)
+        assert np.isfinite(got).all()
+        assert_parity(got, ref, f"tree ramp ps={ps}")
+
+
 def test_tree_verify_full_size_every_row():
     """Every output row of the full tree-verify workload, in the schedule bench.py times and in the
     others, against the oracle (stated tolerance, relative L2, and relative L2 per row)."""
