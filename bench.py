@@ -1,14 +1,17 @@
 #!/usr/bin/env python3
 """Benchmark of the paged decode-attention path on one MI355X.
 
-One step = the whole path over one batch: pa_cache_write of the batch's new
-tokens, pa_decode, and pa_reduce when the context is split.  The inputs are
+One step = the whole path over one batch: the store of the batch's new
+tokens and pa_decode, fused in one pa_decode_append launch (or pa_cache_write
+then pa_decode, for the fp8 and tree layers and with --separate-write), and
+pa_reduce when the context is split.  The inputs are
 the seeded synthetic Llama-3-8B-shaped decode layer (64 sequences, 32 query
 heads / 8 KV heads, head_dim 128, bf16, contexts uniform in [512, 4096], a
 20,000-block pool), resident in HBM before timing starts.
 
 Prints one JSON line:
-  value          tokens/s of whole steps (num_seqs * q_len tokens per step)
+  value          tokens/s of whole steps (num_seqs * q_len tokens per step),
+                 timed by wall clock over K steps with no timing event inside
   roofline       the decode kernel: algorithmic KV + Q bytes per launch over its
                  average launch time (HIP events on the launch stream; for a
                  split context the event pair spans pa_decode and pa_reduce)
@@ -106,10 +109,23 @@ def to_dev(a, torch):
     return torch.from_numpy(a).cuda()
 
 
-class Resident:
-    """The workload in HBM and the three calls of one step."""
+def appended_slots(p: wl.Problem):
+    """Slots of the new tokens under the append rule pa_decode_append follows (new token
+    j of sequence b at position L_b - q_len + j of b's blocks), -1 where none."""
+    slots = []
+    for b in range(p.num_seqs):
+        L = int(p.context_lens[b])
+        for j in range(p.q_len):
+            pos = L - p.q_len + j
+            phys = int(p.block_tables[b, pos // 16]) if pos >= 0 else -1
+            slots.append(phys * 16 + pos % 16 if 0 <= phys < p.num_blocks else -1)
+    return np.array(slots, dtype=np.int64)
 
-    def __init__(self, p: wl.Problem, partition: int, torch):
+
+class Resident:
+    """The workload in HBM and the calls of one step."""
+
+    def __init__(self, p: wl.Problem, partition: int, torch, separate_write: bool = False):
         import paged_kv_attention_decode_amd as pa
 
         self.pa, self.p, self.partition, self.torch = pa, p, partition, torch
@@ -132,8 +148,14 @@ class Resident:
         self.ws = None
         if partition:
             self.ws = pa.new_workspace(self.q, self.k_cache, self.tables, p.q_len, partition)
+        # the new tokens' store fused into the decode launch, where the workload's slots
+        # are the appended positions (always, for the synthetic layers)
+        self.fused = (not separate_write and self.new_k is not None and not self.fp8 and self.parents is None
+                      and self.query_start is None and np.array_equal(appended_slots(p), p.slot_mapping))
 
     def write(self):
+        if self.fused:
+            return
         if self.new_k is not None:
             if self.fp8:
                 self.pa.cache_write_fp8(self.new_k, self.new_v, self.k_cache, self.v_cache, self.slots, self.k_scale,
@@ -154,6 +176,11 @@ class Resident:
         if self.fp8:
             self.pa.decode_fp8(self.q, self.k_cache, self.v_cache, self.k_scale, self.v_scale, self.tables, self.lens,
                                float(p.scale), p.q_len, self.partition, out=self.out, workspace=self.ws)
+            return
+        if self.fused:
+            self.pa.decode_append(self.q, self.new_k, self.new_v, self.k_cache, self.v_cache, self.tables, self.lens,
+                                  float(p.scale), p.q_len, self.partition, out=self.out if self.partition <= 0
+                                  else None, workspace=self.ws)
             return
         self.pa.decode(self.q, self.k_cache, self.v_cache, self.tables, self.lens, float(p.scale), p.q_len,
                        self.partition, out=self.out, workspace=self.ws)
@@ -318,6 +345,9 @@ def main(argv=None):
     ap.add_argument("--op", default="decode", choices=["decode", "copy-blocks", "swap-out", "swap-in"],
                     help="decode: the whole path (default); copy-blocks: pa_copy_blocks of 2048 blocks within "
                          "the pool; swap-out / swap-in: the same 2048 blocks to / from pinned host memory")
+    ap.add_argument("--separate-write", action="store_true",
+                    help="store the new tokens with pa_cache_write before pa_decode instead of the fused "
+                         "pa_decode_append")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a 1 GiB device copy (for scaling memory counters)")
     args = ap.parse_args(argv)
@@ -340,20 +370,29 @@ def main(argv=None):
     spec = wl.CONFIGS[args.config]
     p = wl.make_problem(spec)
     partition = partition_for(p) if args.partition is None else args.partition
-    r = Resident(p, partition, torch)
+    r = Resident(p, partition, torch, args.separate_write)
 
     for _ in range(max(0, args.warmup)):
         r.step()
     torch.cuda.synchronize()
 
-    # The timed region: K whole steps, one event pair around each decode launch
-    # (and its pa_reduce, for a split context: the two make the attention)
-    # (every timing event costs a few microseconds of GPU time, so there are no
-    # others inside the region).
+    # Two timed regions of K whole steps each.  The first has no timing event
+    # inside it (an event pair costs about 5 us of GPU time, which would be
+    # charged to every step): its wall clock gives ms_per_step and value.  The
+    # second brackets each decode launch (and its pa_reduce, for a split
+    # context: the two make the attention) with an event pair on the launch
+    # stream: the launch durations the roofline is rated on.
     K = args.steps
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    for k in range(K):
+        r.step()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1e3 / K
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
+    torch.cuda.synchronize()
+    t2 = time.perf_counter()
     for k in range(K):
         r.write()
         ev[k][0].record()
@@ -361,8 +400,8 @@ def main(argv=None):
         r.reduce()
         ev[k][1].record()
     torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    ms_per_step = (t1 - t0) * 1e3 / K
+    t3 = time.perf_counter()
+    ms_per_step_events = (t3 - t2) * 1e3 / K
     launch_ms = np.array([a.elapsed_time(b) for a, b in ev])
     decode_ms = float(np.mean(launch_ms))
     spread_us = {f"p{q}": round(float(np.percentile(launch_ms, q)) * 1e3, 2) for q in (10, 50, 90)}
@@ -440,6 +479,8 @@ def main(argv=None):
         achieved = kv_bytes / basis_s / 1e9
         traffic, traffic_bytes = load_traffic(args.config, basis_s)
         kernel = decode_kernel_name(p, partition)
+        if r.fused:
+            kernel += ", storing the new tokens first (pa_decode_append)"
         if partition > 0:
             kernel += " + reduce_kernel (pa_reduce)"
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
@@ -474,6 +515,7 @@ def main(argv=None):
         "steps": K,
         "warmup": args.warmup,
         "ms_per_step": round(ms_per_step, 5),
+        "ms_per_step_with_launch_events": round(ms_per_step_events, 5),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -492,7 +534,8 @@ def main(argv=None):
             else ("causal" if int(p.q_counts.max()) > 1 else "none"),
         },
         "kv_hbm_gbps_step": round(kv_bytes / (ms_per_step / 1e3) / 1e9, 1),
-        "breakdown_us": {"cache_write": round(write_ms * 1e3, 2), "decode": round(decode_only_ms * 1e3, 2),
+        "breakdown_us": {"cache_write": "fused into the decode launch" if r.fused else round(write_ms * 1e3, 2),
+                         "decode": round(decode_only_ms * 1e3, 2),
                          "reduce": round(reduce_ms * 1e3, 2),
                          "decode_plus_reduce_timed": round(decode_ms * 1e3, 2),
                          "decode_plus_reduce_cold": None if cold_ms is None else round(cold_ms * 1e3, 2)},

@@ -8,6 +8,8 @@
  *                   its paged KV cache: in one pass, work-balanced across the
  *                   GPU, or as per-partition partials (split context);
  *   pa_reduce       merge the partials of a split pa_decode into the output;
+ *   pa_decode_append
+ *                   pa_cache_write of the new tokens and pa_decode in one launch;
  *   pa_cache_write_fp8, pa_decode_fp8
  *                   the same over a KV cache of fp8 (E4M3) codes with one
  *                   scale per KV head;
@@ -175,6 +177,40 @@ pa_status pa_decode(void* out, const void* q, const void* k_cache, const void* v
                     int32_t num_blocks, int32_t block_size, int32_t max_blocks_per_seq,
                     int32_t partition_size, void* workspace, size_t workspace_bytes, pa_dtype dtype,
                     void* stream);
+
+/*
+ * pa_decode_append - pa_cache_write of the batch's new tokens and pa_decode
+ * over them, in one launch.
+ *
+ * A generated token's key and value are appended in place in its sequence's
+ * last block ("LLM Inference Serving", systeminternals.dev, the Sequence /
+ * block_table sketch), and are written before attention reads them ("07 -
+ * Inference", lourdhu02.github.io, section 3, speculative verify).  Launching
+ * the store and the attention as one kernel removes a launch per step (the
+ * pages name launch overhead as what fusing small kernels saves: lourdhu02,
+ * sections 2.6 and 5.4).
+ *
+ *   new_k, new_v  [num_seqs * q_len, num_kv_heads, head_dim], dtype; row
+ *                 b * q_len + j is new token j of sequence b, whose position is
+ *                 L_b - q_len + j.  It is stored at slot
+ *                 16 * block_tables[b][pos / 16] + pos % 16 of k_cache /
+ *                 v_cache (a position below 0, or a block id outside
+ *                 [0, num_blocks), is skipped, as pa_cache_write skips a slot
+ *                 outside the pool).
+ *   k_cache, v_cache  written (the new rows) and read.
+ * Every other argument, the schedules, the workspace and the results are those
+ * of pa_decode (PA_F32 or PA_BF16).  After the call the caches hold exactly
+ * what pa_cache_write with those slots would have stored, and out (or the
+ * partials for pa_reduce) is bit for bit what pa_decode computes after it.
+ * The new tokens of one sequence must not share a slot with another
+ * sequence's tokens or with any position read by the call.
+ */
+pa_status pa_decode_append(void* out, const void* q, const void* new_k, const void* new_v, void* k_cache,
+                           void* v_cache, const int32_t* block_tables, const int32_t* context_lens, float scale,
+                           int32_t q_len, int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                           int32_t head_dim, int32_t num_blocks, int32_t block_size, int32_t max_blocks_per_seq,
+                           int32_t partition_size, void* workspace, size_t workspace_bytes, pa_dtype dtype,
+                           void* stream);
 
 /*
  * pa_decode_balanced_noalloc - pa_decode with partition_size PA_BALANCED and no

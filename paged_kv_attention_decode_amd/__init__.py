@@ -24,7 +24,7 @@ from typing import Optional
 __all__ = [
     "PA_F32", "PA_BF16", "PA_BALANCED", "PagedAttentionError", "library_path", "load_library", "status_string", "version",
     "cache_write", "decode", "reduce", "decode_workspace_size", "paged_attention", "cache_write_fp8", "decode_fp8",
-    "decode_tree", "prefill", "copy_blocks", "decode_balanced_noalloc", "SYMBOLS",
+    "decode_tree", "prefill", "copy_blocks", "decode_balanced_noalloc", "decode_append", "SYMBOLS",
 ]
 
 PA_F32, PA_BF16 = 0, 1
@@ -32,7 +32,7 @@ PA_BALANCED = -1  # partition_size selecting the work-balanced decode
 BLOCK_SIZE = 16
 SYMBOLS = ("pa_cache_write", "pa_decode", "pa_decode_workspace_size", "pa_reduce", "pa_status_string", "pa_version",
            "pa_cache_write_fp8", "pa_decode_fp8", "pa_decode_tree", "pa_prefill", "pa_copy_blocks",
-           "pa_decode_balanced_noalloc")
+           "pa_decode_balanced_noalloc", "pa_decode_append")
 _STATUS = {0: "PA_OK", 1: "PA_ERR_NULL", 2: "PA_ERR_SHAPE", 3: "PA_ERR_UNSUPPORTED", 4: "PA_ERR_WORKSPACE",
            5: "PA_ERR_HIP", 6: "PA_ERR_MEMORY", 7: "PA_ERR_SCRATCH"}
 
@@ -67,6 +67,9 @@ def load_library():
                               ctypes.c_int, vp]
     lib.pa_decode_workspace_size.restype = sz
     lib.pa_decode_workspace_size.argtypes = [i32] * 8
+    lib.pa_decode_append.restype = ctypes.c_int
+    lib.pa_decode_append.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, f32, i32, i32, i32, i32, i32, i32, i32, i32, i32,
+                                     vp, sz, ctypes.c_int, vp]
     lib.pa_decode_balanced_noalloc.restype = ctypes.c_int
     lib.pa_decode_balanced_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, f32, i32, i32, i32, i32, i32, i32, i32, i32,
                                                ctypes.c_int, vp]
@@ -229,6 +232,41 @@ def decode(q, k_cache, v_cache, block_tables, context_lens, scale: float, q_len:
     st = load_library().pa_decode(pout, *args_common, float(scale), q_len, S, n_h, n_kv, d, NB, bs, MB,
                                   partition_size, pws, nws, _dtype_code(q), _stream(stream))
     _check(st, "pa_decode")
+    return out if partition_size <= 0 else workspace
+
+
+def decode_append(q, new_k, new_v, k_cache, v_cache, block_tables, context_lens, scale: float, q_len: int = 1,
+                  partition_size: int = 0, out=None, workspace=None, stream=None):
+    """pa_decode_append: store the new tokens' K/V rows at their positions (new token j
+    of sequence b at L_b - q_len + j, through the block table) and run pa_decode, in
+    one launch.  Returns out, or the workspace for reduce() when partition_size > 0."""
+    torch = _torch()
+    S = _decode_shapes(q, k_cache, block_tables, context_lens, q_len)
+    n_h, d = q.shape[1], q.shape[2]
+    NB, bs, n_kv = k_cache.shape[0], k_cache.shape[1], k_cache.shape[2]
+    MB = block_tables.shape[1]
+    if v_cache.shape != k_cache.shape:
+        raise ValueError("k_cache and v_cache must have the same shape")
+    if new_k.shape != (S * q_len, n_kv, d) or new_v.shape != new_k.shape:
+        raise ValueError(f"new_k and new_v must be [num_seqs * q_len, n_kv, d] = {(S * q_len, n_kv, d)}")
+    pws, nws = None, 0
+    if partition_size != 0:
+        if workspace is None:
+            workspace = new_workspace(q, k_cache, block_tables, q_len, partition_size)
+        pws, nws = _dev(workspace, "workspace", torch.uint8, 1), workspace.numel()
+    pout = None
+    if partition_size <= 0:
+        if out is None:
+            out = torch.empty_like(q)
+        if out.shape != q.shape:
+            raise ValueError("out must have q's shape")
+        pout = _dev(out, "out", q.dtype, 3)
+    st = load_library().pa_decode_append(
+        pout, _dev(q, "q", ndim=3), _dev(new_k, "new_k", q.dtype, 3), _dev(new_v, "new_v", q.dtype, 3),
+        _dev(k_cache, "k_cache", q.dtype, 4), _dev(v_cache, "v_cache", q.dtype, 4),
+        _dev(block_tables, "block_tables", torch.int32, 2), _dev(context_lens, "context_lens", torch.int32, 1),
+        float(scale), q_len, S, n_h, n_kv, d, NB, bs, MB, partition_size, pws, nws, _dtype_code(q), _stream(stream))
+    _check(st, "pa_decode_append")
     return out if partition_size <= 0 else workspace
 
 

@@ -206,8 +206,8 @@ namespace {
 
 // pa_decode, pa_decode_fp8 and pa_decode_tree: validation, workspace, schedule and launch
 pa_status decode_impl(void* out, const void* q, const void* k_cache, const void* v_cache, const float* k_scale,
-                      const float* v_scale, bool fp8, bool tree, const int32_t* parents,
-                      const int32_t* block_tables, const int32_t* context_lens, float scale, int32_t q_len,
+                      const float* v_scale, bool fp8, bool tree, const int32_t* parents, const void* new_k,
+                      const void* new_v, const int32_t* block_tables, const int32_t* context_lens, float scale, int32_t q_len,
                       int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
                       int32_t num_blocks, int32_t block_size, int32_t max_blocks_per_seq, int32_t partition_size,
                       void* workspace, size_t workspace_bytes, pa_dtype dtype, void* stream) {
@@ -230,6 +230,9 @@ pa_status decode_impl(void* out, const void* q, const void* k_cache, const void*
   if (fp8 && (!k_scale || !v_scale)) return PA_ERR_NULL;
   if (tree && !parents) return PA_ERR_NULL;
   if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || (out && !aligned16(out))) return PA_ERR_SHAPE;
+  const bool append = new_k || new_v;
+  if (append && (!new_k || !new_v)) return PA_ERR_NULL;
+  if (append && (!aligned16(new_k) || !aligned16(new_v))) return PA_ERR_SHAPE;
 
   pa::DecodeParams p = {};
   p.out = out;
@@ -239,6 +242,9 @@ pa_status decode_impl(void* out, const void* q, const void* k_cache, const void*
   p.k_scale = k_scale;
   p.v_scale = v_scale;
   p.parents = tree ? parents : nullptr;
+  p.new_k = append ? new_k : nullptr;
+  p.new_v = append ? new_v : nullptr;
+  p.append_row_bytes = append ? head_dim * (dtype == PA_F32 ? 4 : 2) : 0;
   p.tables = block_tables;
   p.lens = context_lens;
   p.scale_log2 = (float)((double)scale * 1.4426950408889634);
@@ -334,8 +340,8 @@ pa_status pa_decode_balanced_noalloc(void* out, const void* q, const void* k_cac
     const pa_status st = scratch_of_current_device(&ws, static_cast<hipStream_t>(stream));
     if (st != PA_OK) return st;
   }
-  return decode_impl(out, q, k_cache, v_cache, nullptr, nullptr, false, false, nullptr, block_tables, context_lens,
-                     scale, q_len, num_seqs, num_q_heads, num_kv_heads, head_dim, num_blocks, block_size,
+  return decode_impl(out, q, k_cache, v_cache, nullptr, nullptr, false, false, nullptr, nullptr, nullptr, block_tables,
+                     context_lens, scale, q_len, num_seqs, num_q_heads, num_kv_heads, head_dim, num_blocks, block_size,
                      max_blocks_per_seq, PA_BALANCED, ws, kNoAllocScratchBytes, dtype, stream);
 }
 
@@ -344,9 +350,21 @@ pa_status pa_decode(void* out, const void* q, const void* k_cache, const void* v
                     int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
                     int32_t num_blocks, int32_t block_size, int32_t max_blocks_per_seq, int32_t partition_size,
                     void* workspace, size_t workspace_bytes, pa_dtype dtype, void* stream) {
-  return decode_impl(out, q, k_cache, v_cache, nullptr, nullptr, false, false, nullptr, block_tables, context_lens,
-                     scale, q_len, num_seqs, num_q_heads, num_kv_heads, head_dim, num_blocks, block_size,
+  return decode_impl(out, q, k_cache, v_cache, nullptr, nullptr, false, false, nullptr, nullptr, nullptr, block_tables,
+                     context_lens, scale, q_len, num_seqs, num_q_heads, num_kv_heads, head_dim, num_blocks, block_size,
                      max_blocks_per_seq, partition_size, workspace, workspace_bytes, dtype, stream);
+}
+
+pa_status pa_decode_append(void* out, const void* q, const void* new_k, const void* new_v, void* k_cache,
+                           void* v_cache, const int32_t* block_tables, const int32_t* context_lens, float scale,
+                           int32_t q_len, int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                           int32_t head_dim, int32_t num_blocks, int32_t block_size, int32_t max_blocks_per_seq,
+                           int32_t partition_size, void* workspace, size_t workspace_bytes, pa_dtype dtype,
+                           void* stream) {
+  if (num_seqs > 0 && (!new_k || !new_v)) return PA_ERR_NULL;
+  return decode_impl(out, q, k_cache, v_cache, nullptr, nullptr, false, false, nullptr, new_k, new_v, block_tables,
+                     context_lens, scale, q_len, num_seqs, num_q_heads, num_kv_heads, head_dim, num_blocks,
+                     block_size, max_blocks_per_seq, partition_size, workspace, workspace_bytes, dtype, stream);
 }
 
 pa_status pa_decode_tree(void* out, const void* q, const void* k_cache, const void* v_cache,
@@ -355,8 +373,8 @@ pa_status pa_decode_tree(void* out, const void* q, const void* k_cache, const vo
                          int32_t num_kv_heads, int32_t head_dim, int32_t num_blocks, int32_t block_size,
                          int32_t max_blocks_per_seq, int32_t partition_size, void* workspace,
                          size_t workspace_bytes, pa_dtype dtype, void* stream) {
-  return decode_impl(out, q, k_cache, v_cache, nullptr, nullptr, false, true, tree_parents, block_tables,
-                     context_lens, scale, tree_size, num_seqs, num_q_heads, num_kv_heads, head_dim, num_blocks,
+  return decode_impl(out, q, k_cache, v_cache, nullptr, nullptr, false, true, tree_parents, nullptr, nullptr,
+                     block_tables, context_lens, scale, tree_size, num_seqs, num_q_heads, num_kv_heads, head_dim, num_blocks,
                      block_size, max_blocks_per_seq, partition_size, workspace, workspace_bytes, dtype, stream);
 }
 
@@ -366,8 +384,8 @@ pa_status pa_decode_fp8(void* out, const void* q, const void* k_cache, const voi
                         int32_t head_dim, int32_t num_blocks, int32_t block_size, int32_t max_blocks_per_seq,
                         int32_t partition_size, void* workspace, size_t workspace_bytes, pa_dtype dtype,
                         void* stream) {
-  return decode_impl(out, q, k_cache, v_cache, k_scale, v_scale, true, false, nullptr, block_tables, context_lens,
-                     scale, q_len, num_seqs, num_q_heads, num_kv_heads, head_dim, num_blocks, block_size,
+  return decode_impl(out, q, k_cache, v_cache, k_scale, v_scale, true, false, nullptr, nullptr, nullptr, block_tables,
+                     context_lens, scale, q_len, num_seqs, num_q_heads, num_kv_heads, head_dim, num_blocks, block_size,
                      max_blocks_per_seq, partition_size, workspace, workspace_bytes, dtype, stream);
 }
 

@@ -66,6 +66,11 @@ struct DecodeParams {
   const float* k_scale;  // fp8 caches: [n_kv] per-head scales (null otherwise)
   const float* v_scale;
   const int32_t* parents;  // tree verify: [S, q_len] parent of each node (null: causal among the new tokens)
+  // append (pa_decode_append): the new tokens' K and V rows [S*q_len, n_kv, D],
+  // stored at their positions before they are read (null: nothing to store)
+  const void* new_k;
+  const void* new_v;
+  int append_row_bytes;  // bytes of one (token, head) row of K or V
   float scale_log2;      // softmax scale * log2(e)
   int q_len, group, n_h, n_kv, num_blocks, max_blocks;
   int mode;              // DecodeMode

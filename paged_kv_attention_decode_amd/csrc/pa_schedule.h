@@ -108,6 +108,41 @@ __device__ int sequence_of_rank(const DecodeParams& a, int z) {
   return s_pick;
 }
 
+// pa_decode_append: before a workgroup reads blocks [blo, bhi) of sequence b
+// for KV head g, it stores the new tokens that fall in them.  New token j of
+// sequence b sits at position L - q_len + j, in slot 16 * table[b][pos / 16] +
+// pos % 16 (the sequence's own block table: tokens are appended in place);
+// positions before 0 and blocks outside the pool are skipped.  Each (block,
+// KV head) slice is read by exactly one wave in every schedule: wave w of the
+// workgroup owning the block reads blocks blo + w + NW k.  That wave stores
+// the new tokens of its blocks here, before it issues any load, and a wave's
+// memory operations reach memory in the order it issues them, so its loads
+// see the stores without a wait, a barrier, or any other wave involved.
+template <int NT>
+__device__ void append_new_tokens(const DecodeParams& a, int b, int g, int L, int blo, int bhi) {
+  constexpr int NW = NT / 64;
+  const int first = L - a.q_len;  // position of new token 0
+  const int blk0 = (first < 0 ? 0 : first) / kBlockTokens, blk1 = (L - 1) / kBlockTokens;
+  if (L <= 0 || blk1 < blo || blk0 >= bhi) return;  // no new token in these blocks (wave-uniform)
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int chunks = a.append_row_bytes / 16;
+  const size_t tok_bytes = (size_t)a.n_kv * a.append_row_bytes;
+  for (int idx = lane; idx < a.q_len * 2 * chunks; idx += 64) {
+    const int j = idx / (2 * chunks), kv = (idx / chunks) & 1, c = idx % chunks;
+    const int pos = first + j;
+    if (pos < 0) continue;
+    const int blk = pos / kBlockTokens;
+    if (blk < blo || blk >= bhi || (blk - blo) % NW != w) continue;  // another wave's block
+    const int phys = a.tables[(size_t)b * a.max_blocks + blk];
+    if ((unsigned)phys >= (unsigned)a.num_blocks) continue;
+    const char* src = static_cast<const char*>(kv ? a.new_v : a.new_k) +
+                      ((size_t)(b * a.q_len + j) * a.n_kv + g) * a.append_row_bytes + 16 * c;
+    char* dst = static_cast<char*>(const_cast<void*>(kv ? a.v_cache : a.k_cache)) +
+                ((size_t)phys * kBlockTokens + pos % kBlockTokens) * tok_bytes + (size_t)g * a.append_row_bytes + 16 * c;
+    *reinterpret_cast<uint4*>(dst) = *reinterpret_cast<const uint4*>(src);
+  }
+}
+
 template <class Attn>
 __device__ void drive_fixed(const DecodeParams& a, Attn& at) {
   const int part = blockIdx.x, g = blockIdx.y;
@@ -121,12 +156,14 @@ __device__ void drive_fixed(const DecodeParams& a, Attn& at) {
       write_zeros(a, at, b, g);
       return;
     }
+    if (a.new_k) append_new_tokens<Attn::kThreads>(a, b, g, L, 0, nblk);
     at.run(b, g, L, 0, nblk);
     write_final(a, at, b, g);
     return;
   }
   const int lo = part * a.part_blocks;
   if (lo >= nblk) return;  // no token in this partition; pa_reduce never reads it
+  if (a.new_k) append_new_tokens<Attn::kThreads>(a, b, g, L, lo, min(lo + a.part_blocks, nblk));
   at.run(b, g, L, lo, min(lo + a.part_blocks, nblk));
   const int rows = a.group * a.q_len;
   for (int idx = threadIdx.x; idx < rows * Attn::kD; idx += Attn::kThreads) {
@@ -328,6 +365,7 @@ __device__ void drive_balanced(const DecodeParams& a, Attn& at) {
     const int nb = (int)(seg1 - seg0);
     const int blo = (int)((B0 > seg0 ? B0 : seg0) - seg0);
     const int bhi = (int)((B1 < seg1 ? B1 : seg1) - seg0);
+    if (a.new_k) append_new_tokens<NT>(a, bb, g, clamped_len(a, bb), blo, bhi);
     at.run(bb, g, clamped_len(a, bb), blo, bhi);
     if (blo == 0 && bhi == nb) {
       write_final(a, at, bb, g);
