@@ -50,12 +50,16 @@ constexpr int kXcds = 8;  // accelerator complex dies of an MI355X
 constexpr int kStepBlocks = 8;           // blocks staged per step (per barrier), multiplied two at a time
 constexpr int kPrefetch = 1;             // steps whose global loads are in flight
 
-// one block of one KV head in LDS; rows padded by 16 bytes so that the 16
-// token rows one K read touches fall in different banks
+// one block of one KV head in LDS (64 banks of 4 bytes).  K rows are padded by
+// 16 bytes: a K read (16 lanes, 16 bytes each, one per token row) then starts
+// the 16 rows 4 banks apart and touches every bank once.  V rows are padded by
+// 32 bytes: a transposing V read (32 lanes, 8 bytes each: 8 token rows x 32
+// contiguous bytes) then starts the 8 rows 8 banks apart, again every bank
+// once.  With the K padding on V every second row pair shared banks.
 template <int D>
 struct Stage {
   uint16_t k[kBlockTokens][D + 8];
-  uint16_t v[kBlockTokens][D + 8];
+  uint16_t v[kBlockTokens][D + 16];
 };
 
 template <int D>
@@ -156,20 +160,24 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillParams a) {
     const int rem = (threadIdx.x + u * kThreads) % (kBlockTokens * CH);
     voff[u] = (uint32_t)(rem / CH) * tok_stride + (uint32_t)g * D * 2 + 16u * (uint32_t)(rem % CH);
   }
-  // physical id of logical block blk, -1 when past the range or outside the
-  // pool (no branch: the table read is clamped into the range, nblk >= 1)
-  auto phys_of = [&](int blk) -> int {
-    const int phys = table[min(blk, nblk - 1)];
-    return blk < nblk && (unsigned)phys < (unsigned)a.num_blocks ? phys : -1;
+  // The block-table entries of step it, one per lane (lane l % 8: block 8 it +
+  // l % 8, clamped into the range, nblk >= 1): a vector load issued a whole
+  // step before the entries are used, instead of a scalar load per block
+  // waited for on the spot, which would stall every wave at every step.
+  auto table_vec = [&](int it) -> int {
+    const int blk = kStepBlocks * it + (lane & (kStepBlocks - 1));
+    return table[min(blk, nblk - 1)];
   };
-  // the blocks of step it into registers; returns bit bb set where block bb of
-  // the step is valid, so that the multiply needs no block-table reads
-  auto fetch = [&](int it, uint4(&r)[kStepBlocks][LOADS]) -> uint32_t {
+  // the blocks of step it into registers, their table entries in tv (from
+  // table_vec(it)); returns bit bb set where block bb of the step is valid (in
+  // the range and inside the pool), so that the multiply needs no table reads
+  auto fetch = [&](int it, int tv, uint4(&r)[kStepBlocks][LOADS]) -> uint32_t {
     uint32_t okm = 0;
 #pragma unroll
     for (int bb = 0; bb < kStepBlocks; ++bb) {
       const int blk = kStepBlocks * it + bb;
-      const int phys = phys_of(blk);
+      const int raw = __builtin_amdgcn_readlane(tv, bb);
+      const int phys = blk < nblk && (unsigned)raw < (unsigned)a.num_blocks ? raw : -1;
       okm |= (phys >= 0 ? 1u : 0u) << bb;
       const int valid = phys >= 0 ? min(kBlockTokens, L - blk * kBlockTokens) : 0;
       const size_t boff = phys >= 0 ? (size_t)phys * blk_bytes : 0;
@@ -349,15 +357,17 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillParams a) {
     uint4 r[kPrefetch][kStepBlocks][LOADS];
     uint32_t okm[kPrefetch + 1];
 #pragma unroll
-    for (int u = 0; u < kPrefetch; ++u) okm[u] = u < nit ? fetch(u, r[u]) : 0u;
+    for (int u = 0; u < kPrefetch; ++u) okm[u] = u < nit ? fetch(u, table_vec(u), r[u]) : 0u;
     put(0, r[0]);
-    okm[kPrefetch] = kPrefetch < nit ? fetch(kPrefetch, r[0]) : 0u;
+    okm[kPrefetch] = kPrefetch < nit ? fetch(kPrefetch, table_vec(kPrefetch), r[0]) : 0u;
     __syncthreads();
     for (int it0 = 0; it0 < nit; it0 += kPrefetch) {
 #pragma unroll
       for (int u = 0; u < kPrefetch; ++u) {
         const int it = it0 + u;
         if (it >= nit) break;
+        // table entries of the step fetched at the end of this one, loaded now
+        const int tv = it + 1 + kPrefetch < nit ? table_vec(it + 1 + kPrefetch) : 0;
         compute(it, it & 1, mode, okm[0]);
 #pragma unroll
         for (int k = 0; k < kPrefetch; ++k) okm[k] = okm[k + 1];
@@ -365,7 +375,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillParams a) {
         const int nxt = (u + 1) % kPrefetch;  // register slot of step it + 1 (constant once unrolled)
         if (it + 1 < nit) {
           put((it + 1) & 1, r[nxt]);
-          if (it + 1 + kPrefetch < nit) okm[kPrefetch] = fetch(it + 1 + kPrefetch, r[nxt]);
+          if (it + 1 + kPrefetch < nit) okm[kPrefetch] = fetch(it + 1 + kPrefetch, tv, r[nxt]);
         }
         __syncthreads();  // step it + 1 staged; everyone is done with step it
       }
