@@ -87,6 +87,8 @@ __device__ __forceinline__ uint32_t fp8x2_to_bf16x2(uint32_t codes) {
 template <int D, int NT, int NW, int NBUF, bool KV8, bool TREE>
 struct MfmaAttender {
   static constexpr int kThreads = NW * 64;
+  // the new tokens of pa_decode_append are stored by the schedule before run
+  __device__ static bool defers_append(const DecodeParams&) { return false; }
   static constexpr int kD = D;
   static constexpr int R = 16 * NT;  // rows, padded to whole tiles
   static constexpr int KS = D / 32;  // score k-steps

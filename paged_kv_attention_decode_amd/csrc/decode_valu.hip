@@ -132,6 +132,13 @@ struct ValuAttender {
 
   __device__ void store(size_t idx, float x) { store_elem<T>(static_cast<T*>(a.out) + idx, x); }
 
+  // pa_decode_append: when the new tokens' rows of one head fit one 16-byte
+  // chunk per lane, this kernel stores them itself (see run); otherwise the
+  // schedule stores them before run
+  __device__ static bool defers_append(const DecodeParams& a) {
+    return a.q_len * 2 * (a.append_row_bytes / 16) <= 64;
+  }
+
   // merged output of row r, column c over the waves
   __device__ float result(int r, int c, float& M, float& l) const {
     M = sm.m[0][r];
@@ -196,6 +203,37 @@ struct ValuAttender {
     // this wave's blocks: lo + w + NW * k
     const int n_mine = hi - lo > w ? (hi - lo - w + NW - 1) / NW : 0;
 
+    // pa_decode_append (one chunk per lane): lane i takes item i of the new
+    // tokens' rows of head g (token i / (2 C), K or V, 16-byte chunk i % C);
+    // the items of this wave's blocks are loaded now and each is stored just
+    // before its block's loads are issued (issue below), in this wave's
+    // program order, so the block's loads see it.  The load's latency is
+    // spent on the wave's earlier blocks instead of before the first one.
+    int app_blk = -1;  // logical block this lane's item goes to (-1: none)
+    uint4 app_data = make_uint4(0u, 0u, 0u, 0u);
+    char* app_dst = nullptr;
+    if (a.new_k && defers_append(a)) {
+      const int chunks = a.append_row_bytes / 16;
+      if (lane < a.q_len * 2 * chunks) {
+        const int j = lane / (2 * chunks), kv = (lane / chunks) & 1, c = lane % chunks;
+        const int pos = L - a.q_len + j;
+        const int blk = pos >= 0 ? pos / kBlockTokens : -1;
+        if (blk >= lo && blk < hi && (blk - lo) % NW == w) {
+          const int phys = table[blk];
+          if ((unsigned)phys < (unsigned)a.num_blocks) {
+            app_blk = blk;
+            app_data = *reinterpret_cast<const uint4*>(static_cast<const char*>(kv ? a.new_v : a.new_k) +
+                                                       ((size_t)(b * a.q_len + j) * a.n_kv + g) * a.append_row_bytes +
+                                                       16 * c);
+            app_dst = static_cast<char*>(const_cast<void*>(kv ? a.v_cache : a.k_cache)) +
+                      ((size_t)phys * kBlockTokens + pos % kBlockTokens) * a.n_kv * a.append_row_bytes +
+                      (size_t)g * a.append_row_bytes + 16 * c;
+          }
+        }
+      }
+    }
+    const bool app_any = __builtin_amdgcn_ballot_w64(app_blk >= 0) != 0;  // wave-uniform
+
     // ids of this wave's blocks k0 .. k0 + 63, one per lane
     auto block_ids = [&](int k0, int cnt) { return lane < cnt ? table[lo + w + NW * (k0 + lane)] : 0; };
 
@@ -203,6 +241,12 @@ struct ValuAttender {
       const int phys = __builtin_amdgcn_readlane(ids, kk < cnt ? kk : 0);
       ok = kk < cnt && (unsigned)phys < (unsigned)a.num_blocks;
       lblk = lo + w + NW * (k0 + kk);
+      if (app_any) {  // a new token of this block: stored before the block is loaded
+        if (app_blk == lblk) {
+          *reinterpret_cast<uint4*>(app_dst) = app_data;
+          app_blk = -1;
+        }
+      }
       const int valid = min(kBlockTokens, L - lblk * kBlockTokens);
       const size_t boff = ok ? (size_t)phys * blk_bytes : 0;
       const uint32_t nrec = ok ? (uint32_t)valid * tok_bytes : 0u;

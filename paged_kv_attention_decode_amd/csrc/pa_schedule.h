@@ -156,14 +156,15 @@ __device__ void drive_fixed(const DecodeParams& a, Attn& at) {
       write_zeros(a, at, b, g);
       return;
     }
-    if (a.new_k) append_new_tokens<Attn::kThreads>(a, b, g, L, 0, nblk);
+    if (a.new_k && !Attn::defers_append(a)) append_new_tokens<Attn::kThreads>(a, b, g, L, 0, nblk);
     at.run(b, g, L, 0, nblk);
     write_final(a, at, b, g);
     return;
   }
   const int lo = part * a.part_blocks;
   if (lo >= nblk) return;  // no token in this partition; pa_reduce never reads it
-  if (a.new_k) append_new_tokens<Attn::kThreads>(a, b, g, L, lo, min(lo + a.part_blocks, nblk));
+  if (a.new_k && !Attn::defers_append(a))
+    append_new_tokens<Attn::kThreads>(a, b, g, L, lo, min(lo + a.part_blocks, nblk));
   at.run(b, g, L, lo, min(lo + a.part_blocks, nblk));
   const int rows = a.group * a.q_len;
   for (int idx = threadIdx.x; idx < rows * Attn::kD; idx += Attn::kThreads) {
@@ -365,7 +366,7 @@ __device__ void drive_balanced(const DecodeParams& a, Attn& at) {
     const int nb = (int)(seg1 - seg0);
     const int blo = (int)((B0 > seg0 ? B0 : seg0) - seg0);
     const int bhi = (int)((B1 < seg1 ? B1 : seg1) - seg0);
-    if (a.new_k) append_new_tokens<NT>(a, bb, g, clamped_len(a, bb), blo, bhi);
+    if (a.new_k && !Attn::defers_append(a)) append_new_tokens<NT>(a, bb, g, clamped_len(a, bb), blo, bhi);
     at.run(bb, g, clamped_len(a, bb), blo, bhi);
     if (blo == 0 && bhi == nb) {
       write_final(a, at, bb, g);
