@@ -29,8 +29,9 @@
 //           ds_read_b64_tr_b16, which hands lane l the 4 tokens of one value
 //           column directly; call t covers columns 16 t + l % 16.
 //
-// The softmax takes each row's maximum over block 0 (every row sees position
-// 0) as a fixed reference; a score more than 2^64 above it raises a flag, and
+// The softmax takes each row's maximum over the first pair of blocks (blocks
+// 0 and 1; every row sees position 0) as a fixed reference; a score more than
+// 2^64 above it raises a flag, and
 // a workgroup whose flag is up redoes its rows exactly in two more sweeps
 // (true row maxima, then the weighted sums).  Weights are rounded to bf16 for
 // the P V product and the row sums add the same rounded weights.
