@@ -519,8 +519,13 @@ hipError_t launch_one(const DecodeParams& p, hipStream_t s) {
     hipLaunchKernelGGL((decode_valu_kernel<T, D, R, kWaves, kBalancedBlocksInFlight, true>), dim3(q.num_wgs),
                        dim3(kWaves * 64), 0, s, q);
   } else {
+    DecodeParams q = p;
+    if (p.mode == kSinglePass) {
+      static const int resident = resident_per_cu(decode_valu_kernel<T, D, R, kWaves, NB, false>, kWaves * 64);
+      q.pair_stride = one_pass_pairing(resident, p.num_seqs, p.n_kv);
+    }
     dim3 grid(p.mode == kPartitions ? p.num_parts : 1, p.n_kv, p.num_seqs);
-    hipLaunchKernelGGL((decode_valu_kernel<T, D, R, kWaves, NB, false>), grid, dim3(kWaves * 64), 0, s, p);
+    hipLaunchKernelGGL((decode_valu_kernel<T, D, R, kWaves, NB, false>), grid, dim3(kWaves * 64), 0, s, q);
   }
   return hipGetLastError();
 }

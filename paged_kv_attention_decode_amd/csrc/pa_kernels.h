@@ -51,6 +51,26 @@ int resident_per_cu(Kernel kernel, int threads) {
   return n;
 }
 
+// One-pass launches: the pairing stride for decode_pairing in pa_schedule.h,
+// or 0 for plain longest first.  The hardware hands workgroups out in launch
+// order, one per compute unit first, so with two resident per CU workgroups
+// k and k + CUs share a CU.  When the whole grid (S * n_kv workgroups) is
+// resident at once, two per CU at most, the first CUs / n_kv sequence slots
+// take the longest sequences and the rest are dealt shortest first, so that
+// each CU pairs a long sequence with a short one (longest processing time
+// first over the two slots) instead of the first and the CUs / n_kv-th
+// longest.  Larger grids run in rounds, where launch order in descending
+// length already balances.
+inline int one_pass_pairing(int resident_per_cu, int num_seqs, int n_kv) {
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) !=
+                                               hipSuccess || cus <= 0)
+    return 0;
+  const long long wgs = (long long)num_seqs * n_kv;
+  if (resident_per_cu != 2 || cus % n_kv != 0 || wgs <= cus || wgs > 2LL * cus) return 0;
+  return cus / n_kv;
+}
+
 struct DecodeParams {
   void* out;             // [S*q_len, n_h, D] (single pass and balanced)
   const void* q;         // [S*q_len, n_h, D]
@@ -77,6 +97,7 @@ struct DecodeParams {
   int part_blocks;       // partitions: blocks per partition
   int num_parts;         // partitions: partition stride of the workspace
   int num_wgs;           // balanced: workgroups in the grid (set by the launcher)
+  int pair_stride;       // one pass: one_pass_pairing's stride (0: longest first)
   int num_seqs;
 };
 

@@ -143,11 +143,20 @@ __device__ void append_new_tokens(const DecodeParams& a, int b, int g, int L, in
   }
 }
 
+// the length rank a one-pass workgroup slot takes: slots below the pairing
+// stride P take ranks 0 .. P - 1 (the longest), the others the remaining
+// ranks shortest first (S - 1 down to P), so that slot z and its CU partner
+// z + P hold ranks z and S - 1 - z (one_pass_pairing in pa_kernels.h)
+__device__ __forceinline__ int decode_pairing(const DecodeParams& a, int z) {
+  const int P = a.pair_stride;
+  return (P > 0 && z >= P) ? a.num_seqs - 1 + P - z : z;
+}
+
 template <class Attn>
 __device__ void drive_fixed(const DecodeParams& a, Attn& at) {
   const int part = blockIdx.x, g = blockIdx.y;
   const int b = a.mode == kSinglePass && a.num_seqs <= kLongestFirstMaxSeqs
-                    ? sequence_of_rank<Attn::kThreads>(a, (int)blockIdx.z)
+                    ? sequence_of_rank<Attn::kThreads>(a, decode_pairing(a, (int)blockIdx.z))
                     : (int)blockIdx.z;
   const int L = clamped_len(a, b);
   const int nblk = blocks_of(L);
