@@ -53,9 +53,9 @@ int resident_per_cu(Kernel kernel, int threads) {
 
 // One-pass launches: the pairing stride for decode_pairing in pa_schedule.h,
 // or 0 for plain longest first.  The hardware hands workgroups out in launch
-// order, one per compute unit first, so with two resident per CU workgroups
-// k and k + CUs share a CU.  When the whole grid (S * n_kv workgroups) is
-// resident at once, two per CU at most, the first CUs / n_kv sequence slots
+// order, one per compute unit first, so workgroups k and k + CUs share a CU
+// when at least two fit on one.  When the whole grid (S * n_kv workgroups)
+// fits in two per CU, the first CUs / n_kv sequence slots
 // take the longest sequences and the rest are dealt shortest first, so that
 // each CU pairs a long sequence with a short one (longest processing time
 // first over the two slots) instead of the first and the CUs / n_kv-th
@@ -67,7 +67,7 @@ inline int one_pass_pairing(int resident_per_cu, int num_seqs, int n_kv) {
                                                hipSuccess || cus <= 0)
     return 0;
   const long long wgs = (long long)num_seqs * n_kv;
-  if (resident_per_cu != 2 || cus % n_kv != 0 || wgs <= cus || wgs > 2LL * cus) return 0;
+  if (resident_per_cu < 2 || cus % n_kv != 0 || wgs <= cus || wgs > 2LL * cus) return 0;
   return cus / n_kv;
 }
 
