@@ -113,12 +113,18 @@ def trace(args):
     print("\n".join(out))
 
 
-def counters_of(d):
+def per_dispatch(d):
+    """{(kernel, counter): {dispatch id: value}} of a counter-collection folder."""
     rows = read_csv(os.path.join(d, "run_counter_collection.csv"))
     per = {}
     for r in rows:
         per.setdefault((r["Kernel_Name"], r["Counter_Name"]), {}).setdefault(int(r["Dispatch_Id"]), 0.0)
         per[(r["Kernel_Name"], r["Counter_Name"])][int(r["Dispatch_Id"])] += float(r["Counter_Value"])
+    return per
+
+
+def counters_of(d):
+    per = per_dispatch(d)
     return {k: statistics.median(v.values()) for k, v in per.items()}, {k: len(v) for k, v in per.items()}
 
 
@@ -129,19 +135,17 @@ def traffic(args):
     fetch, nf = counters_of(args.dirs[0])
     write, nw = counters_of(args.dirs[1])
     cal = {}
-    cal_items = list(fetch.items()) + list(write.items())
-    for d in args.calibration:  # runs whose copy calibrates the counters, when these have none
-        cal_items += list(counters_of(d)[0].items())
-    for (k, c), v in cal_items:
-        if "copyBuffer" in k and c in ("FETCH_SIZE", "WRITE_SIZE"):
-            cal[c] = max(cal.get(c, 0.0), v)  # the 1 GiB calibration copy is the largest copy
+    for d in list(args.dirs[:2]) + list(args.calibration):  # calibration copies: the runs' own, or others'
+        for (k, c), v in per_dispatch(d).items():
+            if "copyBuffer" in k and c in ("FETCH_SIZE", "WRITE_SIZE"):
+                cal[c] = max([cal.get(c, 0.0)] + list(v.values()))  # the 1 GiB copy is the largest one
     moved_kib = (1 << 30) / 1024
     fs = moved_kib / cal["FETCH_SIZE"] if cal.get("FETCH_SIZE") else 1.0
     ws = moved_kib / cal["WRITE_SIZE"] if cal.get("WRITE_SIZE") else 1.0
     kernels = [k for (k, c) in fetch if c == "FETCH_SIZE" and (is_main(k) or is_reduce(k))]
     p = wl.make_problem(args.config)
     ab = wl.algorithmic_bytes(p)
-    alg = ab["kv_unique"] + ab["q"]
+    alg = ab["kv_unique"] + ab["q"] + (ab["out"] if p.query_start is not None else 0)  # prefill: + the output
     fetch_b = sum(fetch[(k, "FETCH_SIZE")] for k in kernels) * 1024 * fs
     write_b = sum(write.get((k, "WRITE_SIZE"), 0.0) for k in kernels) * 1024 * ws
     sources = bench.PREFILL_SOURCES if p.query_start is not None else bench.KERNEL_SOURCES
@@ -170,8 +174,9 @@ def traffic(args):
     for k in kernels:
         out.append(f"`{short(k)}` ({nf[(k, 'FETCH_SIZE')]} dispatches): FETCH_SIZE {fetch[(k, 'FETCH_SIZE')]:.1f} KiB, "
                    f"WRITE_SIZE {write.get((k, 'WRITE_SIZE'), 0.0):.1f} KiB raw per dispatch (median).")
+    what = "KV of every context token once, shared blocks once, + Q" + (" + output" if p.query_start is not None else "")
     out += ["", f"Per launch after scaling: {fetch_b / 1e6:.2f} MB read, {write_b / 1e6:.2f} MB written; algorithmic "
-                f"bytes (KV of every context token once, shared blocks once, + Q) {alg / 1e6:.2f} MB; measured / "
+                f"bytes ({what}) {alg / 1e6:.2f} MB; measured / "
                 f"algorithmic = {(fetch_b + write_b) / alg:.4f}.",
             "", f"Kernel sources hash {res['kernel_source_sha']} (comments and blank space removed); bench.py uses "
                 f"these figures only while it matches."]
