@@ -133,8 +133,12 @@ class Resident:
 
         self.pa, self.p, self.partition, self.torch = pa, p, partition, torch
         self.q = to_dev(p.q, torch)
-        self.k_cache = to_dev(p.k_cache, torch)
-        self.v_cache = to_dev(p.v_cache, torch)
+        # one allocation per layer, V placed by pa_kv_cache_layout (one head slice off K's offsets)
+        tk = to_dev(p.k_cache, torch)
+        self.k_cache, self.v_cache = pa.allocate_kv_cache(tk.shape[0], tk.shape[2], tk.shape[3], tk.dtype, "cuda")
+        self.k_cache.copy_(tk)
+        del tk
+        self.v_cache.copy_(to_dev(p.v_cache, torch))
         self.tables = torch.from_numpy(p.block_tables).cuda()
         self.lens = torch.from_numpy(p.context_lens).cuda()
         self.new_k = to_dev(p.new_k, torch) if p.new_k is not None else None

@@ -15,7 +15,10 @@
  *                   scale per KV head;
  *   pa_decode_tree  verify a tree of draft tokens under a tree mask;
  *   pa_prefill      chunked prefill: new tokens of varying count per sequence;
- *   pa_copy_blocks  copy whole blocks (copy-on-write, swapping).
+ *   pa_copy_blocks  copy whole blocks (copy-on-write, swapping);
+ *   pa_kv_cache_layout
+ *                   where to place the K and V pools of one layer in one
+ *                   allocation (a host-side query; launches nothing).
  *
  * Sources of the definitions (the web pages this library implements):
  *   - per layer, K and V are each stored as [num_blocks, block_size,
@@ -430,6 +433,40 @@ pa_status pa_prefill(void* out, const void* q, const void* k_cache, const void* 
 pa_status pa_copy_blocks(const void* src_k, const void* src_v, void* dst_k, void* dst_v,
                          const int64_t* block_mapping, int32_t num_pairs, int32_t src_num_blocks,
                          int32_t dst_num_blocks, int64_t block_bytes, void* stream);
+
+/*
+ * pa_kv_cache_layout - placement of one layer's K and V pools in one allocation.
+ *
+ * The pools keep the per-layer shape [num_blocks, block_size, num_kv_heads,
+ * head_dim] ("LLM Inference Serving", systeminternals.dev, the passage on the
+ * per-layer cache shape); this query only says where the V pool starts.  K
+ * sits at byte 0 of an allocation whose base the caller aligns to 2 KiB; V
+ * starts at *v_offset, the K pool's size rounded up to 2 KiB plus one head
+ * slice (head_dim * elem_bytes, rounded up to 128 bytes, modulo 2 KiB).
+ *
+ * Why: on MI355X, reads of the slices that sit at some offsets within each
+ * 1 KiB of the address space complete more slowly than the others.  With the
+ * pools back to back, K and V of a KV head sit at the same offsets, so the
+ * decode workgroups of two heads stream two slow slices per token while the
+ * others stream none, and those workgroups set the launch's length.  Moving V
+ * by one slice puts the slow K and slow V slices on different heads (measured
+ * on the one-pass decode of 64 sequences of 512..4096 tokens, 8 KV heads of
+ * 128: 111 us to 106 us in bf16, 60 us to 55 us with fp8 codes).  Every entry
+ * point accepts any placement; this one is faster, not required.
+ *
+ *   num_blocks    blocks of each pool, > 0.
+ *   block_size    16.
+ *   num_kv_heads, head_dim
+ *                 > 0.
+ *   elem_bytes    bytes of one cache element: 1 (fp8 codes), 2 (bf16) or 4 (fp32).
+ *   total_bytes   out: bytes of the allocation holding both pools.
+ *   v_offset      out: byte offset of the V pool in it (a multiple of 128).
+ *
+ * PA_ERR_NULL for a NULL output, PA_ERR_SHAPE for a size out of range,
+ * PA_ERR_UNSUPPORTED for another block_size or a size past 2^62 bytes.
+ */
+pa_status pa_kv_cache_layout(int64_t num_blocks, int32_t block_size, int32_t num_kv_heads, int32_t head_dim,
+                             int32_t elem_bytes, int64_t* total_bytes, int64_t* v_offset);
 
 const char* pa_status_string(pa_status status);
 

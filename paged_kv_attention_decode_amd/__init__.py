@@ -13,6 +13,7 @@ on the GPU, the call raises.
     paged_attention(...)   # decode, plus reduce when the context is split
     cache_write_fp8(...), decode_fp8(...)   # the same over an fp8 (E4M3) cache with per-head scales
     copy_blocks(...)       # whole-block copies (copy-on-write, swapping)
+    kv_cache_layout(...), allocate_kv_cache(...)   # one layer's K and V pools in one allocation
 """
 
 from __future__ import annotations
@@ -24,7 +25,7 @@ from typing import Optional
 __all__ = [
     "PA_F32", "PA_BF16", "PA_BALANCED", "PagedAttentionError", "library_path", "load_library", "status_string", "version",
     "cache_write", "decode", "reduce", "decode_workspace_size", "paged_attention", "cache_write_fp8", "decode_fp8",
-    "decode_tree", "prefill", "copy_blocks", "decode_balanced_noalloc", "decode_append", "SYMBOLS",
+    "decode_tree", "prefill", "copy_blocks", "decode_balanced_noalloc", "decode_append", "kv_cache_layout", "allocate_kv_cache", "SYMBOLS",
 ]
 
 PA_F32, PA_BF16 = 0, 1
@@ -32,7 +33,7 @@ PA_BALANCED = -1  # partition_size selecting the work-balanced decode
 BLOCK_SIZE = 16
 SYMBOLS = ("pa_cache_write", "pa_decode", "pa_decode_workspace_size", "pa_reduce", "pa_status_string", "pa_version",
            "pa_cache_write_fp8", "pa_decode_fp8", "pa_decode_tree", "pa_prefill", "pa_copy_blocks",
-           "pa_decode_balanced_noalloc", "pa_decode_append")
+           "pa_decode_balanced_noalloc", "pa_decode_append", "pa_kv_cache_layout")
 _STATUS = {0: "PA_OK", 1: "PA_ERR_NULL", 2: "PA_ERR_SHAPE", 3: "PA_ERR_UNSUPPORTED", 4: "PA_ERR_WORKSPACE",
            5: "PA_ERR_HIP", 6: "PA_ERR_MEMORY", 7: "PA_ERR_SCRATCH"}
 
@@ -88,11 +89,12 @@ def load_library():
                                ctypes.c_int, vp]
     lib.pa_copy_blocks.restype = ctypes.c_int
     lib.pa_copy_blocks.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, ctypes.c_int64, vp]
+    lib.pa_kv_cache_layout.restype = ctypes.c_int
+    lib.pa_kv_cache_layout.argtypes = [i64, i32, i32, i32, i32, ctypes.POINTER(i64), ctypes.POINTER(i64)]
     lib.pa_status_string.restype = ctypes.c_char_p
     lib.pa_status_string.argtypes = [ctypes.c_int]
     lib.pa_version.restype = i32
     lib.pa_version.argtypes = []
-    del i64
     _lib = lib
     return lib
 
@@ -492,3 +494,31 @@ def copy_blocks(src_k, src_v, dst_k, dst_v, block_mapping, stream=None) -> None:
                                        block_mapping.shape[0], src_k.shape[0], dst_k.shape[0], block_bytes,
                                        _stream(stream))
     _check(st, "pa_copy_blocks")
+
+
+def kv_cache_layout(num_blocks: int, num_kv_heads: int, head_dim: int, elem_bytes: int) -> tuple:
+    """pa_kv_cache_layout: (total_bytes, v_offset) of one allocation holding a layer's K pool
+    at byte 0 and its V pool at v_offset, each [num_blocks, 16, num_kv_heads, head_dim] of
+    elem_bytes-byte elements.  A host-side query; needs no GPU."""
+    total, voff = ctypes.c_int64(0), ctypes.c_int64(0)
+    st = load_library().pa_kv_cache_layout(num_blocks, BLOCK_SIZE, num_kv_heads, head_dim, elem_bytes,
+                                           ctypes.byref(total), ctypes.byref(voff))
+    _check(st, "pa_kv_cache_layout")
+    return int(total.value), int(voff.value)
+
+
+def allocate_kv_cache(num_blocks: int, num_kv_heads: int, head_dim: int, dtype, device="cuda") -> tuple:
+    """One layer's (k_cache, v_cache), each [num_blocks, 16, num_kv_heads, head_dim] of dtype
+    (torch.bfloat16, torch.float32, or torch.uint8 for fp8 codes), placed in one allocation
+    as pa_kv_cache_layout says: K at a 2 KiB-aligned base, V one head slice off K's offsets.
+    The two tensors are views that keep the allocation alive; contents are uninitialized."""
+    torch = _torch()
+    elem = torch.empty((), dtype=dtype).element_size()
+    total, voff = kv_cache_layout(num_blocks, num_kv_heads, head_dim, elem)
+    buf = torch.empty(total + 2048, dtype=torch.uint8, device=device)
+    base = (-buf.data_ptr()) % 2048
+    pool = num_blocks * BLOCK_SIZE * num_kv_heads * head_dim * elem
+    shape = (num_blocks, BLOCK_SIZE, num_kv_heads, head_dim)
+    k = buf[base:base + pool].view(dtype).view(shape)
+    v = buf[base + voff:base + voff + pool].view(dtype).view(shape)
+    return k, v

@@ -192,6 +192,23 @@ pa_status pa_copy_blocks(const void* src_k, const void* src_v, void* dst_k, void
   return from_hip(pa::launch_copy_blocks(p, static_cast<hipStream_t>(stream)));
 }
 
+pa_status pa_kv_cache_layout(int64_t num_blocks, int32_t block_size, int32_t num_kv_heads, int32_t head_dim,
+                             int32_t elem_bytes, int64_t* total_bytes, int64_t* v_offset) {
+  if (!total_bytes || !v_offset) return PA_ERR_NULL;
+  if (num_blocks <= 0 || num_kv_heads <= 0 || head_dim <= 0 || block_size <= 0 ||
+      (elem_bytes != 1 && elem_bytes != 2 && elem_bytes != 4))
+    return PA_ERR_SHAPE;
+  if (block_size != kBlock) return PA_ERR_UNSUPPORTED;
+  constexpr long long kPeriod = 2048, kLine = 128, kMax = 1LL << 62;
+  const long long row = (long long)num_kv_heads * head_dim * elem_bytes;  // < 2^35
+  if (num_blocks > kMax / (block_size * row) / 3) return PA_ERR_UNSUPPORTED;
+  const long long pool = num_blocks * block_size * row;
+  const long long slice = ((long long)head_dim * elem_bytes + kLine - 1) / kLine * kLine % kPeriod;
+  *v_offset = (pool + kPeriod - 1) / kPeriod * kPeriod + slice;
+  *total_bytes = *v_offset + pool;
+  return PA_OK;
+}
+
 size_t pa_decode_workspace_size(int32_t num_seqs, int32_t q_len, int32_t num_q_heads, int32_t num_kv_heads,
                                 int32_t head_dim, int32_t max_blocks_per_seq, int32_t block_size,
                                 int32_t partition_size) {

@@ -103,6 +103,18 @@ def to_dev(a: np.ndarray, dtype: str, device="cuda"):
     return torch.from_numpy(a).to(device)
 
 
+def to_dev_pools(k: np.ndarray, v: np.ndarray, dtype: str, device="cuda"):
+    """A layer's K and V pools in one allocation, placed by the library's layout query."""
+    import paged_kv_attention_decode_amd as pa
+
+    tk = to_dev(k, dtype, device)
+    kc, vc = pa.allocate_kv_cache(k.shape[0], k.shape[2], k.shape[3], tk.dtype, device)
+    kc.copy_(tk)
+    del tk
+    vc.copy_(to_dev(v, dtype, device))
+    return kc, vc
+
+
 def to_host(t) -> np.ndarray:
     import torch
 
@@ -125,8 +137,7 @@ class DeviceProblem:
         self.p = p
         dt = p.dtype
         self.q = to_dev(p.q, dt, device)
-        self.k_cache = to_dev(p.k_cache, dt, device)
-        self.v_cache = to_dev(p.v_cache, dt, device)
+        self.k_cache, self.v_cache = to_dev_pools(p.k_cache, p.v_cache, dt, device)
         self.block_tables = torch.from_numpy(p.block_tables).to(device)
         self.context_lens = torch.from_numpy(p.context_lens).to(device)
         self.new_k = self.new_v = self.slots = None

@@ -207,3 +207,40 @@ def test_binding_refuses_host_tensors():
     with pytest.raises(ValueError, match="GPU"):
         pa.decode(q, torch.zeros(16, 16, 2, 64), torch.zeros(16, 16, 2, 64), torch.zeros(2, 3, dtype=torch.int32),
                   torch.ones(2, dtype=torch.int32), 0.125)
+
+
+def _layout(lib, nb, bs, n_kv, d, eb):
+    total, voff = ctypes.c_int64(-1), ctypes.c_int64(-1)
+    st = lib.pa_kv_cache_layout(nb, bs, n_kv, d, eb, ctypes.byref(total), ctypes.byref(voff))
+    return st, total.value, voff.value
+
+
+def test_kv_cache_layout_places_v_one_head_slice_off(lib):
+    # the 8B layer's pools (20,000 blocks of 16 tokens x 8 heads x 128): bf16 and fp8 codes
+    assert _layout(lib, 20000, 16, 8, 128, 2) == (0, 2 * 655360000 + 256, 655360000 + 256)
+    assert _layout(lib, 20000, 16, 8, 128, 1) == (0, 2 * 327680000 + 128, 327680000 + 128)
+    # a pool that is not a multiple of 2 KiB rounds up first; a 64-byte slice rounds up to 128
+    assert _layout(lib, 1, 16, 1, 64, 1) == (0, 2048 + 128 + 1024, 2048 + 128)
+    for nb in (1, 3, 1000):
+        for n_kv in (1, 2, 8):
+            for d in (64, 128):
+                for eb in (1, 2, 4):
+                    st, total, voff = _layout(lib, nb, 16, n_kv, d, eb)
+                    pool = nb * 16 * n_kv * d * eb
+                    slice_ = -(-d * eb // 128) * 128 % 2048
+                    assert st == 0 and voff % 128 == 0 and voff >= pool and total == voff + pool
+                    assert voff % 2048 == slice_, (nb, n_kv, d, eb)
+    # with 2 KiB token rows (8 heads of 128 bf16) no head has K and V at the same offset within 1 KiB
+    _, _, voff = _layout(lib, 20000, 16, 8, 128, 2)
+    assert all((256 * g) % 1024 != (voff + 256 * g) % 1024 for g in range(8))
+
+
+def test_kv_cache_layout_rejects_invalid_arguments(lib):
+    total, voff = ctypes.c_int64(0), ctypes.c_int64(0)
+    assert lib.pa_kv_cache_layout(16, 16, 8, 128, 2, None, ctypes.byref(voff)) == 1
+    assert lib.pa_kv_cache_layout(16, 16, 8, 128, 2, ctypes.byref(total), None) == 1
+    assert _layout(lib, 0, 16, 8, 128, 2)[0] == 2
+    assert _layout(lib, 16, 16, 0, 128, 2)[0] == 2
+    assert _layout(lib, 16, 16, 8, 128, 3)[0] == 2
+    assert _layout(lib, 16, 32, 8, 128, 2)[0] == 3          # block_size other than 16
+    assert _layout(lib, 1 << 50, 16, 8, 128, 2)[0] == 3     # past 2^62 bytes

@@ -168,6 +168,28 @@ def test_physical_permutation_is_bitwise_invariant(ps, wide):
     assert np.array_equal(a, b)
 
 
+@pytest.mark.parametrize("ps", [0, 64, -1])
+def test_cache_placement_is_bitwise_invariant(ps):
+    """The pools in one allocation as pa_kv_cache_layout places them (what DeviceProblem
+    uses) and in two separate allocations give the same bits; the layout's views are
+    disjoint, 2 KiB-aligned for K and one head slice off for V."""
+    p = wl.make_problem(INV_SPEC_WIDE)
+    say(f"placement ps={ps}")
+    d = DeviceProblem(p)
+    kc, vc = d.k_cache, d.v_cache
+    nbytes = kc.numel() * kc.element_size()
+    slice_ = p.spec.head_dim * kc.element_size()
+    assert kc.data_ptr() % 2048 == 0 and (vc.data_ptr() - kc.data_ptr()) % 2048 == slice_
+    assert vc.data_ptr() >= kc.data_ptr() + nbytes
+    a = to_host(d.step(ps, write=False).clone())
+    d.k_cache, d.v_cache = kc.clone(), vc.clone()  # separate allocations, same contents
+    assert d.k_cache.data_ptr() != kc.data_ptr()
+    b = to_host(d.step(ps, write=False).clone())
+    torch.cuda.synchronize()
+    assert np.array_equal(a, b)
+    assert np.array_equal(to_host(d.k_cache), to_host(kc)) and np.array_equal(to_host(d.v_cache), to_host(vc))
+
+
 @pytest.mark.parametrize("wide", [False, True], ids=["rows8", "rows40"])
 @pytest.mark.parametrize("ps", [0, 64])
 def test_repeatable_and_batch_independent(ps, wide):
