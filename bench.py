@@ -7,7 +7,9 @@ then pa_decode, for the fp8 and tree layers and with --separate-write), and
 pa_reduce when the context is split.  The inputs are
 the seeded synthetic Llama-3-8B-shaped decode layer (64 sequences, 32 query
 heads / 8 KV heads, head_dim 128, bf16, contexts uniform in [512, 4096], a
-20,000-block pool), resident in HBM before timing starts.
+20,000-block pool), resident in HBM before timing starts.  Before the W
+warm-up steps the step runs untimed for --settle-ms (100 ms) so that the
+GPU has left its idle clocks.
 
 Prints one JSON line:
   value          tokens/s of whole steps (num_seqs * q_len tokens per step),
@@ -311,6 +313,7 @@ def bench_copy_blocks(args, torch) -> int:
             src, dst = (hk, hv), (kc, vc)
         moved, bound, peak = 2 * n * block_bytes, "pcie", PCIE_PEAK_GBPS  # K and V across the link
     mapping = torch.from_numpy(pairs.astype(np.int64)).cuda()
+    settle(lambda: pa.copy_blocks(*src, *dst, mapping), args.settle_ms, torch)
     for _ in range(max(0, args.warmup)):
         pa.copy_blocks(*src, *dst, mapping)
     torch.cuda.synchronize()
@@ -340,11 +343,30 @@ def bench_copy_blocks(args, torch) -> int:
     return 0
 
 
+def settle(step, ms: float, torch) -> float:
+    """Run the step, untimed, until ms of wall clock have passed; returns the time spent.
+
+    An idle MI355X starts a burst of work at lower clocks and takes tens of
+    milliseconds to reach its steady ones: launches in the first ~30 ms of a
+    process ran 6-12% slower.  The settle runs before the W warm-up steps so
+    that the timed steps see the steady state, as a continuously busy server's
+    GPU would, whatever W the caller picks."""
+    t0 = time.perf_counter()
+    while (time.perf_counter() - t0) * 1e3 < ms:
+        for _ in range(8):
+            step()
+        torch.cuda.synchronize()
+    return (time.perf_counter() - t0) * 1e3
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--settle-ms", type=float, default=100.0,
+                    help="before the warm-up steps, run the step untimed for this long so the GPU leaves its "
+                         "idle clocks (0 skips it)")
     ap.add_argument("--config", default=DEFAULT_CONFIG, choices=list(wl.CONFIGS))
     ap.add_argument("--partition", type=int, default=None, help="override the context split (0 = one pass)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the cpu_baseline leg")
@@ -381,6 +403,7 @@ def main(argv=None):
     partition = partition_for(p) if args.partition is None else args.partition
     r = Resident(p, partition, torch, args.separate_write)
 
+    settle_ms = settle(r.step, args.settle_ms, torch)
     for _ in range(max(0, args.warmup)):
         r.step()
     torch.cuda.synchronize()
@@ -529,6 +552,7 @@ def main(argv=None):
         "n_gpus": 1,
         "steps": K,
         "warmup": args.warmup,
+        "settle_ms": round(settle_ms, 1),
         "ms_per_step": round(ms_per_step, 5),
         "higher_is_better": True,
         "scaling": "weak",
