@@ -113,6 +113,9 @@ def trace(args):
     print("\n".join(out))
 
 
+CALIBRATION_COPIES = 5  # bench.py --calibrate-copy: 1 GiB device-to-device copies at the end of the run
+
+
 def per_dispatch(d):
     """{(kernel, counter): {dispatch id: value}} of a counter-collection folder."""
     rows = read_csv(os.path.join(d, "run_counter_collection.csv"))
@@ -137,8 +140,16 @@ def traffic(args):
     cal = {}
     for d in list(args.dirs[:2]) + list(args.calibration):  # calibration copies: the runs' own, or others'
         for (k, c), v in per_dispatch(d).items():
-            if "copyBuffer" in k and c in ("FETCH_SIZE", "WRITE_SIZE"):
-                cal[c] = max([cal.get(c, 0.0)] + list(v.values()))  # the 1 GiB copy is the largest one
+            if "copyBuffer" in k and c in ("FETCH_SIZE", "WRITE_SIZE") and c not in cal:
+                # bench.py --calibrate-copy makes five 1 GiB copies in a row; other copies (the
+                # workload's pools placed on the device, results read back) come singly or in
+                # pairs, of other sizes: take the largest run of five consecutive copy
+                # dispatches that agree to 1%
+                vals = [v[i] for i in sorted(v)]
+                runs = [vals[i:i + CALIBRATION_COPIES] for i in range(len(vals) - CALIBRATION_COPIES + 1)]
+                runs = [r for r in runs if min(r) > 0 and max(r) <= 1.01 * min(r)]
+                if runs:
+                    cal[c] = statistics.median(max(runs, key=statistics.median))
     moved_kib = (1 << 30) / 1024
     fs = moved_kib / cal["FETCH_SIZE"] if cal.get("FETCH_SIZE") else 1.0
     ws = moved_kib / cal["WRITE_SIZE"] if cal.get("WRITE_SIZE") else 1.0
