@@ -22,7 +22,8 @@ Prints one JSON line:
                  (the fp8 layer), warm launches are partly served from the MALL,
                  so the figure is taken over cold launches instead.
   roofline_cold  (roofline_warm) the same figure over the other kind of launch:
-                 cold launches run one at a time, each after a 1 GiB read
+                 cold launches each follow a 1 GiB read; their time is that of
+                 N (read, launch) pairs less that of N reads, one event pair each
   cpu_baseline   the fp64 oracle on a bounded sample of the same workload
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--config NAME] [--partition P]
@@ -462,22 +463,32 @@ def main(argv=None):
     # cold-cache decode launches: a 1 GiB read between launches evicts L2 and MALL.  A read,
     # not a write: the lines a write leaves dirty would be written back during the timed
     # launch (measured: +45-60 us on every workload), which times the flush, not the decode.
+    # Timed by difference, so that no event pair sits around a single launch (a pair costs
+    # about 5 us of GPU time, most of a fp8 launch's 8%): one event pair around N (read, launch)
+    # pairs and one around N reads alone, three rounds, the median of the differences / N.
     cold_ms = None
     if args.cold > 0:
         scratch = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
         scratch.sum()
         torch.cuda.synchronize()
-        times = []
-        for _ in range(args.cold):
-            scratch.sum()
+
+        def timed(with_launch: bool) -> float:
             a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             a.record()
-            r.decode()
-            r.reduce()
+            for _ in range(args.cold):
+                scratch.sum()
+                if with_launch:
+                    r.decode()
+                    r.reduce()
             b.record()
             torch.cuda.synchronize()
-            times.append(a.elapsed_time(b))
-        cold_ms = float(np.median(times))
+            return a.elapsed_time(b)
+
+        diffs = []
+        for _ in range(3):
+            reads = timed(False)
+            diffs.append((timed(True) - reads) / args.cold)
+        cold_ms = float(np.median(diffs))
         del scratch
 
     if args.calibrate_copy:
@@ -525,7 +536,8 @@ def main(argv=None):
                 "traffic": round(traffic, 1) if isinstance(traffic, float) else None,
                 "kernel": kernel,
                 "timing": ("cold launches (each after a 1 GiB read; the working set is under twice the "
-                           "256 MB MALL, which serves part of it between warm launches)") if cold_basis
+                           "256 MB MALL, which serves part of it between warm launches): one event pair around "
+                           f"{args.cold} (read, launch) pairs minus one around {args.cold} reads") if cold_basis
                 else f"warm launches: {K} back to back, one event pair around them",
                 "algorithmic_bytes_per_launch": kv_bytes,
                 "avg_launch_us": round(basis_s * 1e6, 2)}
