@@ -115,6 +115,15 @@ struct MfmaAttender {
   __device__ void store(size_t idx, float x) {
     static_cast<uint16_t*>(a.out)[idx] = (uint16_t)f32_to_bf16_bits(x);
   }
+  // out[idx .. idx + 7] = x, one 16-byte store (idx a multiple of 8)
+  __device__ void store8(size_t idx, const float (&x)[8]) {
+    uint4 v;
+    v.x = f32_to_bf16_bits(x[0]) | (f32_to_bf16_bits(x[1]) << 16);
+    v.y = f32_to_bf16_bits(x[2]) | (f32_to_bf16_bits(x[3]) << 16);
+    v.z = f32_to_bf16_bits(x[4]) | (f32_to_bf16_bits(x[5]) << 16);
+    v.w = f32_to_bf16_bits(x[6]) | (f32_to_bf16_bits(x[7]) << 16);
+    *reinterpret_cast<uint4*>(static_cast<uint16_t*>(a.out) + idx) = v;
+  }
 
   __device__ float result(int r, int c, float& M, float& l) const {
     M = sm.m[r];

@@ -131,6 +131,21 @@ struct ValuAttender {
         tv((threadIdx.x & 63) / NC) {}
 
   __device__ void store(size_t idx, float x) { store_elem<T>(static_cast<T*>(a.out) + idx, x); }
+  // out[idx .. idx + 7] = x in the output type (idx a multiple of 8): 16 or 32 bytes
+  __device__ void store8(size_t idx, const float (&x)[8]) {
+    if constexpr (kBF16) {
+      uint4 v;
+      v.x = f32_to_bf16_bits(x[0]) | (f32_to_bf16_bits(x[1]) << 16);
+      v.y = f32_to_bf16_bits(x[2]) | (f32_to_bf16_bits(x[3]) << 16);
+      v.z = f32_to_bf16_bits(x[4]) | (f32_to_bf16_bits(x[5]) << 16);
+      v.w = f32_to_bf16_bits(x[6]) | (f32_to_bf16_bits(x[7]) << 16);
+      *reinterpret_cast<uint4*>(static_cast<uint16_t*>(a.out) + idx) = v;
+    } else {
+      float* o = static_cast<float*>(a.out) + idx;
+      *reinterpret_cast<float4*>(o) = make_float4(x[0], x[1], x[2], x[3]);
+      *reinterpret_cast<float4*>(o + 4) = make_float4(x[4], x[5], x[6], x[7]);
+    }
+  }
 
   // pa_decode_append: when the new tokens' rows of one head fit one 16-byte
   // chunk per lane, this kernel stores them itself (see run); otherwise the
