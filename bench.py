@@ -22,7 +22,7 @@ Prints one JSON line:
                  (the fp8 layer), warm launches are partly served from the MALL,
                  so the figure is taken over cold launches instead.
   roofline_cold  (roofline_warm) the same figure over the other kind of launch:
-                 cold launches each follow a 1 GiB read; their time is that of
+                 cold launches each follow a 512 MiB read; their time is that of
                  N (read, launch) pairs less that of N reads, one event pair each
   cpu_baseline   the fp64 oracle on a bounded sample of the same workload
 
@@ -314,7 +314,7 @@ def bench_copy_blocks(args, torch) -> int:
             src, dst = (hk, hv), (kc, vc)
         moved, bound, peak = 2 * n * block_bytes, "pcie", PCIE_PEAK_GBPS  # K and V across the link
     mapping = torch.from_numpy(pairs.astype(np.int64)).cuda()
-    settle(lambda: pa.copy_blocks(*src, *dst, mapping), args.settle_ms, torch)
+    settle_ms, settle_steps = settle(lambda: pa.copy_blocks(*src, *dst, mapping), args.settle_ms, torch)
     for _ in range(max(0, args.warmup)):
         pa.copy_blocks(*src, *dst, mapping)
     torch.cuda.synchronize()
@@ -334,7 +334,8 @@ def bench_copy_blocks(args, torch) -> int:
     what = "HBM GB/s (read + written)" if bound == "hbm" else "host-link GB/s"
     print(json.dumps({
         "metric": f"pa_copy_blocks {what} per call", "value": round(achieved, 1), "unit": "GB/s",
-        "n_gpus": 1, "steps": K, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5),
+        "n_gpus": 1, "steps": K, "warmup": args.warmup, "settle_ms": round(settle_ms, 1), "settle_steps": settle_steps,
+        "ms_per_step": round(ms_per_step, 5),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": p.dtype, "data": "synthetic",
         "config": {"workload": args.config, "op": args.op, "blocks_copied": n, "block_bytes": block_bytes},
         "roofline": {"bound": bound, "achieved": round(achieved, 1), "peak": peak, "unit": "GB/s",
@@ -344,20 +345,25 @@ def bench_copy_blocks(args, torch) -> int:
     return 0
 
 
-def settle(step, ms: float, torch) -> float:
+COLD_ROUNDS = 9  # rounds of the cold-launch timing (each times args.cold launches)
+
+
+def settle(step, ms: float, torch) -> tuple:
     """Run the step, untimed, until ms of wall clock have passed; returns the time spent.
 
     An idle MI355X starts a burst of work at lower clocks and takes tens of
     milliseconds to reach its steady ones: launches in the first ~30 ms of a
     process ran 6-12% slower.  The settle runs before the W warm-up steps so
     that the timed steps see the steady state, as a continuously busy server's
-    GPU would, whatever W the caller picks."""
+    GPU would, whatever W the caller picks.  Returns (milliseconds, steps run)."""
     t0 = time.perf_counter()
+    steps = 0
     while (time.perf_counter() - t0) * 1e3 < ms:
         for _ in range(8):
             step()
+        steps += 8
         torch.cuda.synchronize()
-    return (time.perf_counter() - t0) * 1e3
+    return (time.perf_counter() - t0) * 1e3, steps
 
 
 def main(argv=None):
@@ -372,7 +378,7 @@ def main(argv=None):
     ap.add_argument("--partition", type=int, default=None, help="override the context split (0 = one pass)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the cpu_baseline leg")
     ap.add_argument("--cold", type=int, default=8,
-                    help="also time this many decode launches one by one, each after reading 1 GiB "
+                    help="also time this many decode launches one by one, each after reading 512 MiB "
                          "(evicts L2 and MALL); 0 skips them")
     ap.add_argument("--op", default="decode", choices=["decode", "copy-blocks", "swap-out", "swap-in"],
                     help="decode: the whole path (default); copy-blocks: pa_copy_blocks of 2048 blocks within "
@@ -404,7 +410,7 @@ def main(argv=None):
     partition = partition_for(p) if args.partition is None else args.partition
     r = Resident(p, partition, torch, args.separate_write)
 
-    settle_ms = settle(r.step, args.settle_ms, torch)
+    settle_ms, settle_steps = settle(r.step, args.settle_ms, torch)
     for _ in range(max(0, args.warmup)):
         r.step()
     torch.cuda.synchronize()
@@ -460,15 +466,16 @@ def main(argv=None):
     decode_only_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in bev]))
     reduce_ms = float(np.mean([e[2].elapsed_time(e[3]) for e in bev])) if partition > 0 else 0.0
 
-    # cold-cache decode launches: a 1 GiB read between launches evicts L2 and MALL.  A read,
+    # cold-cache decode launches: a 512 MiB read between launches (twice the 256 MB MALL and
+    # the 8 x 4 MB of L2) evicts both.  A read,
     # not a write: the lines a write leaves dirty would be written back during the timed
     # launch (measured: +45-60 us on every workload), which times the flush, not the decode.
     # Timed by difference, so that no event pair sits around a single launch (a pair costs
     # about 5 us of GPU time, most of a fp8 launch's 8%): one event pair around N (read, launch)
-    # pairs and one around N reads alone, three rounds, the median of the differences / N.
+    # pairs and one around N reads alone, nine rounds, the median of the differences / N.
     cold_ms = None
     if args.cold > 0:
-        scratch = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
+        scratch = torch.ones(1 << 27, dtype=torch.float32, device="cuda")
         scratch.sum()
         torch.cuda.synchronize()
 
@@ -485,7 +492,7 @@ def main(argv=None):
             return a.elapsed_time(b)
 
         diffs = []
-        for _ in range(3):
+        for _ in range(COLD_ROUNDS):
             reads = timed(False)
             diffs.append((timed(True) - reads) / args.cold)
         cold_ms = float(np.median(diffs))
@@ -535,7 +542,7 @@ def main(argv=None):
                 "frac": round(achieved / HBM_PEAK_GBPS, 4),
                 "traffic": round(traffic, 1) if isinstance(traffic, float) else None,
                 "kernel": kernel,
-                "timing": ("cold launches (each after a 1 GiB read; the working set is under twice the "
+                "timing": ("cold launches (each after a 512 MiB read; the working set is under twice the "
                            "256 MB MALL, which serves part of it between warm launches): one event pair around "
                            f"{args.cold} (read, launch) pairs minus one around {args.cold} reads") if cold_basis
                 else f"warm launches: {K} back to back, one event pair around them",
@@ -565,6 +572,7 @@ def main(argv=None):
         "steps": K,
         "warmup": args.warmup,
         "settle_ms": round(settle_ms, 1),
+        "settle_steps": settle_steps,
         "ms_per_step": round(ms_per_step, 5),
         "higher_is_better": True,
         "scaling": "weak",
@@ -588,7 +596,8 @@ def main(argv=None):
                          "decode": round(decode_only_ms * 1e3, 2),
                          "reduce": round(reduce_ms * 1e3, 2),
                          "decode_plus_reduce_timed": round(decode_ms * 1e3, 2),
-                         "decode_plus_reduce_cold": None if cold_ms is None else round(cold_ms * 1e3, 2)},
+                         "decode_plus_reduce_cold": None if cold_ms is None else round(cold_ms * 1e3, 2),
+                         "cold_launches": args.cold * COLD_ROUNDS if args.cold > 0 else 0},
         "roofline": roof,
         "outputs_finite": finite,
     }

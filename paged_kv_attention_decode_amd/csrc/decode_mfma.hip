@@ -56,7 +56,11 @@ struct MergeTile {
   float l[R];      // merged row sum
   float wm[R];     // the merging wave's row max
   float wl[R];     // the merging wave's row sum
-  float acc[R][D];
+  // merged P V accumulators in the MFMA output layout, lane-major: entry
+  // ((t * (D / 64) + h) * 4 + e) * 64 + lane holds the 4 rows 16 t + 4 (lane / 16)
+  // .. + 3 of value column col_of(lane % 16, h, e), so a wave merges its own
+  // accumulators with one conflict-free 16-byte LDS read and write each
+  floatx4_t acc[R * D / 4];
   // the query rows of the current range (bf16), read as score B operands; each
   // row is padded by 16 bytes so the 16 rows one read touches fall in different
   // banks
@@ -103,6 +107,8 @@ struct MfmaAttender {
 
   // value column of MFMA column j of the P V call (h, e)
   __device__ static constexpr int col_of(int jj, int h, int e) { return KV8 ? (D / 16) * jj + 4 * h + e : 4 * jj + 64 * h + e; }
+  // slot of the merged accumulators (MergeTile::acc) of tile t, call (h, e), lane
+  __device__ static constexpr int acc_slot(int t, int h, int e, int ln) { return ((t * VH + h) * 4 + e) * 64 + ln; }
 
   __device__ MfmaAttender(const DecodeParams& a_, MergeTile<R, D>& sm_)
       : a(a_),
@@ -128,7 +134,12 @@ struct MfmaAttender {
   __device__ float result(int r, int c, float& M, float& l) const {
     M = sm.m[r];
     l = sm.l[r];
-    return l > 0.0f ? sm.acc[r][c] * out_scale / l : 0.0f;
+    // the MFMA column (jj, h, e) holding value column c: the inverse of col_of
+    const int jj = KV8 ? c / (D / 16) : (c & 63) >> 2;
+    const int h = KV8 ? (c % (D / 16)) >> 2 : c >> 6;
+    const int e = c & 3;
+    const float x = sm.acc[acc_slot(r >> 4, h, e, 16 * ((r >> 2) & 3) + jj)][r & 3];
+    return l > 0.0f ? x * out_scale / l : 0.0f;
   }
 
   __device__ void run(int b, int g, int L, int lo, int hi) {
@@ -474,25 +485,25 @@ struct MfmaAttender {
         wave_lds_sync();
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
+          // rescaling factors of this lane's 4 rows 16 t + 4 grp + v
+          floatx4_t f_old = {0.0f, 0.0f, 0.0f, 0.0f}, f_new = {1.0f, 1.0f, 1.0f, 1.0f};
+          if (u > 0) {
 #pragma unroll
-          for (int v = 0; v < 4; ++v) {
-            const int r = 16 * t + 4 * grp + v;
-            const float mw = sm.wm[r];
-            float f_old = 0.0f, f_new = 1.0f;
-            if (u > 0) {
-              const float mo = sm.m[r];
+            for (int v = 0; v < 4; ++v) {
+              const int r = 16 * t + 4 * grp + v;
+              const float mo = sm.m[r], mw = sm.wm[r];
               const float M = fmaxf(mo, mw);
-              f_old = M == kNegInf ? 0.0f : fast_exp2(mo - M);
-              f_new = M == kNegInf ? 0.0f : fast_exp2(mw - M);
+              f_old[v] = M == kNegInf ? 0.0f : fast_exp2(mo - M);
+              f_new[v] = M == kNegInf ? 0.0f : fast_exp2(mw - M);
             }
-#pragma unroll
-            for (int h = 0; h < VH; ++h)
-#pragma unroll
-              for (int e = 0; e < 4; ++e) {
-                float& dst = sm.acc[r][col_of(j, h, e)];
-                dst = (u > 0 ? dst * f_old : 0.0f) + acc[t][h][e][v] * f_new;
-              }
           }
+#pragma unroll
+          for (int h = 0; h < VH; ++h)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              floatx4_t& dst = sm.acc[acc_slot(t, h, e, lane)];
+              dst = (u > 0 ? dst * f_old : (floatx4_t){0.0f, 0.0f, 0.0f, 0.0f}) + acc[t][h][e] * f_new;
+            }
         }
         wave_lds_sync();
         if (grp == 0) {

@@ -79,18 +79,28 @@ def trace(args):
         out.append(f"| `{short(s['Name'])}` | {s['Calls']} | {float(s['AverageNs']) / 1e3:.2f} | "
                    f"{float(s['MinNs']) / 1e3:.2f} | {float(s['MaxNs']) / 1e3:.2f} | {float(s['Percentage']):.1f}% |")
     out.append("")
+    # bench.py's launches, in order: the settle steps (the GPU leaving its idle clocks), the
+    # warm-up steps, the timed passes, then the cold launches (each after a 512 MiB read):
+    # warm figures are taken over the launches after the settle and warm-up, cold ones over
+    # the cold launches
+    skip = int(bench.get("settle_steps", 0)) + int(bench.get("warmup", 0)) if bench else 0
+    n_cold = int((bench or {}).get("breakdown_us", {}).get("cold_launches", args.cold)) if args.cold else 0
     total_avg = 0.0
+    total_cold = 0.0
     for k in main + red:
         d = per[k]
-        avg = statistics.fmean(d)
+        warm = d[skip:len(d) - n_cold] or d
+        avg = statistics.fmean(warm)
         total_avg += avg
-        out.append(f"`{short(k)}`: {len(d)} launches, average {avg:.2f} us, median {statistics.median(d):.2f} us.")
-        if args.cold and not is_reduce(k):
-            cold = d[-args.cold:]
-            warm = d[:-args.cold]
-            out.append(f"  The last {args.cold} launches are bench.py's cold launches (each after a 1 GiB read): "
-                       f"average {statistics.fmean(cold):.2f} us; the others (warm) average "
-                       f"{statistics.fmean(warm):.2f} us.")
+        out.append(f"`{short(k)}`: {len(d)} launches; after the {skip} settle and warm-up steps and before the "
+                   f"{n_cold} cold launches, {len(warm)} warm launches: average {avg:.2f} us, median "
+                   f"{statistics.median(warm):.2f} us.")
+        if n_cold:
+            cold = d[-n_cold:]
+            total_cold += statistics.fmean(cold)
+            if not is_reduce(k):
+                out.append(f"  The last {n_cold} launches are bench.py's cold launches (each after a 512 MiB read): "
+                           f"average {statistics.fmean(cold):.2f} us, median {statistics.median(cold):.2f} us.")
     if bench is not None:
         r = bench.get("roofline", {})
         out.append("")
@@ -101,8 +111,8 @@ def trace(args):
         if r.get("unit") == "GB/s" and main and "algorithmic_bytes_per_launch" in r:
             b = float(r["algorithmic_bytes_per_launch"])
             base = total_avg
-            if args.cold and r.get("timing", "").startswith("cold"):
-                base = statistics.fmean(per[main[0]][-args.cold:]) + sum(statistics.fmean(per[k]) for k in red)
+            if n_cold and r.get("timing", "").startswith("cold"):
+                base = total_cold
             out.append(f"Trace-based rate: {b:.0f} algorithmic bytes / {base:.2f} us = {b / base / 1e3:.1f} GB/s = "
                        f"{100 * b / base / 1e3 / HBM_PEAK_GBPS:.1f}% of 8 TB/s"
                        + (" (attention kernel + pa_reduce)" if red else "") + ".")
