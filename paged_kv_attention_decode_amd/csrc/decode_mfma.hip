@@ -67,6 +67,8 @@ struct MergeTile {
   uint16_t q[R][D + 8];
   // tree verify: bit i of path[r] is set when node i is on row r's path to the root
   uint64_t path[R];
+  // tree verify: the sequence's parent array, staged so the path walks read LDS
+  int32_t par[64];
 };
 
 // fp8 (E4M3) code pair (bytes 0-1, or 2-3 when HIGH) -> bf16 pair, exact:
@@ -158,16 +160,19 @@ struct MfmaAttender {
       *reinterpret_cast<uint4*>(&sm.q[r][8 * c8]) = v;
     }
     if constexpr (TREE) {
+      // the parent array goes to LDS in one load, so that the walks below are a
+      // chain of LDS reads rather than of dependent global loads
+      for (int i = threadIdx.x; i < a.q_len; i += kThreads) sm.par[i] = a.parents[(size_t)b * a.q_len + i];
+      __syncthreads();
       // row r's path to the root: walk the parents while they point to an
       // earlier node (at most q_len - 1 steps)
       for (int r = threadIdx.x; r < R; r += kThreads) {
         uint64_t m = 0;
         if (r < rows) {
-          const int32_t* __restrict__ par = a.parents + (size_t)b * a.q_len;
           int cur = r / a.group;
           m = 1ull << cur;
           for (int it = 0; it < 64; ++it) {
-            const int pp = par[cur];
+            const int pp = sm.par[cur];
             if (pp < 0 || pp >= cur) break;
             m |= 1ull << pp;
             cur = pp;
