@@ -123,6 +123,14 @@ struct MfmaAttender {
   __device__ void store(size_t idx, float x) {
     static_cast<uint16_t*>(a.out)[idx] = (uint16_t)f32_to_bf16_bits(x);
   }
+  // result() of columns c0 .. c0 + 7 of row r
+  __device__ void result8(int r, int c0, float (&x)[8]) const {
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      float M, l;
+      x[k] = result(r, c0 + k, M, l);
+    }
+  }
   // out[idx .. idx + 7] = x, one 16-byte store (idx a multiple of 8)
   __device__ void store8(size_t idx, const float (&x)[8]) {
     uint4 v;

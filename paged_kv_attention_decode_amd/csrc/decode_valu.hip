@@ -100,7 +100,7 @@ template <typename T, int D, int R, int NW>
 struct WaveTotals {
   float m[NW][R];
   float l[NW][R];
-  float acc[NW][R][D];
+  alignas(16) float acc[NW][R][D];
 };
 
 template <typename T, int D, int R, int NW, int NBUF>
@@ -170,6 +170,31 @@ struct ValuAttender {
       }
     }
     return l > 0.0f ? o / l : 0.0f;
+  }
+
+  // result() of columns c0 .. c0 + 7 of row r (c0 a multiple of 8): the row's
+  // maximum and rescaling factors once, each wave's 8 columns in two 16-byte
+  // reads, the same sums in the same order
+  __device__ void result8(int r, int c0, float (&x)[8]) const {
+    float M = sm.m[0][r];
+#pragma unroll
+    for (int u = 1; u < NW; ++u) M = fmaxf(M, sm.m[u][r]);
+    float l = 0.0f;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) x[k] = 0.0f;
+    if (M != kNegInf) {
+#pragma unroll
+      for (int u = 0; u < NW; ++u) {
+        const float f = fast_exp2(sm.m[u][r] - M);
+        l += f * sm.l[u][r];
+        const float4 a0 = *reinterpret_cast<const float4*>(&sm.acc[u][r][c0]);
+        const float4 a1 = *reinterpret_cast<const float4*>(&sm.acc[u][r][c0 + 4]);
+        x[0] += f * a0.x; x[1] += f * a0.y; x[2] += f * a0.z; x[3] += f * a0.w;
+        x[4] += f * a1.x; x[5] += f * a1.y; x[6] += f * a1.z; x[7] += f * a1.w;
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < 8; ++k) x[k] = l > 0.0f ? x[k] / l : 0.0f;
   }
 
   __device__ void run(int b, int g, int L, int lo, int hi) {

@@ -7,6 +7,8 @@
 //                                                   // all threads; ends with a barrier
 //   float result(int r, int c, float& M, float& l);  // merged row r, column c: the normalized
 //                                                   // output, its max M (log2 units) and sum l
+//   void  result8(int r, int c0, float (&x)[8]);     // result() of columns c0 .. c0 + 7
+//   void  store8(size_t idx, const float (&x)[8]);   // out[idx .. idx + 7] = x
 //   void  store(size_t idx, float x);                // out[idx] = x in the output type
 //
 // Modes:
@@ -64,11 +66,7 @@ __device__ void write_final(const DecodeParams& a, Attn& at, int b, int g) {
   for (int idx = threadIdx.x; idx < rows * CV; idx += Attn::kThreads) {
     const int r = idx / CV, c0 = 8 * (idx % CV);
     float x[8];
-#pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      float M, l;
-      x[k] = at.result(r, c0 + k, M, l);
-    }
+    at.result8(r, c0, x);
     at.store8(out_row(a, b, g, r) * Attn::kD + c0, x);
   }
 }
