@@ -100,6 +100,9 @@ struct MfmaAttender {
   static constexpr int KS = D / 32;  // score k-steps
   static constexpr int VH = D / 64;  // value column halves
   static constexpr int KL = KV8 ? KS / 2 : KS;  // K loads (16 bytes) per block
+  // the query rows go through LDS unless one tile's fit in registers (tree
+  // verify stages them anyway: its path masks need the same barrier)
+  static constexpr bool kStageQ = NT > 1 || TREE;
   static_assert(D == 64 || D == 128, "head_dim 64 or 128");
 
   const DecodeParams& a;
@@ -155,10 +158,12 @@ struct MfmaAttender {
   __device__ void run(int b, int g, int L, int lo, int hi) {
     const int rows = a.group * a.q_len;
 
-    // The query rows go to LDS, not registers (three tiles would hold 48 VGPRs
-    // for the whole range): the score MFMA of tile t, step ks reads its B
-    // operand, row 16 t + j, dims 32 ks + 8 grp .. + 7, from there.
+    // With more than one tile the query rows go to LDS, not registers (three
+    // tiles would hold 48 VGPRs for the whole range): the score MFMA of tile t,
+    // step ks reads its B operand, row 16 t + j, dims 32 ks + 8 grp .. + 7, from
+    // there.  One tile's rows are loaded straight into registers below.
     const uint16_t* __restrict__ qp = static_cast<const uint16_t*>(a.q);
+    if constexpr (kStageQ)
     for (int idx = threadIdx.x; idx < R * (D / 8); idx += kThreads) {
       const int r = idx / (D / 8), c8 = idx % (D / 8);
       uint4 v = make_uint4(0, 0, 0, 0);
@@ -189,7 +194,7 @@ struct MfmaAttender {
         sm.path[r] = m;
       }
     }
-    __syncthreads();
+    if constexpr (kStageQ) __syncthreads();
     // causal: row 16 t + j sees positions below vis[t]; tree: the context
     // positions below vis[t] (the tree's start, 0 for padding rows) and the
     // nodes of its path (sm.path)
@@ -284,8 +289,17 @@ struct MfmaAttender {
     auto q_dim = [&](int ks) { return KV8 ? 64 * (ks / 2) + 16 * grp + 8 * (ks & 1) : 32 * ks + 8 * grp; };
     uint4 qreg[NT == 1 ? KS : 1];
     if constexpr (NT == 1) {
+      if constexpr (kStageQ) {
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) qreg[ks] = *reinterpret_cast<const uint4*>(&sm.q[j][q_dim(ks)]);
+        for (int ks = 0; ks < KS; ++ks) qreg[ks] = *reinterpret_cast<const uint4*>(&sm.q[j][q_dim(ks)]);
+      } else {
+        // row j of the tile, straight from memory (zero for padding rows); the
+        // block-table load that follows shares these loads' round trip
+        const uint16_t* qrow = qp + (((size_t)b * a.q_len + j / a.group) * a.n_h + (size_t)g * a.group + j % a.group) * D;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+          qreg[ks] = j < rows ? *reinterpret_cast<const uint4*>(qrow + q_dim(ks)) : make_uint4(0, 0, 0, 0);
+      }
     }
 
     // scores: s[t][v] = row 16 t + j against token 4 grp + v, log2 units, -inf where masked
