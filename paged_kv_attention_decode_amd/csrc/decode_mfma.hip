@@ -32,6 +32,21 @@
 // add the same rounded weights, so numerator and denominator agree.  The waves
 // of a workgroup merge one after the other into a single LDS tile.
 //
+// VLDS (bf16, four row tiles): V goes from memory straight into LDS
+// with 16-byte buffer-to-LDS loads, one ring of NBUF slots per wave, so that
+// the blocks in flight cost LDS rather than registers (four tiles' accumulators
+// leave room for one block of K and V in registers, but three of K).  Slot
+// layout: token t's D columns are 2 D contiguous bytes, their 16-byte chunks
+// XOR-swizzled by a function X(t) of the token (position chunk ^ 2 X(t)), and
+// P V's B operands come out of it through the transposing LDS read
+// ds_read_b64_tr_b16: within each 16-lane group, output lane 4 b + k takes
+// element k of the 8 bytes that lane 4 a + b addresses, as its element a.
+// Lane (a, b) of group grp addresses token 4 grp + a, columns 16 ct + 4 b .. + 3,
+// so output lane j holds tokens 4 grp .. + 3 of column 16 ct + j: MFMA column j
+// of call (h, e) is value column 64 h + 16 e + j, with no permutes.  The ring
+// shares LDS with the merge tile's accumulators, which are written only after
+// the block loop.
+//
 // TREE: the q_len new tokens are the nodes of a draft tree checked in one pass
 // ("Chapter 18: Speculative Decoding and Serving Optimizations", arunshar.com,
 // section 18.1.2, tree-based verification for Medusa; "07 - Inference",
@@ -50,17 +65,23 @@ namespace {
 
 constexpr int kWaves = 4;
 constexpr float kOverflowSlack = 64.0f;  // log2 units
-template <int R, int D>
-struct MergeTile {
+template <int R, int D, int RING = 0>
+struct alignas(1024) MergeTile {
+  // VLDS: the per-wave rings of staged V blocks (RING bytes), in the same
+  // bytes as the accumulators below, which are written only after the block
+  // loop; 1 KiB aligned, so each slot's swizzle sees whole 256-byte bank rows
+  union {
+    uint8_t vring[RING > 0 ? RING : 16];
+    // merged P V accumulators in the MFMA output layout, lane-major: entry
+    // ((t * (D / 64) + h) * 4 + e) * 64 + lane holds the 4 rows 16 t + 4 (lane / 16)
+    // .. + 3 of value column col_of(lane % 16, h, e), so a wave merges its own
+    // accumulators with one conflict-free 16-byte LDS read and write each
+    floatx4_t acc[R * D / 4];
+  };
   float m[R];      // merged row max (log2 units)
   float l[R];      // merged row sum
   float wm[R];     // the merging wave's row max
   float wl[R];     // the merging wave's row sum
-  // merged P V accumulators in the MFMA output layout, lane-major: entry
-  // ((t * (D / 64) + h) * 4 + e) * 64 + lane holds the 4 rows 16 t + 4 (lane / 16)
-  // .. + 3 of value column col_of(lane % 16, h, e), so a wave merges its own
-  // accumulators with one conflict-free 16-byte LDS read and write each
-  floatx4_t acc[R * D / 4];
   // the query rows of the current range (bf16), read as score B operands; each
   // row is padded by 16 bytes so the 16 rows one read touches fall in different
   // banks
@@ -70,6 +91,90 @@ struct MergeTile {
   // tree verify: the sequence's parent array, staged so the path walks read LDS
   int32_t par[64];
 };
+
+typedef __attribute__((address_space(3))) void* lds_void_t;
+
+// VLDS: N transposing LDS reads (8 bytes each) at the given LDS byte
+// addresses.  In asm, so that the compiler, which cannot tell which LDS bytes
+// the buffer-to-LDS loads in flight will write, does not first wait for all of
+// them: the caller waits for the loads of the slot it reads, and the reads
+// complete inside the block (lgkmcnt(0)) before that slot is loaded again.
+template <int N>
+__device__ __forceinline__ void read_v_tr(uint2 (&vt)[N], const uint32_t (&ad)[N]);
+template <>
+__device__ __forceinline__ void read_v_tr<8>(uint2 (&vt)[8], const uint32_t (&ad)[8]) {
+  asm volatile(
+      "ds_read_b64_tr_b16 %0, %8\n"
+      "ds_read_b64_tr_b16 %1, %9\n"
+      "ds_read_b64_tr_b16 %2, %10\n"
+      "ds_read_b64_tr_b16 %3, %11\n"
+      "ds_read_b64_tr_b16 %4, %12\n"
+      "ds_read_b64_tr_b16 %5, %13\n"
+      "ds_read_b64_tr_b16 %6, %14\n"
+      "ds_read_b64_tr_b16 %7, %15\n"
+      "s_waitcnt lgkmcnt(0)"
+      : "=v"(vt[0]), "=v"(vt[1]), "=v"(vt[2]), "=v"(vt[3]), "=v"(vt[4]), "=v"(vt[5]), "=v"(vt[6]), "=v"(vt[7])
+      : "v"(ad[0]), "v"(ad[1]), "v"(ad[2]), "v"(ad[3]), "v"(ad[4]), "v"(ad[5]), "v"(ad[6]), "v"(ad[7])
+      : "memory");
+}
+template <>
+__device__ __forceinline__ void read_v_tr<4>(uint2 (&vt)[4], const uint32_t (&ad)[4]) {
+  asm volatile(
+      "ds_read_b64_tr_b16 %0, %4\n"
+      "ds_read_b64_tr_b16 %1, %5\n"
+      "ds_read_b64_tr_b16 %2, %6\n"
+      "ds_read_b64_tr_b16 %3, %7\n"
+      "s_waitcnt lgkmcnt(0)"
+      : "=v"(vt[0]), "=v"(vt[1]), "=v"(vt[2]), "=v"(vt[3])
+      : "v"(ad[0]), "v"(ad[1]), "v"(ad[2]), "v"(ad[3])
+      : "memory");
+}
+
+// VLDS: the other LDS reads of the block loop, in asm for the same reason:
+// the query operands of one tile (N 16-byte reads 64 bytes apart) and a row's
+// tree path mask
+template <int N>
+__device__ __forceinline__ void read_q(uint4 (&q)[N], uint32_t ad);
+template <>
+__device__ __forceinline__ void read_q<4>(uint4 (&q)[4], uint32_t ad) {
+  asm volatile(
+      "ds_read_b128 %0, %4\n"
+      "ds_read_b128 %1, %4 offset:64\n"
+      "ds_read_b128 %2, %4 offset:128\n"
+      "ds_read_b128 %3, %4 offset:192\n"
+      "s_waitcnt lgkmcnt(0)"
+      : "=v"(q[0]), "=v"(q[1]), "=v"(q[2]), "=v"(q[3])
+      : "v"(ad)
+      : "memory");
+}
+template <>
+__device__ __forceinline__ void read_q<2>(uint4 (&q)[2], uint32_t ad) {
+  asm volatile(
+      "ds_read_b128 %0, %2\n"
+      "ds_read_b128 %1, %2 offset:64\n"
+      "s_waitcnt lgkmcnt(0)"
+      : "=v"(q[0]), "=v"(q[1])
+      : "v"(ad)
+      : "memory");
+}
+__device__ __forceinline__ uint64_t read_u64(uint32_t ad) {
+  uint64_t x;
+  asm volatile(
+      "ds_read_b64 %0, %1\n"
+      "s_waitcnt lgkmcnt(0)"
+      : "=v"(x)
+      : "v"(ad)
+      : "memory");
+  return x;
+}
+__device__ __forceinline__ uint32_t lds_addr(const void* p) { return (uint32_t)(size_t)(lds_void_t)(void*)p; }
+
+// s_waitcnt vmcnt(n), other counters left alone (n < 64)
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
+}
 
 // fp8 (E4M3) code pair (bytes 0-1, or 2-3 when HIGH) -> bf16 pair, exact:
 // every E4M3 value is a bf16 value
@@ -90,7 +195,7 @@ __device__ __forceinline__ uint32_t fp8x2_to_bf16x2(uint32_t codes) {
 //       pairs of the P V B operand.
 // The K scale of the head multiplies the score scale and the V scale the
 // normalized output, exact refactorings of scale * q . (s_k k) and sum p (s_v v).
-template <int D, int NT, int NW, int NBUF, bool KV8, bool TREE>
+template <int D, int NT, int NW, int NBUF, bool KV8, bool TREE, bool VLDS>
 struct MfmaAttender {
   static constexpr int kThreads = NW * 64;
   // the new tokens of pa_decode_append are stored by the schedule before run
@@ -104,18 +209,30 @@ struct MfmaAttender {
   // verify stages them anyway: its path masks need the same barrier)
   static constexpr bool kStageQ = NT > 1 || TREE;
   static_assert(D == 64 || D == 128, "head_dim 64 or 128");
+  static_assert(!VLDS || (!KV8 && NT > 1), "staged V: bf16, two or more tiles (used with four)");
+  // VLDS: bytes of one staged V block, its 16-byte buffer-to-LDS loads (1 KiB
+  // per wave each), and the vector memory instructions one block issues
+  static constexpr int kVBytes = 16 * D * 2;
+  static constexpr int kVLoads = kVBytes / 1024;
+  static constexpr int kRing = VLDS ? NW * NBUF * kVBytes : 0;
+  static constexpr int kBlockVmem = KL + (VLDS ? kVLoads : 4 * VH);
+  // swizzle of token t's chunks: with 32 lanes reading 8 tokens at one
+  // column tile, every chunk pair lands in its own banks
+  __device__ static constexpr int swz(int t) { return D == 128 ? (t & 7) : ((t >> 1) & 3); }
 
   const DecodeParams& a;
-  MergeTile<R, D>& sm;
+  MergeTile<R, D, kRing>& sm;
   const int lane, w, j, grp;
   float out_scale = 1.0f;  // V scale of the current head (fp8 caches)
 
   // value column of MFMA column j of the P V call (h, e)
-  __device__ static constexpr int col_of(int jj, int h, int e) { return KV8 ? (D / 16) * jj + 4 * h + e : 4 * jj + 64 * h + e; }
+  __device__ static constexpr int col_of(int jj, int h, int e) {
+    return KV8 ? (D / 16) * jj + 4 * h + e : (VLDS ? 64 * h + 16 * e + jj : 4 * jj + 64 * h + e);
+  }
   // slot of the merged accumulators (MergeTile::acc) of tile t, call (h, e), lane
   __device__ static constexpr int acc_slot(int t, int h, int e, int ln) { return ((t * VH + h) * 4 + e) * 64 + ln; }
 
-  __device__ MfmaAttender(const DecodeParams& a_, MergeTile<R, D>& sm_)
+  __device__ MfmaAttender(const DecodeParams& a_, MergeTile<R, D, kRing>& sm_)
       : a(a_),
         sm(sm_),
         lane(threadIdx.x & 63),
@@ -148,9 +265,9 @@ struct MfmaAttender {
     M = sm.m[r];
     l = sm.l[r];
     // the MFMA column (jj, h, e) holding value column c: the inverse of col_of
-    const int jj = KV8 ? c / (D / 16) : (c & 63) >> 2;
+    const int jj = KV8 ? c / (D / 16) : (VLDS ? c & 15 : (c & 63) >> 2);
     const int h = KV8 ? (c % (D / 16)) >> 2 : c >> 6;
-    const int e = c & 3;
+    const int e = VLDS ? (c >> 4) & 3 : c & 3;
     const float x = sm.acc[acc_slot(r >> 4, h, e, 16 * ((r >> 2) & 3) + jj)][r & 3];
     return l > 0.0f ? x * out_scale / l : 0.0f;
   }
@@ -229,6 +346,23 @@ struct MfmaAttender {
     const uint32_t head_off = (uint32_t)g * D * esz;
     const uint32_t k_off = (uint32_t)j * tok_bytes + head_off + (uint32_t)grp * 16;
     const uint32_t v_off = (uint32_t)(4 * grp) * tok_bytes + head_off + (uint32_t)j * (KV8 ? D / 16 : 8);
+    // VLDS: the LDS byte address lane (a, b) of group grp reads for column tile
+    // 0 of slot 0 of this wave's ring (token 4 grp + a, columns 4 b .. + 3; tile
+    // ct flips the swizzle bits by 32 ct), and the source offsets of the wave's
+    // loads into a slot (instruction i fills slot bytes 1024 i + 16 lane)
+    uint32_t vrd = 0;
+    uint32_t vld[VLDS ? kVLoads : 1];
+    if constexpr (VLDS) {
+      const int ta = 4 * grp + ((lane >> 2) & 3), b4 = lane & 3;
+      const uint32_t ring = (uint32_t)(size_t)(lds_void_t)(void*)(sm.vring + w * NBUF * kVBytes);
+      vrd = ring + (uint32_t)(ta * (2 * D) + 16 * (b4 >> 1) + 8 * (b4 & 1) + 32 * swz(ta));
+#pragma unroll
+      for (int i = 0; i < kVLoads; ++i) {
+        const int pos = 1024 * i + 16 * lane;
+        const int t = pos / (2 * D), c = ((pos % (2 * D)) >> 4) ^ (2 * swz(t));
+        vld[i] = (uint32_t)t * tok_bytes + head_off + 16u * (uint32_t)c;
+      }
+    }
     const char* kbase = static_cast<const char*>(a.k_cache);
     const char* vbase = static_cast<const char*>(a.v_cache);
     const int32_t* __restrict__ table = a.tables + (size_t)b * a.max_blocks;
@@ -240,7 +374,8 @@ struct MfmaAttender {
 
     // K: KL loads of 16 bytes; V: 4 tokens x VH halves of 8 bytes (bf16), or
     // 4 tokens x D/16 bytes (fp8, in vb[v][0])
-    auto issue = [&](int ids, int cnt, int k0, int kk, uint4(&kb)[KL], uint2(&vb)[4][VH], int& lblk, bool& ok) {
+    auto issue = [&](int ids, int cnt, int k0, int kk, uint4(&kb)[KL], uint2(&vb)[4][VH], int& lblk, bool& ok,
+                     int su) {
       const int phys = __builtin_amdgcn_readlane(ids, kk < cnt ? kk : 0);
       ok = kk < cnt && (unsigned)phys < (unsigned)a.num_blocks;
       lblk = lo + w + NW * (k0 + kk);
@@ -254,7 +389,13 @@ struct MfmaAttender {
 #pragma unroll
       for (int kl = 0; kl < KL; ++kl)
         kb[kl] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(kr, k_off + 64 * kl, 0, 0));
-      if constexpr (KV8) {
+      if constexpr (VLDS) {
+        // V into slot su of this wave's ring
+        char* slot = reinterpret_cast<char*>(sm.vring) + (w * NBUF + su) * kVBytes;
+#pragma unroll
+        for (int i = 0; i < kVLoads; ++i)
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(vr, (lds_void_t)(slot + 1024 * i), 16, (int)vld[i], 0, 0, 0);
+      } else if constexpr (KV8) {
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
           if constexpr (D == 128)
@@ -311,10 +452,13 @@ struct MfmaAttender {
       // raw q.k of tile t
       auto tile = [&](int t) -> floatx4_t {
         floatx4_t x = {0.0f, 0.0f, 0.0f, 0.0f};
+        uint4 qv[VLDS ? KS : 1];
+        if constexpr (VLDS) read_q<KS>(qv, lds_addr(&sm.q[16 * t + j][q_dim(0)]));
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
           uint4 qb;
           if constexpr (NT == 1) qb = qreg[ks];
+          else if constexpr (VLDS) qb = qv[ks];
           else qb = *reinterpret_cast<const uint4*>(&sm.q[16 * t + j][q_dim(ks)]);
           x = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, k_operand(kb, ks)),
                                                       __builtin_bit_cast(bf16x8_t, qb), x, 0, 0, 0);
@@ -336,7 +480,7 @@ struct MfmaAttender {
         } else {
 #pragma unroll
           for (int t = 0; t < NT; ++t) {
-            const uint64_t path = sm.path[16 * t + j];
+            const uint64_t path = VLDS ? read_u64(lds_addr(&sm.path[16 * t + j])) : sm.path[16 * t + j];
 #pragma unroll
             for (int v = 0; v < 4; ++v) {
               const int rel = pos0 + v - tree_base;  // node index of the position, negative before the tree
@@ -356,9 +500,19 @@ struct MfmaAttender {
       }
     };
 
-    auto accumulate = [&](const floatx4_t(&s)[NT], const uint2(&vb)[4][VH]) {
-      // B operands of P V: column 4 j + 64 h + e of the 4 tokens, bf16 pairs (tokens 0,1), (2,3)
+    // (VLDS: the caller has waited for the loads of slot su)
+    auto accumulate = [&](const floatx4_t(&s)[NT], const uint2(&vb)[4][VH], int su) {
+      // B operands of P V: column col_of(j, h, e) of the 4 tokens, bf16 pairs (tokens 0,1), (2,3)
       uint2 vt[VH][4];
+      if constexpr (VLDS) {
+        uint32_t ad[4 * VH];
+        uint2 vr[4 * VH];
+#pragma unroll
+        for (int ct = 0; ct < 4 * VH; ++ct) ad[ct] = (vrd ^ (32u * ct)) + (uint32_t)(su * kVBytes);
+        read_v_tr<4 * VH>(vr, ad);
+#pragma unroll
+        for (int ct = 0; ct < 4 * VH; ++ct) vt[ct >> 2][ct & 3] = vr[ct];
+      } else
 #pragma unroll
       for (int h = 0; h < VH; ++h) {
 #pragma unroll
@@ -418,7 +572,7 @@ struct MfmaAttender {
       int lb[NBUF];
       bool okb[NBUF];
 #pragma unroll
-      for (int u = 0; u < NBUF; ++u) issue(ids, cnt, k0, u, kb[u], vb[u], lb[u], okb[u]);
+      for (int u = 0; u < NBUF; ++u) issue(ids, cnt, k0, u, kb[u], vb[u], lb[u], okb[u], u);
       if (k0 == 0) {
         floatx4_t s0[NT];
         scores(kb[0], lb[0], okb[0], s0);
@@ -436,9 +590,11 @@ struct MfmaAttender {
 #pragma unroll
               for (int v = 0; v < 4; ++v) big |= s[t][v] > m_ref[t] + kOverflowSlack;
             overflow |= __builtin_amdgcn_ballot_w64(big) != 0;
-            accumulate(s, vb[u]);
+            // the loads of the NBUF - 1 blocks after this one may still be in flight
+            if constexpr (VLDS) wait_vmcnt<(NBUF - 1) * kBlockVmem>();
+            accumulate(s, vb[u], u);
           }
-          issue(ids, cnt, k0, kk + u + NBUF, kb[u], vb[u], lb[u], okb[u]);
+          issue(ids, cnt, k0, kk + u + NBUF, kb[u], vb[u], lb[u], okb[u], u);
         }
       }
     }
@@ -463,7 +619,7 @@ struct MfmaAttender {
           uint2 vb1[4][VH];
           int lb1;
           bool ok1;
-          issue(ids, cnt, k0, kk, kb1, vb1, lb1, ok1);
+          issue(ids, cnt, k0, kk, kb1, vb1, lb1, ok1, 0);
           floatx4_t s[NT];
           scores(kb1, lb1, ok1, s);
 #pragma unroll
@@ -481,10 +637,11 @@ struct MfmaAttender {
           uint2 vb1[4][VH];
           int lb1;
           bool ok1;
-          issue(ids, cnt, k0, kk, kb1, vb1, lb1, ok1);
+          issue(ids, cnt, k0, kk, kb1, vb1, lb1, ok1, 0);
           floatx4_t s[NT];
           scores(kb1, lb1, ok1, s);
-          accumulate(s, vb1);
+          if constexpr (VLDS) wait_vmcnt<0>();
+          accumulate(s, vb1, 0);
         }
       }
     }
@@ -498,7 +655,9 @@ struct MfmaAttender {
       lsum[t] = x;
     }
 
-    // merge the waves one after the other into the LDS tile
+    // merge the waves one after the other into the LDS tile (VLDS: no load into
+    // this wave's ring, which holds the tile's bytes, is still in flight)
+    if constexpr (VLDS) wait_vmcnt<0>();
     __syncthreads();  // the previous range's tile has been read
     for (int u = 0; u < NW; ++u) {
       if (w == u) {
@@ -556,41 +715,48 @@ struct MfmaAttender {
   }
 };
 
-template <int D, int NT, int NW, int NBUF, bool BALANCED, bool KV8, bool TREE>
+template <int D, int NT, int NW, int NBUF, bool BALANCED, bool KV8, bool TREE, bool VLDS>
 // Up to three row tiles the kernel is asked for two waves per SIMD: without
 // the bound the allocator keeps values hoisted out of a balanced range's loop
 // over sequences and lands at one wave per SIMD, while with it everything fits
 // without spilling.  Four tiles fit two waves too with one block in flight in
 // the fixed schedules; the balanced one would spill, so it keeps one wave.
 __global__ __launch_bounds__(NW * 64, (NT <= 3 || !BALANCED) ? 2 : 1) void decode_mfma_kernel(DecodeParams a) {
-  __shared__ MergeTile<16 * NT, D> sm;
-  MfmaAttender<D, NT, NW, NBUF, KV8, TREE> at(a, sm);
+  using Attn = MfmaAttender<D, NT, NW, NBUF, KV8, TREE, VLDS>;
+  __shared__ MergeTile<16 * NT, D, Attn::kRing> sm;
+  Attn at(a, sm);
   if constexpr (BALANCED) drive_balanced(a, at);
   else drive_fixed(a, at);
 }
 
 template <int D, int NT, bool KV8, bool TREE>
 hipError_t launch_tiles(const DecodeParams& p, hipStream_t s) {
-  constexpr int NB = NT >= 4 ? 1 : (NT >= 3 ? 2 : 3);  // blocks in flight per wave, fixed schedules
+  // Fixed schedules.  Four bf16 tiles stage V in LDS, which leaves registers
+  // for two blocks of K in flight per wave where V in registers left one (15-node
+  // tree verify on the 8B shape: 226.9 against 232.2 us).  Fewer tiles keep V
+  // in registers: staging measured the same there (speculative verify, three
+  // tiles: 235.7-236.6 us either way).
+  constexpr bool VL = !KV8 && NT >= 4;
+  constexpr int NB = VL ? 2 : (NT >= 4 ? 1 : (NT >= 3 ? 2 : 3));  // blocks in flight per wave
   if (p.mode == kBalanced) {
     // one block in flight per wave, as in the vector-ALU kernel: cheaper
     // pipeline restarts at the sequences a range crosses (70B layer: 221 us
     // against 239 us with three)
     static const int resident =
-        resident_per_cu(decode_mfma_kernel<D, NT, kWaves, 1, true, KV8, TREE>, kWaves * 64);
+        resident_per_cu(decode_mfma_kernel<D, NT, kWaves, 1, true, KV8, TREE, false>, kWaves * 64);
     DecodeParams q = p;
     q.num_wgs = balanced_workgroups(resident, p.n_kv);
-    hipLaunchKernelGGL((decode_mfma_kernel<D, NT, kWaves, 1, true, KV8, TREE>), dim3(q.num_wgs), dim3(kWaves * 64),
+    hipLaunchKernelGGL((decode_mfma_kernel<D, NT, kWaves, 1, true, KV8, TREE, false>), dim3(q.num_wgs), dim3(kWaves * 64),
                        0, s, q);
   } else {
     DecodeParams q = p;
     if (p.mode == kSinglePass) {
       static const int resident =
-          resident_per_cu(decode_mfma_kernel<D, NT, kWaves, NB, false, KV8, TREE>, kWaves * 64);
+          resident_per_cu(decode_mfma_kernel<D, NT, kWaves, NB, false, KV8, TREE, VL>, kWaves * 64);
       q.pair_stride = one_pass_pairing(resident, p.num_seqs, p.n_kv);
     }
     dim3 grid(p.mode == kPartitions ? p.num_parts : 1, p.n_kv, p.num_seqs);
-    hipLaunchKernelGGL((decode_mfma_kernel<D, NT, kWaves, NB, false, KV8, TREE>), grid, dim3(kWaves * 64), 0, s, q);
+    hipLaunchKernelGGL((decode_mfma_kernel<D, NT, kWaves, NB, false, KV8, TREE, VL>), grid, dim3(kWaves * 64), 0, s, q);
   }
   return hipGetLastError();
 }

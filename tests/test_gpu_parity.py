@@ -329,11 +329,12 @@ def test_identical_keys_count_probe_bf16(G, q_len, lens, parts):
 
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("dtype,q_len,n_h", [("f32", 1, 2), ("f32", 2, 2), ("bf16", 1, 2), ("bf16", 2, 2),
-                                             ("bf16", 5, 2), ("bf16", 5, 8)])
+                                             ("bf16", 5, 2), ("bf16", 5, 8), ("bf16", 8, 8)])
 def test_scores_rising_far_past_the_first_block(dtype, q_len, n_h, d):
     """Scores grow by ~0.1 per position (scale 1/8 at both head sizes), so
     weights relative to a wave's first block exceed 2^64 and every kernel
-    variant (vector ALU and matrix core, d 64 and 128) must take its exact
+    variant (vector ALU and matrix core up to four row tiles, the last with V
+    staged in LDS, d 64 and 128) must take its exact
     two-pass path, in each schedule."""
     spec = wl.Spec(name="ramp", dtype=dtype, num_seqs=3, num_q_heads=n_h, num_kv_heads=1, head_dim=d,
                    lens=("fixed", (1000, 700, 40)), max_len=1024, q_len=q_len, seed=31, scale=0.125)
