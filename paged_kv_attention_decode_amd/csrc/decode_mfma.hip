@@ -83,9 +83,11 @@ struct alignas(1024) MergeTile {
   float wm[R];     // the merging wave's row max
   float wl[R];     // the merging wave's row sum
   // the query rows of the current range (bf16), read as score B operands; each
-  // row is padded by 16 bytes so the 16 rows one read touches fall in different
-  // banks
-  uint16_t q[R][D + 8];
+  // row is padded by 32 bytes: at 288 bytes (72 dwords, 8 banks past a multiple
+  // of 64) the rows one read touches fall in different banks (16-byte padding
+  // left 0.85 bank-conflict cycles per active LDS cycle on three tiles, this
+  // 0.05)
+  uint16_t q[R][D + 16];
   // tree verify: bit i of path[r] is set when node i is on row r's path to the root
   uint64_t path[R];
   // tree verify: the sequence's parent array, staged so the path walks read LDS
