@@ -721,8 +721,9 @@ template <int D, int NT, int NW, int NBUF, bool BALANCED, bool KV8, bool TREE, b
 // Up to three row tiles the kernel is asked for two waves per SIMD: without
 // the bound the allocator keeps values hoisted out of a balanced range's loop
 // over sequences and lands at one wave per SIMD, while with it everything fits
-// without spilling.  Four tiles fit two waves too with one block in flight in
-// the fixed schedules; the balanced one would spill, so it keeps one wave.
+// without spilling.  Four tiles fit two waves too in the fixed schedules (two
+// blocks in flight, V staged in LDS); the balanced one would spill, so it keeps
+// one wave.
 __global__ __launch_bounds__(NW * 64, (NT <= 3 || !BALANCED) ? 2 : 1) void decode_mfma_kernel(DecodeParams a) {
   using Attn = MfmaAttender<D, NT, NW, NBUF, KV8, TREE, VLDS>;
   __shared__ MergeTile<16 * NT, D, Attn::kRing> sm;
