@@ -339,20 +339,25 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillParams a) {
   };
 
   // one step: its pairs of blocks, those some row of the wave sees; bit bb of okm is set
-  // where block bb of the step is valid
-  auto compute = [&](int it, int buf, int mode, uint32_t okm) {
+  // where block bb of the step is valid.  mid() runs after the first half of
+  // the pairs, in every wave, whether or not its rows see them
+  auto compute = [&](int it, int buf, int mode, uint32_t okm, auto&& mid) {
 #pragma unroll
     for (int pp = 0; pp < kStepBlocks / 2; ++pp) {
+      if (pp == kStepBlocks / 4) mid();
       const int blk0 = kStepBlocks * it + 2 * pp;
-      if (!wave_rows || blk0 * kBlockTokens >= wave_end) return;  // wave-uniform
-      pair(blk0, buf, 2 * pp, mode, okm >> (2 * pp));
+      if (wave_rows && blk0 * kBlockTokens < wave_end) pair(blk0, buf, 2 * pp, mode, okm >> (2 * pp));  // wave-uniform
     }
   };
 
   // one pass over the steps.  Global loads run kPrefetch steps ahead in
   // registers (slot it % kPrefetch holds step it); LDS holds two steps: the
   // one being multiplied and the next one.  okm[k] holds the valid-block bits
-  // of step it + k.
+  // of step it + k.  The next step goes to LDS, and the one after it is
+  // requested, halfway through a step's pairs rather than after them: its LDS
+  // buffer was last read in the previous step, which ended at a barrier, and
+  // the barrier at the end of this step publishes it (165.3-165.7 against
+  // 167.7-169.0 us on four 512-token chunks; after the first pair, no gain).
   const int nit = (nblk + kStepBlocks - 1) / kStepBlocks;
   auto sweep = [&](int mode) {
     uint4 r[kPrefetch][kStepBlocks][LOADS];
@@ -369,15 +374,17 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillParams a) {
         if (it >= nit) break;
         // table entries of the step fetched at the end of this one, loaded now
         const int tv = it + 1 + kPrefetch < nit ? table_vec(it + 1 + kPrefetch) : 0;
-        compute(it, it & 1, mode, okm[0]);
+        const int nxt = (u + 1) % kPrefetch;  // register slot of step it + 1 (constant once unrolled)
+        uint32_t okn = 0u;
+        compute(it, it & 1, mode, okm[0], [&] {
+          if (it + 1 < nit) {
+            put((it + 1) & 1, r[nxt]);
+            if (it + 1 + kPrefetch < nit) okn = fetch(it + 1 + kPrefetch, tv, r[nxt]);
+          }
+        });
 #pragma unroll
         for (int k = 0; k < kPrefetch; ++k) okm[k] = okm[k + 1];
-        okm[kPrefetch] = 0u;
-        const int nxt = (u + 1) % kPrefetch;  // register slot of step it + 1 (constant once unrolled)
-        if (it + 1 < nit) {
-          put((it + 1) & 1, r[nxt]);
-          if (it + 1 + kPrefetch < nit) okm[kPrefetch] = fetch(it + 1 + kPrefetch, tv, r[nxt]);
-        }
+        okm[kPrefetch] = okn;
         __syncthreads();  // step it + 1 staged; everyone is done with step it
       }
     }

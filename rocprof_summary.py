@@ -84,7 +84,8 @@ def trace(args):
     # warm figures are taken over the launches after the settle and warm-up, cold ones over
     # the cold launches
     skip = int(bench.get("settle_steps", 0)) + int(bench.get("warmup", 0)) if bench else 0
-    n_cold = int((bench or {}).get("breakdown_us", {}).get("cold_launches", args.cold)) if args.cold else 0
+    # (the count bench.py reports, else --cold)
+    n_cold = int((bench or {}).get("breakdown_us", {}).get("cold_launches", args.cold))
     total_avg = 0.0
     total_cold = 0.0
     for k in main + red:
@@ -241,7 +242,8 @@ def main(argv=None):
     ap.add_argument("--config", required=True)
     ap.add_argument("--bench", help="the bench.py JSON line of the traced command")
     ap.add_argument("--command", action="append", default=[])
-    ap.add_argument("--cold", type=int, default=0, help="the last N attention launches are cold launches")
+    ap.add_argument("--cold", type=int, default=0,
+                    help="the last N attention launches are cold launches, where the bench JSON does not say")
     ap.add_argument("--json", help="traffic: where to write the JSON bench.py reads")
     ap.add_argument("--calibration", action="append", default=[],
                     help="traffic: counter folders of runs with bench.py --calibrate-copy, for the scale factors")
