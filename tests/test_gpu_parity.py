@@ -156,12 +156,16 @@ INV_SPEC = wl.Spec(name="inv", dtype="bf16", num_seqs=6, num_q_heads=16, num_kv_
 
 # 40 rows per KV head (8 query heads per KV head, 5 query tokens)
 INV_SPEC_WIDE = INV_SPEC.with_(num_q_heads=32, num_kv_heads=4, q_len=5, lens=("uniform", 5, 900), seed=29)
+# 64 rows per KV head (8 query tokens): four row tiles, whose one-pass and
+# partition schedules stage V in LDS
+INV_SPEC_64 = INV_SPEC.with_(num_q_heads=32, num_kv_heads=4, q_len=8, lens=("uniform", 8, 900), seed=41)
+INV_SPECS = {"rows8": INV_SPEC, "rows40": INV_SPEC_WIDE, "rows64": INV_SPEC_64}
 
 
-@pytest.mark.parametrize("wide", [False, True], ids=["rows8", "rows40"])
+@pytest.mark.parametrize("rows", list(INV_SPECS))
 @pytest.mark.parametrize("ps", [0, 64, -1])
-def test_physical_permutation_is_bitwise_invariant(ps, wide):
-    p = wl.make_problem(INV_SPEC_WIDE if wide else INV_SPEC)
+def test_physical_permutation_is_bitwise_invariant(ps, rows):
+    p = wl.make_problem(INV_SPECS[rows])
     say(f"permutation ps={ps}")
     _, a = run(p, ps)
     _, b = run(wl.permute_physical(p, 99), ps)
@@ -190,10 +194,10 @@ def test_cache_placement_is_bitwise_invariant(ps):
     assert np.array_equal(to_host(d.k_cache), to_host(kc)) and np.array_equal(to_host(d.v_cache), to_host(vc))
 
 
-@pytest.mark.parametrize("wide", [False, True], ids=["rows8", "rows40"])
+@pytest.mark.parametrize("rows", list(INV_SPECS))
 @pytest.mark.parametrize("ps", [0, 64])
-def test_repeatable_and_batch_independent(ps, wide):
-    p = wl.make_problem(INV_SPEC_WIDE if wide else INV_SPEC)
+def test_repeatable_and_batch_independent(ps, rows):
+    p = wl.make_problem(INV_SPECS[rows])
     ql = p.q_len
     say(f"repeat / batch ps={ps} rows={p.spec.group * ql}")
     d = DeviceProblem(p)
@@ -209,9 +213,9 @@ def test_repeatable_and_batch_independent(ps, wide):
     assert np.array_equal(widen(o1[b * ql:(b + 1) * ql], "bf16"), alone)
 
 
-@pytest.mark.parametrize("wide", [False, True], ids=["rows8", "rows40"])
-def test_unread_rows_poisoned_and_garbage_padding(wide):
-    spec = INV_SPEC_WIDE if wide else INV_SPEC
+@pytest.mark.parametrize("rows", list(INV_SPECS))
+def test_unread_rows_poisoned_and_garbage_padding(rows):
+    spec = INV_SPECS[rows]
     clean = wl.make_problem(spec)
     dirty = wl.make_problem(spec.with_(poison=True, pad="garbage"))
     for ps in (0, 64, -1):
