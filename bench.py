@@ -20,7 +20,9 @@ Prints one JSON line:
                  against the 8 TB/s HBM peak; traffic from the committed counter
                  summary.  Where the working set is under twice the 256 MB MALL
                  (the fp8 layer), warm launches are partly served from the MALL,
-                 so the figure is taken over cold launches instead.
+                 so the figure is taken over cold launches instead.  Shared
+                 prefix blocks count once; achieved_logical / frac_logical
+                 count every sequence's context in full.
   roofline_cold  (roofline_warm) the same figure over the other kind of launch:
                  cold launches each follow a 512 MiB read; their time is that of
                  N (read, launch) pairs less that of N reads, one event pair each
@@ -548,6 +550,13 @@ def main(argv=None):
                 else f"warm launches: {K} back to back, one event pair around them",
                 "algorithmic_bytes_per_launch": kv_bytes,
                 "avg_launch_us": round(basis_s * 1e6, 2)}
+        if ab["kv_logical"] != ab["kv_unique"]:
+            # shared prefix blocks: the headline counts them once; every sequence's
+            # context read in full, as the kernel streams it, is reported beside it
+            logical = (ab["kv_logical"] + ab["q"]) / basis_s / 1e9
+            roof["achieved_logical"] = round(logical, 1)
+            roof["frac_logical"] = round(logical / HBM_PEAK_GBPS, 4)
+            roof["logical_bytes_per_launch"] = ab["kv_logical"] + ab["q"]
         if not cold_basis:
             roof["launch_us_percentiles"] = spread_us
             roof["avg_launch_us_event_pair_each"] = single_pair_us
