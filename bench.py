@@ -54,6 +54,7 @@ METRIC = "decode tokens/s and achieved KV HBM GB/s (% of MI355X peak) per pa_dec
 PREFILL_METRIC = "prefill tokens/s and attention TFLOP/s (% of MI355X bf16 matrix peak) per pa_prefill call"
 KERNEL_SOURCES = ("decode_valu.hip", "decode_mfma.hip", "pa_schedule.h", "pa_kernels.h", "pa_device.h")
 PREFILL_SOURCES = ("prefill.hip", "pa_prefill.h", "pa_device.h")
+COPY_SOURCES = ("copy_blocks.hip", "pa_kernels.h")
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak
 MALL_BYTES = 256 * 1024 * 1024  # MI355X Infinity Cache (memory-side, in front of HBM)
 
@@ -208,10 +209,21 @@ class Resident:
         self.reduce()
 
 
+def calibration_copies(torch):
+    """Five 1 GiB device-to-device copies in a row: rocprof_summary.py scales the
+    FETCH_SIZE and WRITE_SIZE counters of the same run by what they read for these."""
+    src = torch.empty(1 << 28, dtype=torch.float32, device="cuda").fill_(2.0)
+    dst = torch.empty_like(src)
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
+
+
 def load_traffic(workload: str, decode_s: float, sources=KERNEL_SOURCES):
     """HBM traffic of the attention kernel from the committed counter summary, if it
     was taken on the current kernel sources."""
-    kind = "prefill" if sources is PREFILL_SOURCES else "decode"
+    kind = {id(PREFILL_SOURCES): "prefill", id(COPY_SOURCES): "copy"}.get(id(sources), "decode")
     path = os.path.join(ROOT, "profiles", f"{kind}_traffic_{workload}.json")
     if not os.path.exists(path):
         return None, None
@@ -333,6 +345,10 @@ def bench_copy_blocks(args, torch) -> int:
     ms_per_step = (time.perf_counter() - t0) * 1e3 / K
     launch_ms = e0.elapsed_time(e1) / K
     achieved = moved / (launch_ms / 1e3) / 1e9
+    if args.calibrate_copy:
+        calibration_copies(torch)
+    # HBM traffic from the committed counter summary (the copy within the pool only)
+    traffic, traffic_bytes = load_traffic(args.op, launch_ms / 1e3, COPY_SOURCES) if args.op == "copy-blocks" else (None, None)
     what = "HBM GB/s (read + written)" if bound == "hbm" else "host-link GB/s"
     print(json.dumps({
         "metric": f"pa_copy_blocks {what} per call", "value": round(achieved, 1), "unit": "GB/s",
@@ -341,8 +357,12 @@ def bench_copy_blocks(args, torch) -> int:
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": p.dtype, "data": "synthetic",
         "config": {"workload": args.config, "op": args.op, "blocks_copied": n, "block_bytes": block_bytes},
         "roofline": {"bound": bound, "achieved": round(achieved, 1), "peak": peak, "unit": "GB/s",
-                     "frac": round(achieved / peak, 4), "traffic": None, "kernel": "copy_blocks_kernel",
-                     "algorithmic_bytes_per_launch": moved, "avg_launch_us": round(launch_ms * 1e3, 2)},
+                     "frac": round(achieved / peak, 4),
+                     "traffic": round(traffic, 1) if isinstance(traffic, float) else None,
+                     "kernel": "copy_blocks_kernel",
+                     "algorithmic_bytes_per_launch": moved, "avg_launch_us": round(launch_ms * 1e3, 2),
+                     **({"traffic_bytes_per_launch": traffic_bytes} if isinstance(traffic_bytes, (int, float))
+                        else {"traffic_note": traffic_bytes} if traffic_bytes else {})},
     }), flush=True)
     return 0
 
@@ -501,12 +521,7 @@ def main(argv=None):
         del scratch
 
     if args.calibrate_copy:
-        src = torch.empty(1 << 28, dtype=torch.float32, device="cuda").fill_(2.0)
-        dst = torch.empty_like(src)
-        for _ in range(5):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        del src, dst
+        calibration_copies(torch)
 
     out = r.out.float().cpu().numpy().astype(np.float64)
     finite = bool(np.isfinite(out).all())

@@ -165,12 +165,18 @@ def traffic(args):
     fs = moved_kib / cal["FETCH_SIZE"] if cal.get("FETCH_SIZE") else 1.0
     ws = moved_kib / cal["WRITE_SIZE"] if cal.get("WRITE_SIZE") else 1.0
     kernels = [k for (k, c) in fetch if c == "FETCH_SIZE" and (is_main(k) or is_reduce(k))]
-    p = wl.make_problem(args.config)
-    ab = wl.algorithmic_bytes(p)
-    alg = ab["kv_unique"] + ab["q"] + (ab["out"] if p.query_start is not None else 0)  # prefill: + the output
+    copy = args.config == "copy-blocks"
+    if copy:  # pa_copy_blocks: the bytes the bench line names (every block read once and written once)
+        p = None
+        alg = int(json.load(open(args.bench))["roofline"]["algorithmic_bytes_per_launch"])
+        sources = bench.COPY_SOURCES
+    else:
+        p = wl.make_problem(args.config)
+        ab = wl.algorithmic_bytes(p)
+        alg = ab["kv_unique"] + ab["q"] + (ab["out"] if p.query_start is not None else 0)  # prefill: + the output
+        sources = bench.PREFILL_SOURCES if p.query_start is not None else bench.KERNEL_SOURCES
     fetch_b = sum(fetch[(k, "FETCH_SIZE")] for k in kernels) * 1024 * fs
     write_b = sum(write.get((k, "WRITE_SIZE"), 0.0) for k in kernels) * 1024 * ws
-    sources = bench.PREFILL_SOURCES if p.query_start is not None else bench.KERNEL_SOURCES
     res = {
         "workload": args.config,
         "kernels": kernels,
@@ -196,7 +202,8 @@ def traffic(args):
     for k in kernels:
         out.append(f"`{short(k)}` ({nf[(k, 'FETCH_SIZE')]} dispatches): FETCH_SIZE {fetch[(k, 'FETCH_SIZE')]:.1f} KiB, "
                    f"WRITE_SIZE {write.get((k, 'WRITE_SIZE'), 0.0):.1f} KiB raw per dispatch (median).")
-    what = "KV of every context token once, shared blocks once, + Q" + (" + output" if p.query_start is not None else "")
+    what = ("every copied block read once and written once" if copy else
+            "KV of every context token once, shared blocks once, + Q" + (" + output" if p.query_start is not None else ""))
     out += ["", f"Per launch after scaling: {fetch_b / 1e6:.2f} MB read, {write_b / 1e6:.2f} MB written; algorithmic "
                 f"bytes ({what}) {alg / 1e6:.2f} MB; measured / "
                 f"algorithmic = {(fetch_b + write_b) / alg:.4f}.",
