@@ -15,9 +15,10 @@
 // KV head, 32 rows per wave, and all eight waves (two per SIMD, one
 // workgroup per CU) walk the same KV blocks.
 // Each block (16 tokens of K and of V for the head) is staged once per
-// workgroup in LDS, 8 blocks per step, double-buffered (the next step's
-// global loads are in flight while the current one is multiplied), and every
-// wave reads it from there:
+// workgroup in LDS, 8 blocks per step, double-buffered: the next step goes
+// from memory straight into LDS (gfx950's 16-byte buffer-to-LDS loads, wave
+// w loading block w) while the current one is multiplied, and every wave
+// reads it from there:
 //
 //   scores  S^T = K_blk Q^T per 16-row tile, v_mfma_f32_16x16x32_bf16 with
 //           A = K from LDS (lane l: token l % 16, 8 dims) and B = the wave's
@@ -49,28 +50,54 @@ static_assert(kRowsPerWave % 16 == 0, "whole MFMA row tiles per wave");
 constexpr float kOverflowSlack = 64.0f;  // log2 units
 constexpr int kXcds = 8;  // accelerator complex dies of an MI355X
 constexpr int kStepBlocks = 8;           // blocks staged per step (per barrier), multiplied two at a time
-constexpr int kPrefetch = 1;             // steps whose global loads are in flight
 
-// one block of one KV head in LDS (64 banks of 4 bytes).  K rows are padded by
-// 16 bytes: a K read (16 lanes, 16 bytes each, one per token row) then starts
-// the 16 rows 4 banks apart and touches every bank once.  V rows are padded by
-// 32 bytes: a transposing V read (32 lanes, 8 bytes each: 8 token rows x 32
-// contiguous bytes) then starts the 8 rows 8 banks apart, again every bank
-// once.  With the K padding on V every second row pair shared banks.
+// one block of one KV head in LDS (64 banks of 4 bytes).  Rows are not padded:
+// a buffer-to-LDS load fills 1 KiB contiguous per instruction.  Instead the
+// 16-byte chunk c of token row r sits at chunk c ^ kswz(r) of its K row and
+// c ^ vswz(r) of its V row.  A K read (16 lanes, 16 bytes each: 16 rows, one
+// logical chunk) then touches every bank once, and so does a transposing V
+// read (32 lanes, 8 bytes each: 8 token rows x 32 contiguous bytes; the XOR
+// is even there, so a row's two chunks stay side by side).
 template <int D>
 struct Stage {
-  uint16_t k[kBlockTokens][D + 8];
-  uint16_t v[kBlockTokens][D + 16];
+  uint16_t k[kBlockTokens][D];
+  uint16_t v[kBlockTokens][D];
 };
+template <int D>
+__device__ __forceinline__ int kswz(int r) { return D == 128 ? (r & 15) : ((r >> 1) & 7); }
+template <int D>
+__device__ __forceinline__ int vswz(int r) { return D == 128 ? 2 * (r & 7) : 2 * ((r >> 1) & 3); }
+
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+// one 16-byte buffer-to-LDS load per lane (gfx950): LDS lds + 16 lane <- the
+// descriptor's bytes at voff, zero past its record count.  Written in asm so
+// that the compiler does not track it: it would put a vmcnt(0) before the
+// reads of the other buffer, since it cannot tell the two apart.  The caller
+// waits for it (vmcnt) before the barrier that publishes it.  m0, which the
+// load takes its LDS address from, is restored afterwards (the load reads it
+// at issue; the compiler assumes m0 keeps its value across the asm).
+__device__ __forceinline__ void dma16(uint32_t lds, uint32_t voff, u32x4_t rs) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dwordx4 %2, %3, 0 offen lds\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(lds), "v"(voff), "s"(rs)
+      : "memory");
+}
+__device__ __forceinline__ void wait_dma() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+__device__ __forceinline__ uint32_t lds_u32(const void* p) {
+  return (uint32_t)(size_t)(__attribute__((address_space(3))) void*)(void*)p;
+}
 
 template <int D>
 __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillParams a) {
   constexpr int KS = D / 32;                          // score k-steps
   constexpr int VH = D / 64;                          // value column halves
   constexpr int CH = D / 8;                           // 16-byte chunks per token row of the head
-  constexpr int NCHUNK = 2 * kBlockTokens * CH;       // K and V chunks of one block
-  constexpr int LOADS = (NCHUNK + kThreads - 1) / kThreads;
-  constexpr bool kRagged = NCHUNK % kThreads != 0;  // d 64: half the threads stage nothing
 
   __shared__ Stage<D> st[2][kStepBlocks];  // [buffer][block of the step]
   __shared__ int s_overflow;
@@ -146,20 +173,26 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillParams a) {
   };
   clear();
 
-  // staging: chunk c of a block is K (c < 16 CH) or V, token (c % 16 CH) / CH, 16 bytes (c % CH).
-  // 16 CH is a multiple of 64, so whether a load is of K or of V is the same
-  // across a wave.  A block is read through buffer descriptors whose record
-  // count ends at its last context token (the rest reads as zero); a thread's
-  // byte offset inside the block is fixed.
+  // staging: wave w loads block w of each step, K then V, RPI token rows per
+  // instruction; lane l brings 16-byte chunk l % CH of row RPI i + l / CH of
+  // the LDS layout, so it reads that row's logical chunk (l % CH) ^ swizzle.
+  // A block is read through buffer descriptors whose record count ends at its
+  // last context token (the rest reads as zero); a lane's byte offsets inside
+  // the block are fixed.
   const char* kbase = static_cast<const char*>(a.k_cache);
   const char* vbase = static_cast<const char*>(a.v_cache);
   const uint32_t tok_stride = (uint32_t)a.n_kv * D * 2;
   const size_t blk_bytes = (size_t)tok_stride * kBlockTokens;
-  uint32_t voff[LOADS];
+  constexpr int RPI = 1024 / (2 * D);     // token rows per 1 KiB load instruction
+  constexpr int NI = kBlockTokens / RPI;  // load instructions per block, for K and for V
+  static_assert(kStepBlocks == kWaves, "wave w stages block w of every step");
+  uint32_t voffk[NI], voffv[NI];
 #pragma unroll
-  for (int u = 0; u < LOADS; ++u) {
-    const int rem = (threadIdx.x + u * kThreads) % (kBlockTokens * CH);
-    voff[u] = (uint32_t)(rem / CH) * tok_stride + (uint32_t)g * D * 2 + 16u * (uint32_t)(rem % CH);
+  for (int i = 0; i < NI; ++i) {
+    const int row = RPI * i + lane / CH, pc = lane % CH;
+    const uint32_t rb = (uint32_t)row * tok_stride + (uint32_t)g * D * 2;
+    voffk[i] = rb + 16u * (uint32_t)(pc ^ kswz<D>(row));
+    voffv[i] = rb + 16u * (uint32_t)(pc ^ vswz<D>(row));
   }
   // The block-table entries of step it, one per lane (lane l % 8: block 8 it +
   // l % 8, clamped into the range, nblk >= 1): a vector load issued a whole
@@ -169,44 +202,27 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillParams a) {
     const int blk = kStepBlocks * it + (lane & (kStepBlocks - 1));
     return table[min(blk, nblk - 1)];
   };
-  // the blocks of step it into registers, their table entries in tv (from
-  // table_vec(it)); returns bit bb set where block bb of the step is valid (in
-  // the range and inside the pool), so that the multiply needs no table reads
-  auto fetch = [&](int it, int tv, uint4(&r)[kStepBlocks][LOADS]) -> uint32_t {
-    uint32_t okm = 0;
+  // step it into LDS buffer buf: wave w loads block w, its table entries in tv (from
+  // table_vec(it)).  Returns bit bb set where block bb of the step is valid (in
+  // the range and inside the pool), so that the multiply needs no table reads.
+  auto issue = [&](int it, int tv, int buf) -> uint32_t {
+    const int bl = kStepBlocks * it + (lane & (kStepBlocks - 1));
+    const bool okl = lane < kStepBlocks && bl < nblk && (unsigned)tv < (unsigned)a.num_blocks;
+    const uint32_t okm = (uint32_t)__builtin_amdgcn_ballot_w64(okl);
+    const int blk = kStepBlocks * it + w;
+    const bool ok = (okm >> w) & 1u;
+    const int raw = __builtin_amdgcn_readlane(tv, w);
+    const uint32_t nrec = ok ? (uint32_t)min(kBlockTokens, L - blk * kBlockTokens) * tok_stride : 0u;
+    const size_t boff = ok ? (size_t)raw * blk_bytes : 0;
+    const size_t ka = (size_t)(kbase + boff), va = (size_t)(vbase + boff);
+    const u32x4_t kr = {(uint32_t)ka, (uint32_t)(ka >> 32) & 0xffffu, nrec, (uint32_t)kBufferWord3};
+    const u32x4_t vr = {(uint32_t)va, (uint32_t)(va >> 32) & 0xffffu, nrec, (uint32_t)kBufferWord3};
+    const uint32_t kl = lds_u32(&st[buf][w].k[0][0]), vl = lds_u32(&st[buf][w].v[0][0]);
 #pragma unroll
-    for (int bb = 0; bb < kStepBlocks; ++bb) {
-      const int blk = kStepBlocks * it + bb;
-      const int raw = __builtin_amdgcn_readlane(tv, bb);
-      const int phys = blk < nblk && (unsigned)raw < (unsigned)a.num_blocks ? raw : -1;
-      okm |= (phys >= 0 ? 1u : 0u) << bb;
-      const int valid = phys >= 0 ? min(kBlockTokens, L - blk * kBlockTokens) : 0;
-      const size_t boff = phys >= 0 ? (size_t)phys * blk_bytes : 0;
-      const __amdgpu_buffer_rsrc_t kr =
-          __builtin_amdgcn_make_buffer_rsrc((void*)(kbase + boff), (short)0, valid * (int)tok_stride, kBufferWord3);
-      const __amdgpu_buffer_rsrc_t vr =
-          __builtin_amdgcn_make_buffer_rsrc((void*)(vbase + boff), (short)0, valid * (int)tok_stride, kBufferWord3);
+    for (int i = 0; i < NI; ++i) dma16(kl + 1024u * i, voffk[i], kr);
 #pragma unroll
-      for (int u = 0; u < LOADS; ++u) {
-        if (kRagged && threadIdx.x + u * kThreads >= NCHUNK) continue;  // wave-uniform
-        const bool is_k = w * 64 + u * kThreads < kBlockTokens * CH;  // wave-uniform
-        r[bb][u] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(is_k ? kr : vr, voff[u], 0, 0));
-      }
-    }
+    for (int i = 0; i < NI; ++i) dma16(vl + 1024u * i, voffv[i], vr);
     return okm;
-  };
-  auto put = [&](int buf, const uint4(&r)[kStepBlocks][LOADS]) {
-#pragma unroll
-    for (int bb = 0; bb < kStepBlocks; ++bb)
-#pragma unroll
-      for (int u = 0; u < LOADS; ++u) {
-        const int c = threadIdx.x + u * kThreads;
-        if (kRagged && c >= NCHUNK) continue;
-        const int rem = c % (kBlockTokens * CH);
-        const int tok = rem / CH, part = rem % CH;
-        uint16_t* dst = c < kBlockTokens * CH ? &st[buf][bb].k[tok][8 * part] : &st[buf][bb].v[tok][8 * part];
-        *reinterpret_cast<uint4*>(dst) = r[bb][u];
-      }
   };
 
   // per-row reference: the row's maximum (lanes j, j+16, j+32, j+48 share a row)
@@ -244,7 +260,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillParams a) {
         floatx4_t acc_s = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
-          const uint4 kb = *reinterpret_cast<const uint4*>(&st[buf][sl + bb].k[j][32 * ks + 8 * grp]);
+          const uint4 kb = *reinterpret_cast<const uint4*>(&st[buf][sl + bb].k[j][8 * ((4 * ks + grp) ^ kswz<D>(j))]);
           acc_s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kb),
                                                           __builtin_bit_cast(bf16x8_t, qreg[tt][ks]), acc_s, 0, 0, 0);
         }
@@ -311,7 +327,8 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillParams a) {
       for (int h = 0; h < VH; ++h)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const uint16_t* src = &st[buf][sl + bb].v[4 * grp + (j >> 2)][16 * (4 * h + e) + 4 * (j & 3)];
+          const int vr = 4 * grp + (j >> 2), vc = 2 * (4 * h + e) + ((j & 3) >> 1);  // row, logical chunk
+          const uint16_t* src = &st[buf][sl + bb].v[vr][8 * (vc ^ vswz<D>(vr)) + 4 * (j & 1)];
           vt4[bb][h][e] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) short4_t*)src);
         }
 #pragma unroll
@@ -350,43 +367,31 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillParams a) {
     }
   };
 
-  // one pass over the steps.  Global loads run kPrefetch steps ahead in
-  // registers (slot it % kPrefetch holds step it); LDS holds two steps: the
-  // one being multiplied and the next one.  okm[k] holds the valid-block bits
-  // of step it + k.  The next step goes to LDS, and the one after it is
-  // requested, halfway through a step's pairs rather than after them: its LDS
-  // buffer was last read in the previous step, which ended at a barrier, and
-  // the barrier at the end of this step publishes it (165.3-165.7 against
-  // 167.7-169.0 us on four 512-token chunks; after the first pair, no gain).
+  // one pass over the steps.  LDS holds two steps: the one being multiplied
+  // and the next one, whose loads are issued halfway through the step's pairs
+  // (its buffer was last read in the previous step, which ended at a
+  // barrier); each wave waits for its own loads before the barrier that ends
+  // the step.  On four 512-token chunks (three alternating runs): 139.3-139.4
+  // us; issued at the start of the step 146.2-147.2, after the first pair
+  // 141.0-141.3, after the third 141.6-142.2; global loads into registers that
+  // the waves then wrote to LDS, 165.0-165.1 us with 32 VGPRs more.
   const int nit = (nblk + kStepBlocks - 1) / kStepBlocks;
   auto sweep = [&](int mode) {
-    uint4 r[kPrefetch][kStepBlocks][LOADS];
-    uint32_t okm[kPrefetch + 1];
-#pragma unroll
-    for (int u = 0; u < kPrefetch; ++u) okm[u] = u < nit ? fetch(u, table_vec(u), r[u]) : 0u;
-    put(0, r[0]);
-    okm[kPrefetch] = kPrefetch < nit ? fetch(kPrefetch, table_vec(kPrefetch), r[0]) : 0u;
+    // table loads are unconditional (clamped to the last step): a register
+    // set to 0 on the other path would need a wait for the load in flight into it
+    int tvn = table_vec(min(1, nit - 1));
+    uint32_t okm = issue(0, table_vec(0), 0);
+    wait_dma();
     __syncthreads();
-    for (int it0 = 0; it0 < nit; it0 += kPrefetch) {
-#pragma unroll
-      for (int u = 0; u < kPrefetch; ++u) {
-        const int it = it0 + u;
-        if (it >= nit) break;
-        // table entries of the step fetched at the end of this one, loaded now
-        const int tv = it + 1 + kPrefetch < nit ? table_vec(it + 1 + kPrefetch) : 0;
-        const int nxt = (u + 1) % kPrefetch;  // register slot of step it + 1 (constant once unrolled)
-        uint32_t okn = 0u;
-        compute(it, it & 1, mode, okm[0], [&] {
-          if (it + 1 < nit) {
-            put((it + 1) & 1, r[nxt]);
-            if (it + 1 + kPrefetch < nit) okn = fetch(it + 1 + kPrefetch, tv, r[nxt]);
-          }
-        });
-#pragma unroll
-        for (int k = 0; k < kPrefetch; ++k) okm[k] = okm[k + 1];
-        okm[kPrefetch] = okn;
-        __syncthreads();  // step it + 1 staged; everyone is done with step it
-      }
+    for (int it = 0; it < nit; ++it) {
+      uint32_t okn = 0u;
+      compute(it, it & 1, mode, okm, [&] {
+        okn = it + 1 < nit ? issue(it + 1, tvn, (it + 1) & 1) : 0u;
+        tvn = table_vec(min(it + 2, nit - 1));
+      });
+      okm = okn;
+      wait_dma();
+      __syncthreads();  // step it + 1 staged; everyone is done with step it
     }
   };
 
