@@ -248,6 +248,10 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillParams a) {
   // mode 0: reference from the first pair, weighted sums, largest exponents; 1: row maxima only;
   // 2: weighted sums
   auto pair = [&](int blk0, int buf, int sl, int mode, uint32_t okb) {
+    // the compiler's interleaving of LDS reads with matrix instructions:
+    // 143.5-143.9 against 144.9-145.9 us on four 512-token chunks (three
+    // alternating runs; variant 1 143.8-144.1)
+    __builtin_amdgcn_iglp_opt(0);
     floatx4_t x[2][TW];  // raw q.k: [block][tile], lane: tokens 4 grp + v of row j
     bool ok[2], whole[2];
 #pragma unroll
