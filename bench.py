@@ -18,8 +18,9 @@ Prints one JSON line:
                  average launch time (HIP events on the launch stream; for a
                  split context the event pair spans pa_decode and pa_reduce)
                  against the 8 TB/s HBM peak; traffic from the committed counter
-                 summary.  Where the working set is under twice the 256 MB MALL
-                 (the fp8 layer), warm launches are partly served from the MALL,
+                 summary.  Where the K bytes are under twice the 256 MB MALL (the
+                 kernels load V non-temporally, so K is what can stay cached;
+                 the 8B layers), warm launches are partly served from the MALL,
                  so the figure is taken over cold launches instead.  Shared
                  prefix blocks count once; achieved_logical / frac_logical
                  count every sequence's context in full.
@@ -545,8 +546,10 @@ def main(argv=None):
                 "avg_launch_us_event_pair_each": single_pair_us}
     else:
         # rated over warm launches (the timed region), or over cold ones where the
-        # MALL could serve a large part of the working set between warm launches
-        cold_basis = kv_bytes < 2 * MALL_BYTES and cold_ms is not None
+        # MALL could serve a large part of the working set between warm launches.
+        # The kernels load V non-temporally, so what can stay cached is K: half
+        # the KV bytes.
+        cold_basis = kv_bytes / 2 < 2 * MALL_BYTES and cold_ms is not None
         basis_s = cold_ms / 1e3 if cold_basis else decode_s
         achieved = kv_bytes / basis_s / 1e9
         traffic, traffic_bytes = load_traffic(args.config, basis_s)
@@ -559,8 +562,8 @@ def main(argv=None):
                 "frac": round(achieved / HBM_PEAK_GBPS, 4),
                 "traffic": round(traffic, 1) if isinstance(traffic, float) else None,
                 "kernel": kernel,
-                "timing": ("cold launches (each after a 512 MiB read; the working set is under twice the "
-                           "256 MB MALL, which serves part of it between warm launches): one event pair around "
+                "timing": ("cold launches (each after a 512 MiB read; the K bytes are under twice the "
+                           "256 MB MALL, which serves part of them between warm launches): one event pair around "
                            f"{args.cold} (read, launch) pairs minus one around {args.cold} reads") if cold_basis
                 else f"warm launches: {K} back to back, one event pair around them",
                 "algorithmic_bytes_per_launch": kv_bytes,

@@ -376,6 +376,13 @@ struct MfmaAttender {
 
     // K: KL loads of 16 bytes; V: 4 tokens x VH halves of 8 bytes (bf16), or
     // 4 tokens x D/16 bytes (fp8, in vb[v][0])
+    // V loads are non-temporal (cache policy nt), K loads ordinary.  Two
+    // alternating runs, us: 70B 193.8 / 194.3 against 208.8 / 208.1, fp8 8B
+    // (cold) 57.2 / 56.9 against 60.9 / 61.5, speculative verify 227.3 / 227.0
+    // against 237.3 / 235.9, tree verify 217.6 / 217.6 against 226.1 / 226.9.
+    // Non-temporal K loads made every one of them slower (224.9, 65.1, 252.0,
+    // 234.2 us), and so did both together.
+    constexpr int kVPolicy = 2;
     auto issue = [&](int ids, int cnt, int k0, int kk, uint4(&kb)[KL], uint2(&vb)[4][VH], int& lblk, bool& ok,
                      int su) {
       const int phys = __builtin_amdgcn_readlane(ids, kk < cnt ? kk : 0);
@@ -396,14 +403,14 @@ struct MfmaAttender {
         char* slot = reinterpret_cast<char*>(sm.vring) + (w * NBUF + su) * kVBytes;
 #pragma unroll
         for (int i = 0; i < kVLoads; ++i)
-          __builtin_amdgcn_raw_ptr_buffer_load_lds(vr, (lds_void_t)(slot + 1024 * i), 16, (int)vld[i], 0, 0, 0);
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(vr, (lds_void_t)(slot + 1024 * i), 16, (int)vld[i], 0, 0, kVPolicy);
       } else if constexpr (KV8) {
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
           if constexpr (D == 128)
-            vb[v][0] = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(vr, v_off, v * tok_bytes, 0));
+            vb[v][0] = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(vr, v_off, v * tok_bytes, kVPolicy));
           else
-            vb[v][0] = make_uint2(__builtin_amdgcn_raw_buffer_load_b32(vr, v_off, v * tok_bytes, 0), 0u);
+            vb[v][0] = make_uint2(__builtin_amdgcn_raw_buffer_load_b32(vr, v_off, v * tok_bytes, kVPolicy), 0u);
         }
       } else {
 #pragma unroll
@@ -411,7 +418,7 @@ struct MfmaAttender {
 #pragma unroll
           for (int h = 0; h < VH; ++h)
             vb[v][h] = __builtin_bit_cast(
-                uint2, __builtin_amdgcn_raw_buffer_load_b64(vr, v_off + 128 * h, v * tok_bytes, 0));
+                uint2, __builtin_amdgcn_raw_buffer_load_b64(vr, v_off + 128 * h, v * tok_bytes, kVPolicy));
       }
     };
 

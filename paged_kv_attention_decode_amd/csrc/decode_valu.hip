@@ -103,11 +103,15 @@ struct WaveTotals {
   alignas(16) float acc[NW][R][D];
 };
 
-// NTL: K and V loads non-temporal (cache policy nt)
-template <typename T, int D, int R, int NW, int NBUF, bool NTL>
+template <typename T, int D, int R, int NW, int NBUF>
 struct ValuAttender {
   static constexpr int kThreads = NW * 64;
-  static constexpr int kLoadPolicy = NTL ? 2 : 0;
+  // V loads are non-temporal (cache policy nt), K loads ordinary.  Two
+  // alternating runs, us: 8B layer 91.7 / 91.7 warm and 97.8 / 97.4 cold
+  // against 100.4 / 100.5 and 103.0 / 103.7 with both non-temporal, and
+  // 107.5-108.4 / 106.2-107.7 with neither; long contexts in 512-token
+  // partitions 450.8 / 451.6 against 482.3 / 482.2 (both) and 482.5 (neither).
+  static constexpr int kVPolicy = 2;
   static constexpr int kD = D;
   static constexpr bool kBF16 = sizeof(T) == 2;
   static constexpr int EPC = Elem<T>::kPer16B;     // elements per 16-byte chunk
@@ -299,10 +303,10 @@ struct ValuAttender {
 #pragma unroll
       for (int c = 0; c < NCK; ++c)
         kb[c] = __builtin_bit_cast(uint4,
-                                   __builtin_amdgcn_raw_buffer_load_b128(kr, k_off + 64 * c, 0, kLoadPolicy));
+                                   __builtin_amdgcn_raw_buffer_load_b128(kr, k_off + 64 * c, 0, 0));
 #pragma unroll
       for (int i = 0; i < NV; ++i)
-        vb[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(vr, v_off, i * v_step, kLoadPolicy));
+        vb[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(vr, v_off, i * v_step, kVPolicy));
     };
 
     // scores of this lane's token for every row, log2 units, -inf where masked
@@ -522,10 +526,10 @@ struct ValuAttender {
   }
 };
 
-template <typename T, int D, int R, int NW, int NBUF, bool BALANCED, bool NTL>
+template <typename T, int D, int R, int NW, int NBUF, bool BALANCED>
 __global__ __launch_bounds__(NW * 64) void decode_valu_kernel(DecodeParams a) {
   __shared__ WaveTotals<T, D, R, NW> sm;
-  ValuAttender<T, D, R, NW, NBUF, NTL> at(a, sm);
+  ValuAttender<T, D, R, NW, NBUF> at(a, sm);
   if constexpr (BALANCED) drive_balanced(a, at);
   else drive_fixed(a, at);
 }
@@ -556,26 +560,19 @@ hipError_t launch_one(const DecodeParams& p, hipStream_t s) {
     // steady state stays at the same bandwidth (measured on the 8B layer:
     // 122 us against 126 us with three blocks).
     static const int resident =
-        resident_per_cu(decode_valu_kernel<T, D, R, kWaves, kBalancedBlocksInFlight, true, false>, kWaves * 64);
+        resident_per_cu(decode_valu_kernel<T, D, R, kWaves, kBalancedBlocksInFlight, true>, kWaves * 64);
     DecodeParams q = p;
     q.num_wgs = balanced_workgroups(resident, p.n_kv);
-    hipLaunchKernelGGL((decode_valu_kernel<T, D, R, kWaves, kBalancedBlocksInFlight, true, false>), dim3(q.num_wgs),
-                       dim3(kWaves * 64), 0, s, q);
-  } else if (p.mode == kSinglePass) {
-    // Non-temporal K and V loads: each block is read once per step.  8B
-    // layer, three alternating runs: 100.7-100.9 against 107.5-108.4 us warm,
-    // 103.4-104.0 against 106.2-107.7 us cold.  The split schedule keeps
-    // ordinary loads (long contexts in 512-token partitions: 488.5 against
-    // 482.5 us with them), and so do the matrix-core kernels (1.5-6% slower
-    // with them on the 70B, fp8 and speculative-verify layers).
-    static const int resident = resident_per_cu(decode_valu_kernel<T, D, R, kWaves, NB, false, true>, kWaves * 64);
-    DecodeParams q = p;
-    q.pair_stride = one_pass_pairing(resident, p.num_seqs, p.n_kv);
-    hipLaunchKernelGGL((decode_valu_kernel<T, D, R, kWaves, NB, false, true>), dim3(1, p.n_kv, p.num_seqs),
+    hipLaunchKernelGGL((decode_valu_kernel<T, D, R, kWaves, kBalancedBlocksInFlight, true>), dim3(q.num_wgs),
                        dim3(kWaves * 64), 0, s, q);
   } else {
-    hipLaunchKernelGGL((decode_valu_kernel<T, D, R, kWaves, NB, false, false>), dim3(p.num_parts, p.n_kv, p.num_seqs),
-                       dim3(kWaves * 64), 0, s, p);
+    DecodeParams q = p;
+    if (p.mode == kSinglePass) {
+      static const int resident = resident_per_cu(decode_valu_kernel<T, D, R, kWaves, NB, false>, kWaves * 64);
+      q.pair_stride = one_pass_pairing(resident, p.num_seqs, p.n_kv);
+    }
+    dim3 grid(p.mode == kPartitions ? p.num_parts : 1, p.n_kv, p.num_seqs);
+    hipLaunchKernelGGL((decode_valu_kernel<T, D, R, kWaves, NB, false>), grid, dim3(kWaves * 64), 0, s, q);
   }
   return hipGetLastError();
 }
